@@ -1,0 +1,352 @@
+/*
+ * LatentMoE layer forward pass: plain fp64 CPU oracle.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code,
+ * header or constant with the GPU library.
+ *
+ * Sources (cited by page title and the part of the page):
+ *   [EXPL]   "LatentMoE: NVIDIA's Latent Mixture of Experts Explained Through
+ *            Equations, Architecture, Code and ..." (wpnews.pro).
+ *   [README] "Latent-MoE" (GitHub README of kyegomez/Latent-MoE).
+ *
+ * What is computed, per token t (tokens are independent):
+ *   1. router scores s = x_t W_r (+ b)                 [EXPL, Figure 3; Figure 8 top path]
+ *   2. p = softmax(s) over all N' experts              [EXPL, Figure 3]
+ *   3. the K' experts with the largest scores, slot k being the k-th in the
+ *      order (score descending, expert index ascending)
+ *                                                     [EXPL, Figure 3; LatentMoE code block]
+ *   4. gate_k = p[sel_k] / sum_j p[sel_j]              [EXPL, MoE code block: the K weights
+ *                                                      are renormalised to sum to 1]
+ *   5. z = x_t W_down (width l)                        [EXPL, Figure 6 upper half]
+ *   6. u = sum_k gate_k * W2_e relu(W1_e z)^2, e = sel_k  (experts run in l)
+ *                                                     [EXPL, Figure 9; LatentMoE code block]
+ *   7. y_t = u W_up + sum_s W2_s relu(W1_s x_t)^2      [EXPL, Figure 6 lower half; Figure 8
+ *                                                      bottom path; shared experts unweighted]
+ *   8. dispatch order: a stable counting sort of the (token, slot) pairs by
+ *      expert, then token                             [EXPL, Figure 12 reading: one GPU]
+ *
+ * Readings where the pages are silent: selection is taken on the scores
+ * (softmax is strictly increasing, so the set is the same in exact
+ * arithmetic); ties go to the lower expert index; there is no residual
+ * inside the layer, no bias other than the optional router bias (added to the
+ * scores before softmax), no capacity limit and no token dropping.
+ *
+ * Arithmetic: every stored value (bf16 bits or float32) is widened exactly
+ * to double and all sums are in double in plain index order.  No blocking,
+ * fusion or reordering beyond the definition above.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef struct {
+    int64_t d, l, m, m_s, n_shared, n_experts, top_k;
+    int32_t bf16;     /* 1: tensors hold bf16 bit patterns, 0: float32 */
+    int32_t has_bias; /* 1: b_router is used */
+} orc_shape;
+
+typedef struct {
+    const void *x;        /* [T, d] */
+    const void *w_router; /* [d, N'] */
+    const float *b_router;/* [N'] or NULL */
+    const void *w_down;   /* [d, l] */
+    const void *w1;       /* [N', l, m] */
+    const void *w2;       /* [N', m, l] */
+    const void *w_up;     /* [l, d] */
+    const void *w1_s;     /* [S, d, m_s] */
+    const void *w2_s;     /* [S, m_s, d] */
+} orc_tensors;
+
+/* Optional per-token outputs; any pointer may be NULL.  Row r of each array
+ * belongs to tokens[r]. */
+typedef struct {
+    double *logits;  /* [n, N'] */
+    int32_t *idx;    /* [n, K'] */
+    double *gate;    /* [n, K'] */
+    double *z;       /* [n, l] */
+    double *h;       /* [n, K', m]  relu(W1_e z)^2 per slot */
+    double *o;       /* [n, K', l]  W2_e h per slot (before the gate) */
+    double *u;       /* [n, l] */
+    double *hs;      /* [n, S*m_s]  relu(W1_s x)^2 */
+    double *y;       /* [n, d] */
+} orc_outputs;
+
+static double ld_elem(const void *base, int64_t i, int bf16)
+{
+    if (bf16) {
+        uint32_t u = ((uint32_t)((const uint16_t *)base)[i]) << 16;
+        float f;
+        memcpy(&f, &u, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)base)[i];
+}
+
+/* out[j] = sum_i in[i] * W[off + i*cols + j]  (W row-major [rows, cols]) */
+static void matvec(const double *in, const void *W, int64_t off, int64_t rows,
+                   int64_t cols, int bf16, double *out)
+{
+    for (int64_t j = 0; j < cols; ++j)
+        out[j] = 0.0;
+    for (int64_t i = 0; i < rows; ++i) {
+        const double a = in[i];
+        const int64_t row = off + i * cols;
+        for (int64_t j = 0; j < cols; ++j)
+            out[j] += a * ld_elem(W, row + j, bf16);
+    }
+}
+
+static double sq_relu(double a) { return a > 0.0 ? a * a : 0.0; }
+
+/* The K' indices with the largest s, ordered by (s descending, index
+ * ascending).  Plain repeated selection. */
+static int select_topk(const double *s, int64_t n, int64_t k, int32_t *idx,
+                       unsigned char *taken)
+{
+    memset(taken, 0, (size_t)n);
+    for (int64_t r = 0; r < k; ++r) {
+        int64_t best = -1;
+        for (int64_t e = 0; e < n; ++e) {
+            if (taken[e])
+                continue;
+            if (best < 0 || s[e] > s[best])
+                best = e;
+        }
+        if (best < 0)
+            return -1;
+        taken[best] = 1;
+        idx[r] = (int32_t)best;
+    }
+    return 0;
+}
+
+/* gate_k = p[idx_k] / sum_j p[idx_j] with p = softmax(s) over all n. */
+static void gates(const double *s, int64_t n, const int32_t *idx, int64_t k,
+                  double *g)
+{
+    double mx = s[0];
+    for (int64_t e = 1; e < n; ++e)
+        if (s[e] > mx)
+            mx = s[e];
+    double zsum = 0.0;
+    for (int64_t e = 0; e < n; ++e)
+        zsum += exp(s[e] - mx);
+    double gsum = 0.0;
+    for (int64_t r = 0; r < k; ++r) {
+        g[r] = exp(s[idx[r]] - mx) / zsum;
+        gsum += g[r];
+    }
+    for (int64_t r = 0; r < k; ++r)
+        g[r] /= gsum;
+}
+
+static int check_shape(const orc_shape *c)
+{
+    if (!c || c->d <= 0 || c->l <= 0 || c->m <= 0 || c->n_experts <= 0 ||
+        c->top_k <= 0 || c->top_k > c->n_experts || c->n_shared < 0 ||
+        (c->n_shared > 0 && c->m_s <= 0))
+        return -1;
+    return 0;
+}
+
+/* Forward pass for the listed tokens.  idx_in (NULL or [n, K']) forces the
+ * routing: those experts are used, with gates from this oracle's own
+ * scores.  Returns 0 on success. */
+int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
+                const int64_t *tokens, int64_t n_tok, const int32_t *idx_in,
+                const orc_outputs *out, int n_threads)
+{
+    if (check_shape(c) || !w || !tokens || !out)
+        return -1;
+    for (int64_t r = 0; r < n_tok; ++r)
+        if (tokens[r] < 0 || tokens[r] >= T)
+            return -2;
+    const int64_t d = c->d, l = c->l, m = c->m, ms = c->m_s, S = c->n_shared;
+    const int64_t N = c->n_experts, K = c->top_k;
+    const int bf = c->bf16;
+    int err = 0;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+
+#pragma omp parallel reduction(| : err)
+    {
+        double *x = malloc(sizeof(double) * (size_t)d);
+        double *s = malloc(sizeof(double) * (size_t)N);
+        int32_t *sel = malloc(sizeof(int32_t) * (size_t)K);
+        double *g = malloc(sizeof(double) * (size_t)K);
+        unsigned char *taken = malloc((size_t)N);
+        double *z = malloc(sizeof(double) * (size_t)l);
+        double *a = malloc(sizeof(double) * (size_t)(m > ms ? m : ms));
+        double *o = malloc(sizeof(double) * (size_t)(l > d ? l : d));
+        double *u = malloc(sizeof(double) * (size_t)l);
+        double *y = malloc(sizeof(double) * (size_t)d);
+        double *tmp = malloc(sizeof(double) * (size_t)d);
+        if (!x || !s || !sel || !g || !taken || !z || !a || !o || !u || !y || !tmp)
+            err |= 1;
+
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n_tok; ++r) {
+            if (err)
+                continue;
+            const int64_t t = tokens[r];
+            for (int64_t i = 0; i < d; ++i)
+                x[i] = ld_elem(w->x, t * d + i, bf);
+
+            /* 1. router scores */
+            matvec(x, w->w_router, 0, d, N, bf, s);
+            if (c->has_bias && w->b_router)
+                for (int64_t e = 0; e < N; ++e)
+                    s[e] += (double)w->b_router[e];
+            if (out->logits)
+                memcpy(out->logits + r * N, s, sizeof(double) * (size_t)N);
+
+            /* 3. selection (or forced routing) */
+            if (idx_in) {
+                for (int64_t k = 0; k < K; ++k) {
+                    sel[k] = idx_in[r * K + k];
+                    if (sel[k] < 0 || sel[k] >= N)
+                        err |= 2;
+                }
+            } else if (select_topk(s, N, K, sel, taken)) {
+                err |= 4;
+            }
+            if (err)
+                continue;
+            /* 2 + 4. softmax and renormalised gates */
+            gates(s, N, sel, K, g);
+            if (out->idx)
+                memcpy(out->idx + r * K, sel, sizeof(int32_t) * (size_t)K);
+            if (out->gate)
+                memcpy(out->gate + r * K, g, sizeof(double) * (size_t)K);
+
+            /* 5. shared down-projection */
+            matvec(x, w->w_down, 0, d, l, bf, z);
+            if (out->z)
+                memcpy(out->z + r * l, z, sizeof(double) * (size_t)l);
+
+            /* 6. latent experts and weighted combine in l */
+            for (int64_t j = 0; j < l; ++j)
+                u[j] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t e = sel[k];
+                matvec(z, w->w1, e * l * m, l, m, bf, a);
+                for (int64_t j = 0; j < m; ++j)
+                    a[j] = sq_relu(a[j]);
+                if (out->h)
+                    memcpy(out->h + (r * K + k) * m, a, sizeof(double) * (size_t)m);
+                matvec(a, w->w2, e * m * l, m, l, bf, o);
+                if (out->o)
+                    memcpy(out->o + (r * K + k) * l, o, sizeof(double) * (size_t)l);
+                for (int64_t j = 0; j < l; ++j)
+                    u[j] += g[k] * o[j];
+            }
+            if (out->u)
+                memcpy(out->u + r * l, u, sizeof(double) * (size_t)l);
+
+            /* 7. up-projection once, plus the unweighted shared experts */
+            matvec(u, w->w_up, 0, l, d, bf, y);
+            for (int64_t sh = 0; sh < S; ++sh) {
+                matvec(x, w->w1_s, sh * d * ms, d, ms, bf, a);
+                for (int64_t j = 0; j < ms; ++j)
+                    a[j] = sq_relu(a[j]);
+                if (out->hs)
+                    memcpy(out->hs + r * S * ms + sh * ms, a, sizeof(double) * (size_t)ms);
+                matvec(a, w->w2_s, sh * ms * d, ms, d, bf, tmp);
+                for (int64_t i = 0; i < d; ++i)
+                    y[i] += tmp[i];
+            }
+            if (out->y)
+                memcpy(out->y + r * d, y, sizeof(double) * (size_t)d);
+        }
+        free(x); free(s); free(sel); free(g); free(taken); free(z);
+        free(a); free(o); free(u); free(y); free(tmp);
+    }
+    return err ? -3 : 0;
+}
+
+/* Step 3 on given scores (for example a GPU's float32 logits widened to
+ * double): idx[t, :] for every row of s[T, N']. */
+int orc_select(const double *s, int64_t T, int64_t N, int64_t K, int32_t *idx)
+{
+    if (!s || !idx || N <= 0 || K <= 0 || K > N)
+        return -1;
+    unsigned char *taken = malloc((size_t)N);
+    if (!taken)
+        return -1;
+    int err = 0;
+    for (int64_t t = 0; t < T && !err; ++t)
+        err = select_topk(s + t * N, N, K, idx + t * K, taken);
+    free(taken);
+    return err;
+}
+
+/* Steps 2 + 4 on given scores and indices. */
+int orc_gates(const double *s, int64_t T, int64_t N, const int32_t *idx,
+              int64_t K, double *g)
+{
+    if (!s || !idx || !g || N <= 0 || K <= 0 || K > N)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        gates(s + t * N, N, idx + t * K, K, g + t * K);
+    return 0;
+}
+
+/* Step 8: counts[e], offsets[e] (exclusive scan, offsets[N] = T*K),
+ * pos[t, k] = offsets[e] + #{t' < t : e in idx[t']} and perm[pos] = t.
+ * Fails on an index out of range or an expert repeated within a token. */
+int orc_dispatch(const int32_t *idx, int64_t T, int64_t K, int64_t N,
+                 int32_t *counts, int32_t *offsets, int32_t *pos, int32_t *perm)
+{
+    if (!idx || !counts || !offsets || !pos || !perm || N <= 0 || K <= 0)
+        return -1;
+    for (int64_t e = 0; e < N; ++e)
+        counts[e] = 0;
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t k = 0; k < K; ++k) {
+            const int32_t e = idx[t * K + k];
+            if (e < 0 || e >= N)
+                return -2;
+            for (int64_t j = 0; j < k; ++j)
+                if (idx[t * K + j] == e)
+                    return -3;
+            counts[e] += 1;
+        }
+    int64_t run = 0;
+    for (int64_t e = 0; e < N; ++e) {
+        offsets[e] = (int32_t)run;
+        run += counts[e];
+    }
+    offsets[N] = (int32_t)run;
+    int32_t *fill = malloc(sizeof(int32_t) * (size_t)N);
+    if (!fill)
+        return -1;
+    for (int64_t e = 0; e < N; ++e)
+        fill[e] = offsets[e];
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t k = 0; k < K; ++k) {
+            const int32_t e = idx[t * K + k];
+            const int32_t p = fill[e]++;
+            pos[t * K + k] = p;
+            perm[p] = (int32_t)t;
+        }
+    free(fill);
+    return 0;
+}
+
+int orc_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,65 @@
+"""Small helpers shared by the tests (no layer arithmetic here)."""
+
+import numpy as np
+
+from synth import LayerShape, Workload
+from synth.generate import f32_to_bf16_bits
+
+
+def shape(name="custom", T=8, d=8, l=4, m=6, n_experts=4, top_k=2, n_shared=1,
+          m_shared=5, alpha=2, variant="acc", dtype="f32", seed=0, zipf_s=None):
+    return LayerShape(name, T=T, d=d, l=l, m=m, n_experts=n_experts, top_k=top_k,
+                      n_shared=n_shared, m_shared=m_shared, alpha=alpha,
+                      variant=variant, dtype=dtype, seed=seed, zipf_s=zipf_s)
+
+
+def workload_from_arrays(sh: LayerShape, arrays: dict) -> Workload:
+    """Build a workload from float arrays (exactly representable in the
+    shape's dtype).  Missing shared banks become empty."""
+    t = {}
+    for k in ("x", "w_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s"):
+        a = np.asarray(arrays[k], dtype=np.float32)
+        if sh.dtype == "bf16":
+            bits = f32_to_bf16_bits(a)
+            assert np.array_equal((bits.astype(np.uint32) << 16).view(np.float32), a), k
+            t[k] = bits
+        else:
+            t[k] = np.ascontiguousarray(a)
+    b = arrays.get("b_router")
+    t["b_router"] = None if b is None else np.asarray(b, dtype=np.float32)
+    return Workload(sh, t)
+
+
+def random_arrays(sh: LayerShape, rng, scale=1.0):
+    """Random float32 inputs of the right shapes, N(0, scale^2/fan_in)."""
+    def nrm(shape, fan):
+        return (rng.standard_normal(shape) * scale / np.sqrt(fan)).astype(np.float32)
+    S = sh.n_shared
+    a = {
+        "x": rng.standard_normal((sh.T, sh.d)).astype(np.float32),
+        "w_router": nrm((sh.d, sh.n_experts), sh.d),
+        "w_down": nrm((sh.d, sh.l), sh.d),
+        "w1": nrm((sh.n_experts, sh.l, sh.m), sh.l),
+        "w2": nrm((sh.n_experts, sh.m, sh.l), sh.m),
+        "w_up": nrm((sh.l, sh.d), sh.l),
+        "w1_s": nrm((S, sh.d, sh.m_shared), sh.d),
+        "w2_s": nrm((S, sh.m_shared, sh.d), sh.m_shared),
+    }
+    if sh.has_bias:
+        a["b_router"] = rng.standard_normal(sh.n_experts).astype(np.float32)
+    if sh.dtype == "bf16":
+        from synth import round_to_bf16
+        a = {k: (round_to_bf16(v) if k != "b_router" else v) for k, v in a.items()}
+    return a
+
+
+def random_workload(sh: LayerShape, seed=0, scale=1.0) -> Workload:
+    return workload_from_arrays(sh, random_arrays(sh, np.random.default_rng(seed), scale))
+
+
+def near_tie_mask(logits: np.ndarray, K: int, gap: float = 1e-3) -> np.ndarray:
+    """True for tokens whose K-th and (K+1)-th largest scores differ by < gap."""
+    if K >= logits.shape[1]:
+        return np.zeros(logits.shape[0], dtype=bool)
+    srt = -np.sort(-logits, axis=1)
+    return (srt[:, K - 1] - srt[:, K]) < gap
