@@ -1,0 +1,786 @@
+// LatentMoE layer forward pass on MI355X (gfx950): host plan and C ABI.
+//
+// The layer is the one of the explainer page "LatentMoE: NVIDIA's Latent
+// Mixture of Experts Explained Through Equations, Architecture, Code and
+// ..." (Figures 3, 6, 8, 9; LatentMoE code block); see include/latentmoe.h.
+//
+// One forward is a fixed sequence of launches on the caller's stream, with
+// no host synchronisation (the grouped GEMMs read their tile tables from
+// device memory):
+//   0 router_topk        s = x W_r (+b), top-K', gates, chunk ranks/counts
+//   1 dispatch_scan      per-expert scan over 32-token chunks, counts
+//   2 dispatch_offsets   offsets, grouped-GEMM tile table
+//   3 dispatch_finalize  pos[t,k], perm_token[p]
+//   4 gemm_down_shared1  [z | h_s] = x [W_down | W1_s], relu^2 on the h_s part
+//   5 grouped_gemm1      H = relu(z[perm] W1_e)^2 per expert
+//   6 grouped_gemm2      Y = H W2_e per expert
+//   7 combine            u[t] = sum_k gate[t,k] Y[pos[t,k]], written over z
+//   8 gemm_up_shared2    y = [u | h_s] [W_up ; W2_s]
+// Stages 4 and 8 fold the always-on shared experts into the down- and
+// up-projection GEMMs: both read x (resp. produce y) at width d, so one pass
+// over x and one output write serve both paths.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "latentmoe.h"
+
+#include "combine.hpp"
+#include "common.hpp"
+#include "dispatch.hpp"
+#include "gemm.hpp"
+#include "repack.hpp"
+#include "router.hpp"
+
+using namespace lmoe;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+enum Stage {
+    ST_ROUTER = 0,
+    ST_SCAN,
+    ST_OFFSETS,
+    ST_FINALIZE,
+    ST_GEMM_DOWN,
+    ST_GEMM1,
+    ST_GEMM2,
+    ST_COMBINE,
+    ST_GEMM_UP,
+    ST_COUNT
+};
+
+const char *kStageNames[ST_COUNT] = {"router_topk",       "dispatch_scan",  "dispatch_offsets",
+                                     "dispatch_finalize", "gemm_down_shared1", "grouped_gemm1_relu2",
+                                     "grouped_gemm2",     "combine",        "gemm_up_shared2"};
+
+struct HipError {
+    hipError_t e;
+};
+
+inline void hip_check(hipError_t e)
+{
+    if (e != hipSuccess)
+        throw HipError{e};
+}
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Tile shapes.  Grouped GEMMs pick their M tile from the expected rows per
+// expert; both grouped GEMMs of one forward share it (one tile table).
+constexpr int kDenseBM = 128, kDenseBN = 128;
+constexpr int kGroupBN = 128;
+
+struct Plan {
+    int64_t d, l, m, ms, S, N, K, alpha, Tmax;
+    int dtype;      // latentmoe_dtype
+    int esize;      // bytes per element
+    int64_t ld_zh;  // l + S*ms: row of [z|u , h_s]
+    int64_t nchunks_max;
+    int64_t P_max;
+    int group_bm;
+    int64_t max_mtiles;
+};
+
+int choose_group_bm(int64_t T, int64_t K, int64_t N)
+{
+    (void)T;
+    (void)K;
+    (void)N;
+    return 64;
+}
+
+int64_t max_mtiles_for(int64_t P, int64_t N, int bm) { return (P + bm - 1) / bm + std::min<int64_t>(N, P); }
+
+}  // namespace
+
+struct latentmoe_handle {
+    latentmoe_config cfg;
+    Plan plan;
+    int device = 0;
+    // repacked weights (one allocation)
+    void *wbuf = nullptr;
+    void *wrT = nullptr, *wcat1T = nullptr, *w1T = nullptr, *w2T = nullptr, *wcat2T = nullptr;
+    float *bias = nullptr;
+    // workspace (one allocation)
+    void *ws = nullptr;
+    int *idx = nullptr, *rank = nullptr, *pos = nullptr, *perm = nullptr;
+    float *gate = nullptr;
+    int *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
+    int *tile_expert = nullptr, *tile_row0 = nullptr, *n_mtiles = nullptr;
+    void *zh = nullptr, *H = nullptr, *Yp = nullptr;
+    // profiling
+    bool prof = false;
+    int prof_cap = 0, prof_used = 0;
+    std::vector<hipEvent_t> ev;  // [prof_cap][ST_COUNT][2]
+    std::vector<int> ev_used;    // [prof_cap][ST_COUNT]
+};
+
+namespace {
+
+int validate(const latentmoe_config *c)
+{
+    if (!c)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->d <= 0 || c->l <= 0 || c->m <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->alpha <= 0 ||
+        c->n_shared < 0 || c->max_tokens <= 0)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->l * c->alpha != c->d)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->n_experts % c->alpha != 0 || c->top_k > c->n_experts)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->variant != LATENTMOE_VARIANT_ACC && c->variant != LATENTMOE_VARIANT_EFF)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->variant == LATENTMOE_VARIANT_ACC && c->top_k % c->alpha != 0)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->dtype != LATENTMOE_DTYPE_F32 && c->dtype != LATENTMOE_DTYPE_BF16)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->has_router_bias != 0 && c->has_router_bias != 1)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->n_shared > 0 && c->m_shared <= 0)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    // kernel support
+    if (c->d % 64 || c->l % 64 || c->m % 64 || (c->n_shared > 0 && c->m_shared % 64))
+        return LATENTMOE_ERR_UNSUPPORTED;
+    if (c->n_experts % 16 || c->n_experts > 1024 || c->top_k > 64)
+        return LATENTMOE_ERR_UNSUPPORTED;
+    const int64_t ms = c->n_shared > 0 ? c->m_shared : 0;
+    const int64_t P = c->max_tokens * c->top_k;
+    const int64_t widest = std::max<int64_t>({c->d, c->m, c->l + c->n_shared * ms});
+    if (P >= (int64_t(1) << 31) || c->max_tokens * widest >= (int64_t(1) << 40) || P * c->m >= (int64_t(1) << 40))
+        return LATENTMOE_ERR_UNSUPPORTED;
+    return LATENTMOE_OK;
+}
+
+Plan make_plan(const latentmoe_config *c)
+{
+    Plan p;
+    p.d = c->d;
+    p.l = c->l;
+    p.m = c->m;
+    p.S = c->n_shared;
+    p.ms = c->n_shared > 0 ? c->m_shared : 0;
+    p.N = c->n_experts;
+    p.K = c->top_k;
+    p.alpha = c->alpha;
+    p.Tmax = c->max_tokens;
+    p.dtype = c->dtype;
+    p.esize = c->dtype == LATENTMOE_DTYPE_BF16 ? 2 : 4;
+    p.ld_zh = p.l + p.S * p.ms;
+    p.nchunks_max = (p.Tmax + kRouterTokens - 1) / kRouterTokens;
+    p.P_max = p.Tmax * p.K;
+    // The tile table must hold the worst case of every BM the forward may pick.
+    p.group_bm = 16;
+    p.max_mtiles = max_mtiles_for(p.P_max, p.N, p.group_bm);
+    return p;
+}
+
+struct Layout {
+    int64_t off_idx, off_gate, off_rank, off_pos, off_perm, off_cc, off_cb, off_counts, off_offsets, off_te, off_tr,
+        off_nmt, off_zh, off_H, off_Yp, total;
+};
+
+Layout ws_layout(const Plan &p)
+{
+    Layout L;
+    int64_t o = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = o;
+        o = align_up(o + bytes, 256);
+        return at;
+    };
+    L.off_idx = take(4 * p.P_max);
+    L.off_gate = take(4 * p.P_max);
+    L.off_rank = take(4 * p.P_max);
+    L.off_pos = take(4 * p.P_max);
+    L.off_perm = take(4 * p.P_max);
+    L.off_cc = take(4 * p.nchunks_max * p.N);
+    L.off_cb = take(4 * p.nchunks_max * p.N);
+    L.off_counts = take(4 * p.N);
+    L.off_offsets = take(4 * (p.N + 1));
+    L.off_te = take(4 * p.max_mtiles);
+    L.off_tr = take(4 * p.max_mtiles);
+    L.off_nmt = take(4);
+    L.off_zh = take((int64_t)p.esize * p.Tmax * p.ld_zh);
+    L.off_H = take((int64_t)p.esize * p.P_max * p.m);
+    L.off_Yp = take((int64_t)p.esize * p.P_max * p.l);
+    L.total = o;
+    return L;
+}
+
+struct WLayout {
+    int64_t off_wr, off_c1, off_w1, off_w2, off_c2, off_bias, total;
+};
+
+WLayout w_layout(const Plan &p)
+{
+    WLayout L;
+    int64_t o = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = o;
+        o = align_up(o + bytes, 256);
+        return at;
+    };
+    const int64_t es = p.esize;
+    L.off_wr = take(es * p.N * p.d);
+    L.off_c1 = take(es * p.ld_zh * p.d);
+    L.off_w1 = take(es * p.N * p.m * p.l);
+    L.off_w2 = take(es * p.N * p.l * p.m);
+    L.off_c2 = take(es * p.d * p.ld_zh);
+    L.off_bias = take(4 * p.N);
+    L.total = o;
+    return L;
+}
+
+template <typename E>
+void launch_transpose(const void *src, int64_t R, int64_t C, int64_t batch, int64_t src_bstride, void *dst,
+                      int64_t dst_ld, int64_t dst_bstride, hipStream_t s)
+{
+    dim3 grid((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32), (unsigned)batch);
+    transpose_kernel<E><<<grid, dim3(256), 0, s>>>(static_cast<const E *>(src), R, C, src_bstride,
+                                                   static_cast<E *>(dst), dst_ld, dst_bstride);
+    hip_check(hipGetLastError());
+}
+
+template <typename E>
+void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t s)
+{
+    const Plan &p = h->plan;
+    char *base = static_cast<char *>(h->wbuf);
+    const WLayout L = w_layout(p);
+    E *wr = reinterpret_cast<E *>(base + L.off_wr);
+    E *c1 = reinterpret_cast<E *>(base + L.off_c1);
+    E *w1 = reinterpret_cast<E *>(base + L.off_w1);
+    E *w2 = reinterpret_cast<E *>(base + L.off_w2);
+    E *c2 = reinterpret_cast<E *>(base + L.off_c2);
+    // router W_r [d, N'] -> [N', d]
+    launch_transpose<E>(w->w_router, p.d, p.N, 1, 0, wr, p.d, 0, s);
+    // [W_down | W1_s] -> rows: W_down^T (l rows), then W1_s[j]^T (m_s rows each)
+    launch_transpose<E>(w->w_down, p.d, p.l, 1, 0, c1, p.d, 0, s);
+    if (p.S > 0)
+        launch_transpose<E>(w->w1_shared, p.d, p.ms, p.S, p.d * p.ms, c1 + p.l * p.d, p.d, p.ms * p.d, s);
+    // W1 [N', l, m] -> [N', m, l];  W2 [N', m, l] -> [N', l, m]
+    launch_transpose<E>(w->w1, p.l, p.m, p.N, p.l * p.m, w1, p.l, p.m * p.l, s);
+    launch_transpose<E>(w->w2, p.m, p.l, p.N, p.m * p.l, w2, p.m, p.l * p.m, s);
+    // [W_up ; W2_s] -> [d, l + S m_s]: row i holds W_up[:, i] then W2_s[j][:, i]
+    launch_transpose<E>(w->w_up, p.l, p.d, 1, 0, c2, p.ld_zh, 0, s);
+    if (p.S > 0)
+        launch_transpose<E>(w->w2_shared, p.ms, p.d, p.S, p.ms * p.d, c2 + p.l, p.ld_zh, p.ms, s);
+    h->wrT = wr;
+    h->wcat1T = c1;
+    h->w1T = w1;
+    h->w2T = w2;
+    h->wcat2T = c2;
+    h->bias = reinterpret_cast<float *>(base + L.off_bias);
+    if (h->cfg.has_router_bias)
+        hip_check(hipMemcpyAsync(h->bias, w->b_router, 4 * p.N, hipMemcpyDeviceToDevice, s));
+}
+
+// ---- kernel launch helpers -------------------------------------------------
+
+template <typename E, int BM, int BN, int WM, int WN, bool GROUPED>
+void set_gemm_smem()
+{
+    hip_check(hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_kernel<E, BM, BN, WM, WN, GROUPED>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)gemm_smem_bytes<E, BM, BN>()));
+}
+
+template <typename E, int BM, int BN, int WM, int WN>
+void launch_dense(const GemmParams &gp, hipStream_t s)
+{
+    const int64_t ntm = (gp.M + BM - 1) / BM, ntn = (gp.N + BN - 1) / BN;
+    const int64_t grid = align_up(ntm * ntn, 8);
+    gemm_kernel<E, BM, BN, WM, WN, false><<<dim3((unsigned)grid), dim3(256), gemm_smem_bytes<E, BM, BN>(), s>>>(gp);
+    hip_check(hipGetLastError());
+}
+
+template <typename E, int BM, int BN, int WM, int WN>
+void launch_grouped(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
+{
+    const int64_t ntn = (gp.N + BN - 1) / BN;
+    const int64_t grid = align_up(max_mtiles * ntn, 8);
+    gemm_kernel<E, BM, BN, WM, WN, true><<<dim3((unsigned)grid), dim3(256), gemm_smem_bytes<E, BM, BN>(), s>>>(gp);
+    hip_check(hipGetLastError());
+}
+
+template <typename E, int NSW>
+void launch_router_n(latentmoe_handle *h, const void *x, int T, float *logits, hipStream_t s)
+{
+    const Plan &p = h->plan;
+    constexpr int NPL = NSW >= 2 ? NSW / 2 : 1;
+    const int blocks = (T + kRouterTokens - 1) / kRouterTokens;
+    router_topk_kernel<E, NSW, NPL><<<dim3(blocks), dim3(256), router_smem_bytes((int)p.N, (int)p.K), s>>>(
+        static_cast<const E *>(x), static_cast<const E *>(h->wrT), h->cfg.has_router_bias ? h->bias : nullptr, T,
+        (int)p.d, (int)p.N, (int)p.K, logits, h->idx, h->gate, h->rank, h->chunk_counts);
+    hip_check(hipGetLastError());
+}
+
+template <typename E, int NSW>
+void set_router_smem_n(int64_t bytes)
+{
+    constexpr int NPL = NSW >= 2 ? NSW / 2 : 1;
+    hip_check(hipFuncSetAttribute(reinterpret_cast<const void *>(router_topk_kernel<E, NSW, NPL>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes));
+}
+
+int router_nsw(int64_t N)
+{
+    const int64_t need = (N + 31) / 32;
+    int nsw = 1;
+    while (nsw < need)
+        nsw *= 2;
+    return nsw;
+}
+
+template <typename E>
+void set_router_smem(const Plan &p)
+{
+    const int64_t bytes = router_smem_bytes((int)p.N, (int)p.K);
+    switch (router_nsw(p.N)) {
+    case 1: set_router_smem_n<E, 1>(bytes); break;
+    case 2: set_router_smem_n<E, 2>(bytes); break;
+    case 4: set_router_smem_n<E, 4>(bytes); break;
+    case 8: set_router_smem_n<E, 8>(bytes); break;
+    case 16: set_router_smem_n<E, 16>(bytes); break;
+    default: set_router_smem_n<E, 32>(bytes); break;
+    }
+}
+
+template <typename E>
+void launch_router(latentmoe_handle *h, const void *x, int T, float *logits, hipStream_t s)
+{
+    switch (router_nsw(h->plan.N)) {
+    case 1: launch_router_n<E, 1>(h, x, T, logits, s); break;
+    case 2: launch_router_n<E, 2>(h, x, T, logits, s); break;
+    case 4: launch_router_n<E, 4>(h, x, T, logits, s); break;
+    case 8: launch_router_n<E, 8>(h, x, T, logits, s); break;
+    case 16: launch_router_n<E, 16>(h, x, T, logits, s); break;
+    default: launch_router_n<E, 32>(h, x, T, logits, s); break;
+    }
+}
+
+template <typename E>
+void set_all_smem(const Plan &p)
+{
+    set_router_smem<E>(p);
+    set_gemm_smem<E, kDenseBM, kDenseBN, 2, 2, false>();
+    set_gemm_smem<E, 64, kGroupBN, 2, 2, true>();
+}
+
+// ---- the forward -----------------------------------------------------------
+
+struct StageTimer {
+    latentmoe_handle *h;
+    hipStream_t s;
+    int slot;
+    void begin(int st)
+    {
+        if (slot >= 0)
+            hip_check(hipEventRecord(h->ev[((size_t)slot * ST_COUNT + st) * 2], s));
+    }
+    void end(int st)
+    {
+        if (slot >= 0) {
+            hip_check(hipEventRecord(h->ev[((size_t)slot * ST_COUNT + st) * 2 + 1], s));
+            h->ev_used[(size_t)slot * ST_COUNT + st] = 1;
+        }
+    }
+};
+
+void copy2d(void *dst, int64_t dst_pitch, const void *src, int64_t src_pitch, int64_t width, int64_t rows,
+            hipStream_t s)
+{
+    hip_check(hipMemcpy2DAsync(dst, dst_pitch, src, src_pitch, width, rows, hipMemcpyDeviceToDevice, s));
+}
+
+template <typename E>
+void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_t s, const latentmoe_debug *dbg)
+{
+    const Plan &p = h->plan;
+    const int N = (int)p.N, K = (int)p.K;
+    const int64_t P = (int64_t)T * K;
+    const int nchunks = (T + kRouterTokens - 1) / kRouterTokens;
+    const int es = p.esize;
+    const int gbm = choose_group_bm(T, K, N);
+    const int64_t max_mt = max_mtiles_for(P, N, gbm);
+    StageTimer tm{h, s, -1};
+    if (h->prof && h->prof_used < h->prof_cap)
+        tm.slot = h->prof_used++;
+
+    // 0: router + top-K' + chunk ranks
+    tm.begin(ST_ROUTER);
+    launch_router<E>(h, x, T, dbg ? dbg->logits : nullptr, s);
+    tm.end(ST_ROUTER);
+    // 1-3: dispatch order
+    tm.begin(ST_SCAN);
+    chunk_scan_kernel<<<dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s>>>(h->chunk_counts, nchunks, N,
+                                                                            h->chunk_base, h->counts);
+    hip_check(hipGetLastError());
+    tm.end(ST_SCAN);
+    tm.begin(ST_OFFSETS);
+    expert_offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(h->counts, N, gbm, h->offsets, h->tile_expert,
+                                                         h->tile_row0, h->n_mtiles);
+    hip_check(hipGetLastError());
+    tm.end(ST_OFFSETS);
+    tm.begin(ST_FINALIZE);
+    finalize_kernel<<<dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s>>>(
+        h->idx, h->rank, h->chunk_base, h->offsets, T, K, N, kRouterTokens, h->pos, h->perm);
+    hip_check(hipGetLastError());
+    tm.end(ST_FINALIZE);
+
+    // 4: [z | h_s] = x [W_down | W1_s]
+    GemmParams g{};
+    g.A = x;
+    g.lda = p.d;
+    g.B = h->wcat1T;
+    g.ldb = p.d;
+    g.C = h->zh;
+    g.ldc = p.ld_zh;
+    g.M = T;
+    g.N = (int)p.ld_zh;
+    g.K = (int)p.d;
+    g.relu2_from = (int)p.l;
+    g.group_m = 8;
+    tm.begin(ST_GEMM_DOWN);
+    launch_dense<E, kDenseBM, kDenseBN, 2, 2>(g, s);
+    tm.end(ST_GEMM_DOWN);
+    if (dbg && dbg->z)
+        copy2d(dbg->z, es * p.l, h->zh, es * p.ld_zh, es * p.l, T, s);
+    if (dbg && dbg->h_shared && p.S > 0)
+        copy2d(dbg->h_shared, es * (p.ld_zh - p.l), static_cast<char *>(h->zh) + es * p.l, es * p.ld_zh,
+               es * (p.ld_zh - p.l), T, s);
+
+    // 5: H = relu(z[perm] W1_e)^2
+    GemmParams g1{};
+    g1.A = h->zh;
+    g1.lda = p.ld_zh;
+    g1.B = h->w1T;
+    g1.ldb = p.l;
+    g1.strideB = p.m * p.l;
+    g1.C = h->H;
+    g1.ldc = p.m;
+    g1.N = (int)p.m;
+    g1.K = (int)p.l;
+    g1.relu2_from = 0;
+    g1.gather = h->perm;
+    g1.tile_expert = h->tile_expert;
+    g1.tile_row0 = h->tile_row0;
+    g1.n_mtiles = h->n_mtiles;
+    g1.offsets = h->offsets;
+    tm.begin(ST_GEMM1);
+    launch_grouped<E, 64, kGroupBN, 2, 2>(g1, max_mt, s);
+    tm.end(ST_GEMM1);
+
+    // 6: Y = H W2_e
+    GemmParams g2 = g1;
+    g2.A = h->H;
+    g2.lda = p.m;
+    g2.B = h->w2T;
+    g2.ldb = p.m;
+    g2.strideB = p.l * p.m;
+    g2.C = h->Yp;
+    g2.ldc = p.l;
+    g2.N = (int)p.l;
+    g2.K = (int)p.m;
+    g2.relu2_from = 1 << 30;
+    g2.gather = nullptr;
+    tm.begin(ST_GEMM2);
+    launch_grouped<E, 64, kGroupBN, 2, 2>(g2, max_mt, s);
+    tm.end(ST_GEMM2);
+
+    // 7: u = sum_k gate Y[pos], written over z (z is dead after stage 5)
+    tm.begin(ST_COMBINE);
+    combine_kernel<E><<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s>>>(
+        static_cast<const E *>(h->Yp), h->pos, h->gate, T, K, (int)p.l, static_cast<E *>(h->zh), p.ld_zh);
+    hip_check(hipGetLastError());
+    tm.end(ST_COMBINE);
+
+    // 8: y = [u | h_s] [W_up ; W2_s]
+    GemmParams g3{};
+    g3.A = h->zh;
+    g3.lda = p.ld_zh;
+    g3.B = h->wcat2T;
+    g3.ldb = p.ld_zh;
+    g3.C = y;
+    g3.ldc = p.d;
+    g3.M = T;
+    g3.N = (int)p.d;
+    g3.K = (int)p.ld_zh;
+    g3.relu2_from = 1 << 30;
+    g3.group_m = 8;
+    tm.begin(ST_GEMM_UP);
+    launch_dense<E, kDenseBM, kDenseBN, 2, 2>(g3, s);
+    tm.end(ST_GEMM_UP);
+
+    if (dbg) {
+        if (dbg->idx)
+            hip_check(hipMemcpyAsync(dbg->idx, h->idx, 4 * P, hipMemcpyDeviceToDevice, s));
+        if (dbg->gate)
+            hip_check(hipMemcpyAsync(dbg->gate, h->gate, 4 * P, hipMemcpyDeviceToDevice, s));
+        if (dbg->counts)
+            hip_check(hipMemcpyAsync(dbg->counts, h->counts, 4 * p.N, hipMemcpyDeviceToDevice, s));
+        if (dbg->offsets)
+            hip_check(hipMemcpyAsync(dbg->offsets, h->offsets, 4 * (p.N + 1), hipMemcpyDeviceToDevice, s));
+        if (dbg->perm_token)
+            hip_check(hipMemcpyAsync(dbg->perm_token, h->perm, 4 * P, hipMemcpyDeviceToDevice, s));
+        if (dbg->pos)
+            hip_check(hipMemcpyAsync(dbg->pos, h->pos, 4 * P, hipMemcpyDeviceToDevice, s));
+        if (dbg->h)
+            hip_check(hipMemcpyAsync(dbg->h, h->H, (size_t)es * P * p.m, hipMemcpyDeviceToDevice, s));
+        if (dbg->y_perm)
+            hip_check(hipMemcpyAsync(dbg->y_perm, h->Yp, (size_t)es * P * p.l, hipMemcpyDeviceToDevice, s));
+        if (dbg->u)
+            copy2d(dbg->u, es * p.l, h->zh, es * p.ld_zh, es * p.l, T, s);
+    }
+}
+
+void free_handle(latentmoe_handle *h)
+{
+    if (!h)
+        return;
+    for (hipEvent_t e : h->ev)
+        if (e)
+            (void)hipEventDestroy(e);
+    if (h->wbuf)
+        (void)hipFree(h->wbuf);
+    if (h->ws)
+        (void)hipFree(h->ws);
+    delete h;
+}
+
+double log10_comb(double n, double k) { return (std::lgamma(n + 1) - std::lgamma(k + 1) - std::lgamma(n - k + 1)) / std::log(10.0); }
+
+}  // namespace
+
+extern "C" {
+
+const char *latentmoe_status_string(int status)
+{
+    switch (status) {
+    case LATENTMOE_OK: return "ok";
+    case LATENTMOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LATENTMOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LATENTMOE_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case LATENTMOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+int latentmoe_last_hip_error(void) { return g_last_hip_error; }
+
+int latentmoe_validate_config(const latentmoe_config *cfg) { return validate(cfg); }
+
+int latentmoe_workspace_bytes(const latentmoe_config *cfg, int64_t *bytes)
+{
+    const int st = validate(cfg);
+    if (st != LATENTMOE_OK)
+        return st;
+    if (!bytes)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    const Plan p = make_plan(cfg);
+    *bytes = ws_layout(p).total + w_layout(p).total;
+    return LATENTMOE_OK;
+}
+
+int latentmoe_cost(const latentmoe_config *c, latentmoe_cost_out *o)
+{
+    const int st = validate(c);
+    if (st != LATENTMOE_OK)
+        return st;
+    if (!o)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    const double d = (double)c->d, l = (double)c->l, m = (double)c->m, N = (double)c->n_experts,
+                 K = (double)c->top_k, a = (double)c->alpha, S = (double)c->n_shared,
+                 ms = c->n_shared > 0 ? (double)c->m_shared : 0.0;
+    std::memset(o, 0, sizeof *o);
+    o->latent_expert_params = 2 * l * m;
+    o->routed_pool_params = N * 2 * l * m;
+    o->projection_params = 2 * d * l;
+    o->router_params = d * N;
+    o->shared_params = S * 2 * d * ms;
+    o->layer_params_excl_router = o->routed_pool_params + o->shared_params + o->projection_params;
+    o->active_params_per_token = K * 2 * l * m + o->shared_params + o->projection_params;
+    o->expert_bytes_per_token_fp8 = K * 2 * l * m;
+    o->expert_bytes_per_token_bf16 = K * 2 * l * m * 2;
+    o->a2a_bytes_per_token = K * l * (0.5 + 2.0);
+    o->flops_per_token = 2 * (d * N + 2 * d * l + 2 * K * l * m + 2 * S * d * ms);
+    o->log10_combinations = log10_comb(N, K);
+    const double Nb = N / a, Kb = c->variant == LATENTMOE_VARIANT_ACC ? K / a : K;
+    o->baseline_n_experts = Nb;
+    o->baseline_top_k = Kb;
+    o->baseline_expert_params = 2 * d * m;
+    o->baseline_layer_params_excl_router = Nb * 2 * d * m + o->shared_params;
+    o->baseline_active_params_per_token = Kb * 2 * d * m + o->shared_params;
+    o->baseline_a2a_bytes_per_token = Kb * d * (0.5 + 2.0);
+    o->baseline_log10_combinations = log10_comb(Nb, Kb);
+    o->log10_combination_bound = a * o->baseline_log10_combinations;
+    return LATENTMOE_OK;
+}
+
+int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, void *hip_stream,
+                     latentmoe_handle **out)
+{
+    if (!out)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    const int st = validate(cfg);
+    if (st != LATENTMOE_OK)
+        return st;
+    if (!w || !w->w_router || !w->w_down || !w->w1 || !w->w2 || !w->w_up)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (cfg->n_shared > 0 && (!w->w1_shared || !w->w2_shared))
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (cfg->has_router_bias && !w->b_router)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    latentmoe_handle *h = new (std::nothrow) latentmoe_handle();
+    if (!h)
+        return LATENTMOE_ERR_OUT_OF_MEMORY;
+    h->cfg = *cfg;
+    h->plan = make_plan(cfg);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    try {
+        hip_check(hipGetDevice(&h->device));
+        const Plan &p = h->plan;
+        const WLayout WL = w_layout(p);
+        const Layout L = ws_layout(p);
+        if (hipMalloc(&h->wbuf, WL.total) != hipSuccess) {
+            (void)hipGetLastError();
+            free_handle(h);
+            return LATENTMOE_ERR_OUT_OF_MEMORY;
+        }
+        if (hipMalloc(&h->ws, L.total) != hipSuccess) {
+            (void)hipGetLastError();
+            free_handle(h);
+            return LATENTMOE_ERR_OUT_OF_MEMORY;
+        }
+        char *b = static_cast<char *>(h->ws);
+        h->idx = reinterpret_cast<int *>(b + L.off_idx);
+        h->gate = reinterpret_cast<float *>(b + L.off_gate);
+        h->rank = reinterpret_cast<int *>(b + L.off_rank);
+        h->pos = reinterpret_cast<int *>(b + L.off_pos);
+        h->perm = reinterpret_cast<int *>(b + L.off_perm);
+        h->chunk_counts = reinterpret_cast<int *>(b + L.off_cc);
+        h->chunk_base = reinterpret_cast<int *>(b + L.off_cb);
+        h->counts = reinterpret_cast<int *>(b + L.off_counts);
+        h->offsets = reinterpret_cast<int *>(b + L.off_offsets);
+        h->tile_expert = reinterpret_cast<int *>(b + L.off_te);
+        h->tile_row0 = reinterpret_cast<int *>(b + L.off_tr);
+        h->n_mtiles = reinterpret_cast<int *>(b + L.off_nmt);
+        h->zh = b + L.off_zh;
+        h->H = b + L.off_H;
+        h->Yp = b + L.off_Yp;
+        if (p.dtype == LATENTMOE_DTYPE_BF16) {
+            set_all_smem<bf16>(p);
+            repack_weights<bf16>(h, w, s);
+        } else {
+            set_all_smem<float>(p);
+            repack_weights<float>(h, w, s);
+        }
+        hip_check(hipStreamSynchronize(s));
+    } catch (const HipError &e) {
+        g_last_hip_error = (int)e.e;
+        free_handle(h);
+        return LATENTMOE_ERR_HIP;
+    } catch (const std::bad_alloc &) {
+        free_handle(h);
+        return LATENTMOE_ERR_OUT_OF_MEMORY;
+    }
+    *out = h;
+    return LATENTMOE_OK;
+}
+
+int latentmoe_forward(latentmoe_handle *h, const void *x, void *y, int64_t T, void *hip_stream,
+                      const latentmoe_debug *dbg)
+{
+    if (!h || !x || !y || T < 1 || T > h->plan.Tmax)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    const int64_t bytes = T * h->plan.d * h->plan.esize;
+    const char *xb = static_cast<const char *>(x);
+    const char *yb = static_cast<const char *>(y);
+    if (xb < yb + bytes && yb < xb + bytes)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    try {
+        if (h->plan.dtype == LATENTMOE_DTYPE_BF16)
+            forward_impl<bf16>(h, x, y, (int)T, s, dbg);
+        else
+            forward_impl<float>(h, x, y, (int)T, s, dbg);
+    } catch (const HipError &e) {
+        g_last_hip_error = (int)e.e;
+        return LATENTMOE_ERR_HIP;
+    }
+    return LATENTMOE_OK;
+}
+
+int latentmoe_destroy(latentmoe_handle *h)
+{
+    free_handle(h);
+    return LATENTMOE_OK;
+}
+
+int latentmoe_profile_begin(latentmoe_handle *h, int max_forwards)
+{
+    if (!h || max_forwards < 1 || max_forwards > 100000)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    try {
+        for (hipEvent_t e : h->ev)
+            if (e)
+                hip_check(hipEventDestroy(e));
+        h->ev.assign((size_t)max_forwards * ST_COUNT * 2, nullptr);
+        h->ev_used.assign((size_t)max_forwards * ST_COUNT, 0);
+        for (auto &e : h->ev)
+            hip_check(hipEventCreate(&e));
+    } catch (const HipError &e) {
+        g_last_hip_error = (int)e.e;
+        return LATENTMOE_ERR_HIP;
+    }
+    h->prof = true;
+    h->prof_cap = max_forwards;
+    h->prof_used = 0;
+    return LATENTMOE_OK;
+}
+
+int latentmoe_profile_end(latentmoe_handle *h, double *ms, int32_t *launches, int32_t *n_stages)
+{
+    if (!h || !ms || !launches || !n_stages || !h->prof)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    for (int s = 0; s < LATENTMOE_MAX_STAGES; ++s) {
+        ms[s] = 0.0;
+        launches[s] = 0;
+    }
+    try {
+        for (int f = 0; f < h->prof_used; ++f)
+            for (int s = 0; s < ST_COUNT; ++s) {
+                if (!h->ev_used[(size_t)f * ST_COUNT + s])
+                    continue;
+                hipEvent_t a = h->ev[((size_t)f * ST_COUNT + s) * 2], b = h->ev[((size_t)f * ST_COUNT + s) * 2 + 1];
+                hip_check(hipEventSynchronize(b));
+                float t = 0.f;
+                hip_check(hipEventElapsedTime(&t, a, b));
+                ms[s] += t;
+                launches[s] += 1;
+            }
+    } catch (const HipError &e) {
+        g_last_hip_error = (int)e.e;
+        return LATENTMOE_ERR_HIP;
+    }
+    *n_stages = ST_COUNT;
+    h->prof = false;
+    return LATENTMOE_OK;
+}
+
+const char *latentmoe_stage_name(int stage)
+{
+    if (stage < 0 || stage >= ST_COUNT)
+        return "";
+    return kStageNames[stage];
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+"""Torch-facing wrapper around the C ABI: moves host arrays into device
+memory, passes pointers and the current HIP stream, and allocates outputs.
+No layer arithmetic happens here."""
+
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+from . import _abi
+
+_TORCH = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """float32 array, or uint16 array of bf16 bits, -> device tensor."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        assert dtype == "bf16"
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    if dtype == "bf16":
+        raise TypeError("bf16 tensors are passed as uint16 bit patterns")
+    return torch.from_numpy(a.astype(np.float32, copy=False)).to(device)
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclass
+class Shape:
+    d: int
+    l: int
+    m: int
+    n_experts: int
+    top_k: int
+    alpha: int
+    n_shared: int
+    m_shared: int
+    variant: str
+    dtype: str
+    has_bias: bool
+
+
+class LatentMoE:
+    """One configured layer on one device.
+
+    ``arrays``: x is not needed; w_router [d,N'], b_router [N'] (fp32, or
+    None), w_down [d,l], w1 [N',l,m], w2 [N',m,l], w_up [l,d],
+    w1_s [S,d,m_s], w2_s [S,m_s,d] as float32 or bf16-bit uint16 arrays.
+    """
+
+    def __init__(self, shape: Shape, arrays: Dict[str, np.ndarray], max_tokens: int, device="cuda:0"):
+        self.shape = shape
+        self.device = torch.device(device)
+        self.max_tokens = int(max_tokens)
+        self.tdtype = _TORCH[shape.dtype]
+        self.cfg = _abi.make_config(shape.d, shape.l, shape.m, shape.n_experts, shape.top_k, shape.alpha,
+                                    shape.n_shared, shape.m_shared, shape.variant, shape.dtype,
+                                    self.max_tokens, shape.has_bias)
+        dev = {}
+        for k in ("w_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s"):
+            if k in ("w1_s", "w2_s") and shape.n_shared == 0:
+                dev[k] = None
+                continue
+            dev[k] = to_device(arrays[k], shape.dtype, self.device)
+        b = arrays.get("b_router")
+        dev["b_router"] = (torch.from_numpy(np.asarray(b, np.float32)).to(self.device)
+                           if (shape.has_bias and b is not None) else None)
+
+        def ptr(t):
+            return None if t is None else t.data_ptr()
+
+        w = _abi.latentmoe_weights(ptr(dev["w_router"]), ptr(dev["b_router"]), ptr(dev["w_down"]),
+                                   ptr(dev["w1"]), ptr(dev["w2"]), ptr(dev["w_up"]), ptr(dev["w1_s"]),
+                                   ptr(dev["w2_s"]))
+        with torch.cuda.device(self.device):
+            self.handle = _abi.latentmoe_create(self.cfg, w, _stream_ptr(self.device))
+        del dev  # create copied the weights
+
+    @classmethod
+    def from_workload(cls, wl, max_tokens: Optional[int] = None, device="cuda:0") -> "LatentMoE":
+        sh = wl.shape
+        s = Shape(sh.d, sh.l, sh.m, sh.n_experts, sh.top_k, sh.alpha, sh.n_shared, sh.m_shared,
+                  sh.variant, sh.dtype, sh.has_bias)
+        return cls(s, wl.tensors, max_tokens or sh.T, device)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _abi.latentmoe_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                dbg: Optional[_abi.latentmoe_debug] = None) -> torch.Tensor:
+        assert x.is_contiguous() and x.dtype == self.tdtype and x.device == self.device
+        T = x.shape[0]
+        assert x.shape == (T, self.shape.d)
+        if y is None:
+            y = torch.empty_like(x)
+        _abi.latentmoe_forward(self.handle, x.data_ptr(), y.data_ptr(), T, _stream_ptr(self.device), dbg)
+        return y
+
+    def forward_debug(self, x: torch.Tensor, want=("logits", "idx", "gate", "counts", "offsets",
+                                                   "perm_token", "pos", "z", "h_shared", "h", "y_perm",
+                                                   "u")):
+        """Forward that also returns the intermediate results (device tensors)."""
+        s = self.shape
+        T = x.shape[0]
+        P = T * s.top_k
+        i32, f32, E = torch.int32, torch.float32, self.tdtype
+        shapes = {"logits": ((T, s.n_experts), f32), "idx": ((T, s.top_k), i32), "gate": ((T, s.top_k), f32),
+                  "counts": ((s.n_experts,), i32), "offsets": ((s.n_experts + 1,), i32),
+                  "perm_token": ((P,), i32), "pos": ((T, s.top_k), i32), "z": ((T, s.l), E),
+                  "h_shared": ((T, s.n_shared * s.m_shared), E), "h": ((P, s.m), E),
+                  "y_perm": ((P, s.l), E), "u": ((T, s.l), E)}
+        out = {k: torch.empty(*shapes[k][0], dtype=shapes[k][1], device=self.device) for k in want}
+        dbg = _abi.latentmoe_debug(*[(out[k].data_ptr() if k in out else None)
+                                     for k, _ in _abi.latentmoe_debug._fields_])
+        out["y"] = self.forward(x, dbg=dbg)
+        return out

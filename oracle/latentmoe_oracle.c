@@ -228,6 +228,10 @@ int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
             if (out->gate)
                 memcpy(out->gate + r * K, g, sizeof(double) * (size_t)K);
 
+            /* Routing outputs only: the remaining steps are skipped. */
+            if (!out->z && !out->h && !out->o && !out->u && !out->hs && !out->y)
+                continue;
+
             /* 5. shared down-projection */
             matvec(x, w->w_down, 0, d, l, bf, z);
             if (out->z)

@@ -1,0 +1,147 @@
+"""GPU parity: the HIP layer (through the C ABI) against the fp64 oracle on
+the same seeded inputs (the oracle never sees anything the GPU computed).
+
+  * routing: the GPU's fp32 scores within DELTA/2 of the oracle's; on every
+    token whose oracle top-(K'+1) scores are DELTA apart, the same experts in
+    the same slot order and the same gates; elsewhere a valid top-K';
+  * dispatch: its defining properties, and bit-exact against the oracle's
+    counting sort whenever routing agrees on every token;
+  * every intermediate (z, h_s, H, Y, u) on decided tokens;
+  * the layer output: max |y - y_oracle| <= 2e-2 RMS(y_oracle) for bf16,
+    1e-4 for fp32, excluding tokens whose K'-th and (K'+1)-th oracle scores
+    are closer than 1e-3.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_layer_latentmoe_amd import _abi
+from mixture_experts_layer_latentmoe_amd.layer import LatentMoE, to_device
+from oracle import oracle
+from synth import get_config, make_workload
+from tests import gpu_util as G
+from tests.helpers import random_arrays, random_workload, shape, workload_from_arrays
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _abi.lib()  # the HIP library must be there; raises otherwise
+
+
+def _full_check(wl, n_sample=None):
+    return G.full_check(wl, n_sample)
+
+
+def test_tiny_f32_all_tokens():
+    _full_check(make_workload(get_config("tiny_f32")))
+
+
+def test_readme_weights_ragged_tokens():
+    """300 tokens: several 32-token router chunks and a ragged tail."""
+    _full_check(make_workload(get_config("readme_acc"), T=300))
+
+
+def test_zipf_bias_ragged_tokens():
+    _full_check(make_workload(get_config("zipf_skew"), T=231))
+
+
+@pytest.mark.parametrize("name,n_sample", [("readme_acc", 48), ("decode_eff", 64),
+                                           ("wide_prefill", 32), ("zipf_skew", 40)])
+def test_full_size(name, n_sample):
+    """Full-size workloads: routing and dispatch bit-exact on every token,
+    output and intermediates on a sample of tokens."""
+    _full_check(make_workload(get_config(name)), n_sample=n_sample)
+
+
+def test_single_token():
+    _full_check(make_workload(get_config("readme_acc"), T=1))
+
+
+def test_one_handle_many_token_counts():
+    wl = make_workload(get_config("tiny_f32"))
+    layer = LatentMoE.from_workload(wl, max_tokens=256)
+    try:
+        for T in (256, 17, 1, 100):
+            sub = wl.with_x(np.ascontiguousarray(wl.tensors["x"][:T]))
+            out = G.run_gpu(sub, layer=layer)
+            G.check_routing(out, sub, G.oracle_routing(sub))
+            toks = np.arange(T)
+            ref = oracle.forward(sub, want=("logits", "y"))
+            G.check_output(out, sub, ref, toks)
+    finally:
+        layer.close()
+
+
+def test_zero_router_ties_fill_first_experts():
+    """W_r = 0: every score ties, so every token takes experts 0..K'-1 with
+    gates 1/K' and four experts hold all 1000 tokens (many tiles each)."""
+    sh = shape(T=1000, d=256, l=128, m=192, n_experts=32, top_k=4, n_shared=1, m_shared=128,
+               dtype="bf16")
+    arr = random_arrays(sh, np.random.default_rng(3))
+    arr["w_router"] = np.zeros_like(arr["w_router"])
+    wl = workload_from_arrays(sh, arr)
+    out = G.run_gpu(wl)
+    # exact ties everywhere: the index rule decides, on both sides
+    assert np.all(out["logits"] == 0.0)
+    assert np.all(out["idx"] == np.arange(4, dtype=np.int32)[None, :])
+    assert np.all(out["gate"] == np.float32(0.25))
+    G.check_dispatch_properties(out, 4, 32)
+    ref_route = G.oracle_routing(wl)
+    assert np.array_equal(ref_route.idx, out["idx"])
+    dp = oracle.dispatch(ref_route.idx, 32)
+    assert np.array_equal(out["pos"], dp.pos) and np.array_equal(out["perm_token"], dp.perm)
+    toks = G.sample_tokens(1000, 50)
+    ref = oracle.forward(wl, tokens=toks, want=("logits", "idx", "gate", "z", "h", "o", "u", "hs", "y"))
+    G.check_stages(out, wl, ref, toks, np.ones(len(toks), dtype=bool))
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=70, d=128, l=64, m=128, n_experts=16, top_k=1, n_shared=1, m_shared=64, alpha=2, variant="eff"),
+    dict(T=45, d=128, l=64, m=64, n_experts=16, top_k=16, n_shared=1, m_shared=64, alpha=2, variant="eff"),
+    dict(T=64, d=128, l=64, m=128, n_experts=32, top_k=4, n_shared=0, m_shared=0, alpha=2),
+    dict(T=99, d=256, l=64, m=320, n_experts=64, top_k=8, n_shared=3, m_shared=192, alpha=4),
+    dict(T=40, d=128, l=128, m=64, n_experts=16, top_k=2, n_shared=1, m_shared=64, alpha=1),
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_shape_edge_cases(cfg, dtype):
+    """K' = 1, K' = N', no shared expert, odd tile multiples, alpha = 1."""
+    sh = shape(dtype=dtype, **cfg)
+    _full_check(random_workload(sh, seed=cfg["T"]))
+
+
+def test_deterministic_bits():
+    wl = make_workload(get_config("readme_acc"), T=512)
+    layer = LatentMoE.from_workload(wl)
+    try:
+        a = G.run_gpu(wl, layer=layer)
+        b = G.run_gpu(wl, layer=layer)
+    finally:
+        layer.close()
+    for k in ("idx", "gate", "pos", "perm_token", "y", "h", "u"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_forward_argument_errors():
+    wl = make_workload(get_config("tiny_f32"), T=8)
+    layer = LatentMoE.from_workload(wl, max_tokens=8)
+    try:
+        x = to_device(wl.tensors["x"], "f32", "cuda:0")
+        y = torch.empty_like(x)
+        s = torch.cuda.current_stream().cuda_stream
+        L = _abi.lib()
+        import ctypes
+        for T in (0, 9, -1):
+            assert L.latentmoe_forward(ctypes.c_void_p(layer.handle), ctypes.c_void_p(x.data_ptr()),
+                                       ctypes.c_void_p(y.data_ptr()), T, ctypes.c_void_p(s), None) == \
+                _abi.LATENTMOE_ERR_INVALID_ARGUMENT
+        # in place (x and y overlap) is rejected
+        assert L.latentmoe_forward(ctypes.c_void_p(layer.handle), ctypes.c_void_p(x.data_ptr()),
+                                   ctypes.c_void_p(x.data_ptr()), 8, ctypes.c_void_p(s), None) == \
+            _abi.LATENTMOE_ERR_INVALID_ARGUMENT
+    finally:
+        layer.close()
