@@ -33,13 +33,15 @@ def stage_work(sh, T):
     es = 2 if sh.dtype == "bf16" else 4
     ldzh = sh.l + sh.n_shared * sh.m_shared
     return {
-        "router_topk": ("flop", 2.0 * T * sh.d * sh.n_experts),
-        "gemm_down_shared1": ("flop", 2.0 * T * sh.d * ldzh),
+        # one pass over x: router scores, z and the shared-expert hidden layer
+        "gemm_x_router_down_shared1": ("flop", 2.0 * T * sh.d * (sh.n_experts + ldzh)),
         "grouped_gemm1_relu2": ("flop", 2.0 * P * sh.l * sh.m),
         "grouped_gemm2": ("flop", 2.0 * P * sh.m * sh.l),
         "gemm_up_shared2": ("flop", 2.0 * T * ldzh * sh.d),
         # gather P rows of l, write T rows of l, read pos and gate
         "combine": ("byte", float(P * sh.l * es + T * sh.l * es + P * 8)),
+        # read the T x N' fp32 scores, write idx/gate/rank (12 bytes per slot)
+        "router_select": ("byte", float(T * sh.n_experts * 4 + P * 12)),
         "dispatch_scan": ("byte", None),
         "dispatch_offsets": ("byte", None),
         "dispatch_finalize": ("byte", None),

@@ -7,6 +7,7 @@
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace lmoe {
 
@@ -45,6 +46,34 @@ template <> struct Mfma<float> {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+        return c;
+    }
+};
+
+// 32x32 output tiles (v_mfma_f32_32x32x16_bf16 runs at the full dense rate on
+// gfx950; the 16x16x32 form measured at little more than half of it).
+// A lane's 16-byte fragment holds k = 8*(lane/32) .. +7 of a 16-wide bf16
+// step, or k = 4*(lane/32) + j of an 8-wide fp32 step (four
+// v_mfma_f32_32x32x2f32 issues, element j of every lane each).  Row (first
+// operand) / column (second operand) of the tile = lane % 32.
+// Output: lane l holds D[8*(q/4) + 4*(l/32) + q%4][l % 32], q = 0..15.
+template <typename E> struct Mfma32;
+
+template <> struct Mfma32<bf16> {
+    static __device__ __forceinline__ f32x16 run(const uint4 &a, const uint4 &b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+template <> struct Mfma32<float> {
+    static __device__ __forceinline__ f32x16 run(const uint4 &a, const uint4 &b, f32x16 c)
+    {
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
         return c;
     }
 };

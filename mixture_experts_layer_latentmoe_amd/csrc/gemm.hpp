@@ -9,14 +9,20 @@
 // at position c ^ (row & 7) so that both the 16-byte writes of a row and the
 // 16-row fragment reads of one chunk column hit distinct banks.
 //
+// Global loads are buffer loads: a row outside the valid range gets an
+// offset beyond the buffer's size, and the hardware returns zeros for it, so
+// the main loop has no branches.  The next k-tile is loaded into registers
+// while the current one is multiplied from LDS.
+//
 // Dense mode: rows = M; tiles walk grouped-by-M order inside each XCD.
 // Grouped mode (routed experts): the dispatch rows of expert e are the
 // contiguous range [offsets[e], offsets[e+1]); a device-built tile table
 // lists (expert, first row) for every BM-row tile, so no host round trip is
 // needed.  A rows may be gathered through `gather` (dispatch row -> token).
 //
-// Epilogue: columns >= relu2_from get relu(v)^2 (squared-ReLU expert
-// activation), then the result is rounded to E and stored.
+// Epilogue: the first c_split columns (router scores) are stored in fp32 with
+// a per-column bias; the rest go to C, where columns >= relu2_from get
+// relu(v)^2 (squared-ReLU expert activation), rounded to E.
 #pragma once
 
 #include "common.hpp"
@@ -26,13 +32,18 @@ namespace lmoe {
 struct GemmParams {
     const void *A;
     int64_t lda;        // elements
+    int64_t a_bytes;    // size of the A buffer in bytes (range of the loads)
     const void *B;      // B^T rows: [N][ldb]
     int64_t ldb;        // elements
     int64_t strideB;    // elements between experts (grouped)
-    void *C;
+    void *C;            // columns [c_split, N) go to C[row][col - c_split]
     int64_t ldc;        // elements
+    float *C32;         // columns [0, c_split) go to C32[row][col] in fp32 (+ bias32)
+    int64_t ldc32;
+    const float *bias32;  // nullable
+    int c_split;        // multiple of 4; 0: no fp32 part
     int M, N, K;        // M: dense rows (unused in grouped mode)
-    int relu2_from;     // first column that gets relu^2 (>= N: none)
+    int relu2_from;     // first column of C (after the split) that gets relu^2
     int group_m;        // dense: tiles of this many M-tiles are walked together
     // grouped mode
     const int *gather;       // dispatch row -> A row, or nullptr (A rows = dispatch rows)
@@ -42,20 +53,92 @@ struct GemmParams {
     const int *offsets;      // [N'+1] first dispatch row of each expert
 };
 
-template <typename E, int BM, int BN, int WM, int WN, bool GROUPED>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p)
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor over `bytes` bytes at p (loads past the end read 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes)
 {
-    static_assert(WM * WN == 4, "four waves per workgroup");
+    const int n = bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+constexpr unsigned kOOB = 0x80000000u;  // offset that is always out of range
+
+#define LMOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// vmcnt <= N and lgkmcnt == 0 (gfx9 s_waitcnt: vmcnt[3:0] + vmcnt[15:14],
+// expcnt[6:4] left at 7 = no wait, lgkmcnt[11:8])
+template <int N> __device__ __forceinline__ void wait_vm_lgkm0()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Multiply one LDS k-tile (128 bytes of K: four k-steps of 32 bytes) into the
+// wave's 32x32 accumulator tiles.
+template <typename E, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, const uint4 *b, int wm, int wn, int lane)
+{
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int c = s * 2 + (lane >> 5);
+        uint4 af[TM], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * WTM + i * 32 + (lane & 31);
+            af[i] = a[r * 8 + (c ^ (r & 7))];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int r = wn * WTN + j * 32 + (lane & 31);
+            bfr[j] = b[r * 8 + (c ^ (r & 7))];
+        }
+        // B fragment first: the tile's rows are output columns, so a lane
+        // owns runs of 4 consecutive output columns of output row lane % 32.
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = Mfma32<E>::run(bfr[j], af[i], acc[i][j]);
+    }
+}
+
+// k-tile kt of A and B straight into LDS (buffer loads with the LDS bit: lane
+// l of a wave writes 16 bytes at the wave's base + 16 l; rows out of range
+// read as zeros).  Position P of a tile holds row P / 8, chunk
+// (P % 8) ^ (row % 8); instruction i of wave w fills positions
+// (i * NW + w) * 64 .. +63.
+#define LMOE_TILE_DMA(SA, SB, KOFF)                                                                       \
+    {                                                                                                      \
+        _Pragma("unroll") for (int i_ = 0; i_ < NIA; ++i_) __builtin_amdgcn_raw_ptr_buffer_load_lds(       \
+            ra_rsrc, LMOE_LDS((SA) + (i_ * NW + wave) * 64), 16, a_off[i_] + (KOFF), 0, 0, 0);              \
+        _Pragma("unroll") for (int i_ = 0; i_ < NIB; ++i_) __builtin_amdgcn_raw_ptr_buffer_load_lds(       \
+            rb_rsrc, LMOE_LDS((SB) + (i_ * NW + wave) * 64), 16, b_off[i_] + (KOFF), 0, 0, 0);              \
+    }
+
+// NT = 64 * WM * WN threads; NS LDS stages (2 or 3), one barrier per k-tile;
+// tiles kt+1 .. kt+NS-1 are in flight while tile kt is multiplied.
+template <typename E, int BM, int BN, int WM, int WN, int NS, bool GROUPED, int MINB = 1>
+__global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmParams p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+    constexpr int NW = WM * WN, NT = 64 * NW;
     constexpr int VEC = 16 / (int)sizeof(E);    // elements per 16-byte chunk
     constexpr int BK = 8 * VEC;                 // elements per k-tile
     constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
-    constexpr int TM = WTM / 16, TN = WTN / 16; // 16x16 MFMA tiles per wave
-    constexpr int ACH = BM * 8 / 256, BCH = BN * 8 / 256;
-    static_assert(TM >= 1 && TN >= 1 && ACH >= 1 && BCH >= 1, "tile shape");
+    constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
+    constexpr int NIA = BM * 8 / NT, NIB = BN * 8 / NT;  // LDS-DMA instructions per thread
+    static_assert(TM >= 1 && TN >= 1 && NIA >= 1 && NIB >= 1, "tile shape");
+    static_assert(NIA * NT == BM * 8 && NIB * NT == BN * 8, "tile shape");
+    static_assert(NS == 2 || NS == 3, "stages");
 
-    extern __shared__ uint4 smem[];
-    uint4 *sA = smem;                 // [2][BM * 8]
-    uint4 *sB = smem + 2 * BM * 8;    // [2][BN * 8]
+    __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[NS > 2 ? BM * 8 : 1];
+    __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[NS > 2 ? BN * 8 : 1];
 
     const int ntn = (p.N + BN - 1) / BN;
     int tm, tn, rows_valid, expert = 0;
@@ -91,131 +174,124 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p)
     }
     const int n0 = tn * BN;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave - (wave / WN) * WN;
 
-    // Source addresses of this thread's chunks (fixed for the whole K loop).
-    const char *a_src[ACH];
-    const char *b_src[BCH];
-    const char *Abase = static_cast<const char *>(p.A);
-    const char *Bbase = static_cast<const char *>(p.B) + (int64_t)expert * p.strideB * (int64_t)sizeof(E);
+    // Buffer descriptors and this thread's source offsets (fixed for the K loop).
+    const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(p.A, p.a_bytes);
+    const char *Bexp = static_cast<const char *>(p.B) + (int64_t)expert * p.strideB * (int64_t)sizeof(E);
+    const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bexp, (int64_t)p.N * p.ldb * (int64_t)sizeof(E));
+    unsigned a_off[NIA], b_off[NIB];
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) {
-        const int q = tid + i * 256, r = q >> 3, c = q & 7;
-        a_src[i] = nullptr;
+    for (int i = 0; i < NIA; ++i) {
+        const int P = (i * NW + wave) * 64 + lane, r = P >> 3, c = (P & 7) ^ (r & 7);
+        a_off[i] = kOOB;
         if (r < rows_valid) {
             int64_t arow = row_base + r;
             if (GROUPED && p.gather)
                 arow = p.gather[arow];
-            a_src[i] = Abase + (arow * p.lda) * (int64_t)sizeof(E) + c * 16;
+            a_off[i] = (unsigned)(arow * p.lda * (int64_t)sizeof(E)) + c * 16;
         }
     }
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) {
-        const int q = tid + i * 256, r = q >> 3, c = q & 7;
-        b_src[i] = nullptr;
-        if (n0 + r < p.N)
-            b_src[i] = Bbase + ((int64_t)(n0 + r) * p.ldb) * (int64_t)sizeof(E) + c * 16;
+    for (int i = 0; i < NIB; ++i) {
+        const int P = (i * NW + wave) * 64 + lane, r = P >> 3, c = (P & 7) ^ (r & 7);
+        b_off[i] = (n0 + r < p.N) ? (unsigned)((int64_t)(n0 + r) * p.ldb * (int64_t)sizeof(E)) + c * 16 : kOOB;
     }
 
-    uint4 ra[ACH], rb[BCH];
-    const uint4 zero = make_uint4(0, 0, 0, 0);
-    auto gload = [&](int kt) {
-        const int64_t off = (int64_t)kt * 128;
-#pragma unroll
-        for (int i = 0; i < ACH; ++i)
-            ra[i] = a_src[i] ? *reinterpret_cast<const uint4 *>(a_src[i] + off) : zero;
-#pragma unroll
-        for (int i = 0; i < BCH; ++i)
-            rb[i] = b_src[i] ? *reinterpret_cast<const uint4 *>(b_src[i] + off) : zero;
-    };
-    auto sstore = [&](int st) {
-        uint4 *a = sA + st * BM * 8;
-        uint4 *b = sB + st * BN * 8;
-#pragma unroll
-        for (int i = 0; i < ACH; ++i) {
-            const int q = tid + i * 256, r = q >> 3, c = q & 7;
-            a[r * 8 + (c ^ (r & 7))] = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < BCH; ++i) {
-            const int q = tid + i * 256, r = q >> 3, c = q & 7;
-            b[r * 8 + (c ^ (r & 7))] = rb[i];
-        }
-    };
-
-    f32x4 acc[TM][TN];
+    f32x16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                acc[i][j][q] = 0.f;
 
+    constexpr int NI = NIA + NIB;
     const int nk = p.K / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < nk)
-            gload(kt + 1);
-        const uint4 *a = sA + st * BM * 8;
-        const uint4 *b = sB + st * BN * 8;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int c = s * 4 + (lane >> 4);
-            uint4 af[TM], bfr[TN];
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = wm * WTM + i * 16 + (lane & 15);
-                af[i] = a[r * 8 + (c ^ (r & 7))];
-            }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int r = wn * WTN + j * 16 + (lane & 15);
-                bfr[j] = b[r * 8 + (c ^ (r & 7))];
-            }
-            // B fragment first: lane l then owns 4 consecutive output columns
-            // (4*(l/16) + 0..3) of output row (l % 16).
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = Mfma<E>::run(bfr[j], af[i], acc[i][j]);
-        }
-        if (kt + 1 < nk)
-            sstore(st ^ 1);
-        __syncthreads();
+    LMOE_TILE_DMA(sA0, sB0, 0u)
+    if (NS > 2 && nk > 1)
+        LMOE_TILE_DMA(sA1, sB1, 128u)
+
+// One k-tile step: wait until tile kt is in LDS for every wave (and every
+// wave is done with the stage about to be refilled), refill it with tile
+// kt + NS - 1, multiply tile kt.
+#define LMOE_KSTEP(SA, SB, NA, NB)                                                                            \
+    {                                                                                                         \
+        if (NS > 2 && kt + 1 < nk)                                                                            \
+            wait_vm_lgkm0<NI>();                                                                              \
+        else                                                                                                  \
+            wait_vm_lgkm0<0>();                                                                               \
+        __builtin_amdgcn_s_barrier();                                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                                                    \
+        if (kt + NS - 1 < nk)                                                                                 \
+            LMOE_TILE_DMA(NA, NB, (unsigned)(kt + NS - 1) * 128u)                                          \
+        tile_mma<E, TM, TN, WTM, WTN>(acc, SA, SB, wm, wn, lane);                                            \
+        __builtin_amdgcn_sched_barrier(0);                                                                    \
+        if (++kt >= nk)                                                                                       \
+            break;                                                                                            \
     }
+
+    int kt = 0;
+    if constexpr (NS == 2) {
+        for (;;) {
+            LMOE_KSTEP(sA0, sB0, sA1, sB1)
+            LMOE_KSTEP(sA1, sB1, sA0, sB0)
+        }
+    } else {
+        for (;;) {
+            LMOE_KSTEP(sA0, sB0, sA2, sB2)
+            LMOE_KSTEP(sA1, sB1, sA0, sB0)
+            LMOE_KSTEP(sA2, sB2, sA1, sB1)
+        }
+    }
+#undef LMOE_KSTEP
+#undef LMOE_TILE_DMA
 
     E *C = static_cast<E *>(p.C);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-        const int rl = wm * WTM + i * 16 + (lane & 15);
+        const int rl = wm * WTM + i * 32 + (lane & 31);
         if (rl >= rows_valid)
             continue;
-        E *crow = C + (row_base + rl) * p.ldc;
+        const int64_t row = row_base + rl;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-            const int col = n0 + wn * WTN + j * 16 + 4 * (lane >> 4);
-            if (col >= p.N)
-                continue;
-            float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (col + r >= p.relu2_from) {
-                    const float t = fmaxf(v[r], 0.f);
-                    v[r] = t * t;
+            for (int g = 0; g < 4; ++g) {
+                const int col = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                if (col >= p.N)
+                    continue;
+                float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                if (col < p.c_split) {
+                    if (p.bias32) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] += p.bias32[col + r];
+                    }
+                    store4(p.C32 + row * p.ldc32 + col, v[0], v[1], v[2], v[3]);
+                    continue;
                 }
-            store4(crow + col, v[0], v[1], v[2], v[3]);
+                const int mc = col - p.c_split;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (mc + r >= p.relu2_from) {
+                        const float t = fmaxf(v[r], 0.f);
+                        v[r] = t * t;
+                    }
+                store4(C + row * p.ldc + mc, v[0], v[1], v[2], v[3]);
+            }
         }
     }
+#endif
 }
 
-template <typename E, int BM, int BN>
-constexpr size_t gemm_smem_bytes()
+template <int BM, int BN, int NS>
+constexpr size_t gemm_lds_bytes()
 {
-    return (size_t)2 * (BM + BN) * 8 * 16;
+    return (size_t)NS * (BM + BN) * 8 * 16;
 }
 
 }  // namespace lmoe

@@ -7,18 +7,20 @@
 // One forward is a fixed sequence of launches on the caller's stream, with
 // no host synchronisation (the grouped GEMMs read their tile tables from
 // device memory):
-//   0 router_topk        s = x W_r (+b), top-K', gates, chunk ranks/counts
-//   1 dispatch_scan      per-expert scan over 32-token chunks, counts
-//   2 dispatch_offsets   offsets, grouped-GEMM tile table
-//   3 dispatch_finalize  pos[t,k], perm_token[p]
-//   4 gemm_down_shared1  [z | h_s] = x [W_down | W1_s], relu^2 on the h_s part
-//   5 grouped_gemm1      H = relu(z[perm] W1_e)^2 per expert
-//   6 grouped_gemm2      Y = H W2_e per expert
-//   7 combine            u[t] = sum_k gate[t,k] Y[pos[t,k]], written over z
-//   8 gemm_up_shared2    y = [u | h_s] [W_up ; W2_s]
-// Stages 4 and 8 fold the always-on shared experts into the down- and
-// up-projection GEMMs: both read x (resp. produce y) at width d, so one pass
-// over x and one output write serve both paths.
+//   0 gemm_x            [s | z | h_s] = x [W_r | W_down | W1_s]: router scores
+//                       in fp32 (+ bias), z, and the squared-ReLU hidden layer of
+//                       the shared experts -- one MFMA pass over x
+//   1 router_select     top-K', gates, chunk ranks / counts
+//   2 dispatch_scan     per-expert scan over 32-token chunks, counts
+//   3 dispatch_offsets  offsets, grouped-GEMM tile table
+//   4 dispatch_finalize pos[t,k], perm_token[p]
+//   5 grouped_gemm1     H = relu(z[perm] W1_e)^2 per expert
+//   6 grouped_gemm2     Y = H W2_e per expert
+//   7 combine           u[t] = sum_k gate[t,k] Y[pos[t,k]], written over z
+//   8 gemm_up_shared2   y = [u | h_s] [W_up ; W2_s]
+// Stages 0 and 8 fold the router and the always-on shared experts into the
+// down- and up-projection GEMMs: all of them read x (resp. produce y) at
+// width d, so one pass over x and one output write serve every path.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -44,11 +46,11 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 enum Stage {
-    ST_ROUTER = 0,
+    ST_GEMM_X = 0,
+    ST_SELECT,
     ST_SCAN,
     ST_OFFSETS,
     ST_FINALIZE,
-    ST_GEMM_DOWN,
     ST_GEMM1,
     ST_GEMM2,
     ST_COMBINE,
@@ -56,9 +58,9 @@ enum Stage {
     ST_COUNT
 };
 
-const char *kStageNames[ST_COUNT] = {"router_topk",       "dispatch_scan",  "dispatch_offsets",
-                                     "dispatch_finalize", "gemm_down_shared1", "grouped_gemm1_relu2",
-                                     "grouped_gemm2",     "combine",        "gemm_up_shared2"};
+const char *kStageNames[ST_COUNT] = {"gemm_x_router_down_shared1", "router_select", "dispatch_scan",
+                                     "dispatch_offsets", "dispatch_finalize", "grouped_gemm1_relu2",
+                                     "grouped_gemm2", "combine", "gemm_up_shared2"};
 
 struct HipError {
     hipError_t e;
@@ -72,29 +74,18 @@ inline void hip_check(hipError_t e)
 
 inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// Tile shapes.  Grouped GEMMs pick their M tile from the expected rows per
-// expert; both grouped GEMMs of one forward share it (one tile table).
-constexpr int kDenseBM = 128, kDenseBN = 128;
-constexpr int kGroupBN = 128;
-
 struct Plan {
     int64_t d, l, m, ms, S, N, K, alpha, Tmax;
     int dtype;      // latentmoe_dtype
     int esize;      // bytes per element
     int64_t ld_zh;  // l + S*ms: row of [z|u , h_s]
+    int64_t n_x;    // N' + l + S*ms: output columns of the pass over x
     int64_t nchunks_max;
     int64_t P_max;
-    int group_bm;
-    int64_t max_mtiles;
+    int64_t max_mtiles;  // tile table capacity (smallest grouped M tile)
 };
 
-int choose_group_bm(int64_t T, int64_t K, int64_t N)
-{
-    (void)T;
-    (void)K;
-    (void)N;
-    return 64;
-}
+constexpr int kMinGroupBM = 32;
 
 int64_t max_mtiles_for(int64_t P, int64_t N, int bm) { return (P + bm - 1) / bm + std::min<int64_t>(N, P); }
 
@@ -106,12 +97,12 @@ struct latentmoe_handle {
     int device = 0;
     // repacked weights (one allocation)
     void *wbuf = nullptr;
-    void *wrT = nullptr, *wcat1T = nullptr, *w1T = nullptr, *w2T = nullptr, *wcat2T = nullptr;
+    void *wcat1T = nullptr, *w1T = nullptr, *w2T = nullptr, *wcat2T = nullptr;
     float *bias = nullptr;
     // workspace (one allocation)
     void *ws = nullptr;
     int *idx = nullptr, *rank = nullptr, *pos = nullptr, *perm = nullptr;
-    float *gate = nullptr;
+    float *gate = nullptr, *logits = nullptr;
     int *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
     int *tile_expert = nullptr, *tile_row0 = nullptr, *n_mtiles = nullptr;
     void *zh = nullptr, *H = nullptr, *Yp = nullptr;
@@ -155,6 +146,14 @@ int validate(const latentmoe_config *c)
     const int64_t widest = std::max<int64_t>({c->d, c->m, c->l + c->n_shared * ms});
     if (P >= (int64_t(1) << 31) || c->max_tokens * widest >= (int64_t(1) << 40) || P * c->m >= (int64_t(1) << 40))
         return LATENTMOE_ERR_UNSUPPORTED;
+    // every GEMM operand is addressed through a buffer descriptor with 32-bit
+    // offsets: each must stay below 2 GiB
+    const int64_t es = c->dtype == LATENTMOE_DTYPE_BF16 ? 2 : 4;
+    const int64_t ld_zh = c->l + c->n_shared * ms;
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    if (c->max_tokens * c->d * es > lim || c->max_tokens * ld_zh * es > lim || P * c->m * es > lim ||
+        (c->n_experts + ld_zh) * c->d * es > lim || c->d * ld_zh * es > lim || c->max_tokens * c->n_experts * 4 > lim)
+        return LATENTMOE_ERR_UNSUPPORTED;
     return LATENTMOE_OK;
 }
 
@@ -173,17 +172,16 @@ Plan make_plan(const latentmoe_config *c)
     p.dtype = c->dtype;
     p.esize = c->dtype == LATENTMOE_DTYPE_BF16 ? 2 : 4;
     p.ld_zh = p.l + p.S * p.ms;
+    p.n_x = p.N + p.ld_zh;
     p.nchunks_max = (p.Tmax + kRouterTokens - 1) / kRouterTokens;
     p.P_max = p.Tmax * p.K;
-    // The tile table must hold the worst case of every BM the forward may pick.
-    p.group_bm = 16;
-    p.max_mtiles = max_mtiles_for(p.P_max, p.N, p.group_bm);
+    p.max_mtiles = max_mtiles_for(p.P_max, p.N, kMinGroupBM);
     return p;
 }
 
 struct Layout {
     int64_t off_idx, off_gate, off_rank, off_pos, off_perm, off_cc, off_cb, off_counts, off_offsets, off_te, off_tr,
-        off_nmt, off_zh, off_H, off_Yp, total;
+        off_nmt, off_logits, off_zh, off_H, off_Yp, total;
 };
 
 Layout ws_layout(const Plan &p)
@@ -207,6 +205,7 @@ Layout ws_layout(const Plan &p)
     L.off_te = take(4 * p.max_mtiles);
     L.off_tr = take(4 * p.max_mtiles);
     L.off_nmt = take(4);
+    L.off_logits = take(4 * p.Tmax * p.N);
     L.off_zh = take((int64_t)p.esize * p.Tmax * p.ld_zh);
     L.off_H = take((int64_t)p.esize * p.P_max * p.m);
     L.off_Yp = take((int64_t)p.esize * p.P_max * p.l);
@@ -215,7 +214,7 @@ Layout ws_layout(const Plan &p)
 }
 
 struct WLayout {
-    int64_t off_wr, off_c1, off_w1, off_w2, off_c2, off_bias, total;
+    int64_t off_c1, off_w1, off_w2, off_c2, off_bias, total;
 };
 
 WLayout w_layout(const Plan &p)
@@ -228,8 +227,7 @@ WLayout w_layout(const Plan &p)
         return at;
     };
     const int64_t es = p.esize;
-    L.off_wr = take(es * p.N * p.d);
-    L.off_c1 = take(es * p.ld_zh * p.d);
+    L.off_c1 = take(es * p.n_x * p.d);
     L.off_w1 = take(es * p.N * p.m * p.l);
     L.off_w2 = take(es * p.N * p.l * p.m);
     L.off_c2 = take(es * p.d * p.ld_zh);
@@ -254,17 +252,16 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
     const Plan &p = h->plan;
     char *base = static_cast<char *>(h->wbuf);
     const WLayout L = w_layout(p);
-    E *wr = reinterpret_cast<E *>(base + L.off_wr);
     E *c1 = reinterpret_cast<E *>(base + L.off_c1);
     E *w1 = reinterpret_cast<E *>(base + L.off_w1);
     E *w2 = reinterpret_cast<E *>(base + L.off_w2);
     E *c2 = reinterpret_cast<E *>(base + L.off_c2);
-    // router W_r [d, N'] -> [N', d]
-    launch_transpose<E>(w->w_router, p.d, p.N, 1, 0, wr, p.d, 0, s);
-    // [W_down | W1_s] -> rows: W_down^T (l rows), then W1_s[j]^T (m_s rows each)
-    launch_transpose<E>(w->w_down, p.d, p.l, 1, 0, c1, p.d, 0, s);
+    // [W_r | W_down | W1_s] [d, N' + l + S m_s] -> K-contiguous rows:
+    // W_r^T (N' rows), W_down^T (l rows), then W1_s[j]^T (m_s rows each)
+    launch_transpose<E>(w->w_router, p.d, p.N, 1, 0, c1, p.d, 0, s);
+    launch_transpose<E>(w->w_down, p.d, p.l, 1, 0, c1 + p.N * p.d, p.d, 0, s);
     if (p.S > 0)
-        launch_transpose<E>(w->w1_shared, p.d, p.ms, p.S, p.d * p.ms, c1 + p.l * p.d, p.d, p.ms * p.d, s);
+        launch_transpose<E>(w->w1_shared, p.d, p.ms, p.S, p.d * p.ms, c1 + (p.N + p.l) * p.d, p.d, p.ms * p.d, s);
     // W1 [N', l, m] -> [N', m, l];  W2 [N', m, l] -> [N', l, m]
     launch_transpose<E>(w->w1, p.l, p.m, p.N, p.l * p.m, w1, p.l, p.m * p.l, s);
     launch_transpose<E>(w->w2, p.m, p.l, p.N, p.m * p.l, w2, p.m, p.l * p.m, s);
@@ -272,7 +269,6 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
     launch_transpose<E>(w->w_up, p.l, p.d, 1, 0, c2, p.ld_zh, 0, s);
     if (p.S > 0)
         launch_transpose<E>(w->w2_shared, p.ms, p.d, p.S, p.ms * p.d, c2 + p.l, p.ld_zh, p.ms, s);
-    h->wrT = wr;
     h->wcat1T = c1;
     h->w1T = w1;
     h->w2T = w2;
@@ -284,94 +280,67 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
 
 // ---- kernel launch helpers -------------------------------------------------
 
-template <typename E, int BM, int BN, int WM, int WN, bool GROUPED>
-void set_gemm_smem()
-{
-    hip_check(hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_kernel<E, BM, BN, WM, WN, GROUPED>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)gemm_smem_bytes<E, BM, BN>()));
-}
-
-template <typename E, int BM, int BN, int WM, int WN>
+template <typename E, int BM, int BN, int WM, int WN, int NS>
 void launch_dense(const GemmParams &gp, hipStream_t s)
 {
     const int64_t ntm = (gp.M + BM - 1) / BM, ntn = (gp.N + BN - 1) / BN;
     const int64_t grid = align_up(ntm * ntn, 8);
-    gemm_kernel<E, BM, BN, WM, WN, false><<<dim3((unsigned)grid), dim3(256), gemm_smem_bytes<E, BM, BN>(), s>>>(gp);
+    gemm_kernel<E, BM, BN, WM, WN, NS, false><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
     hip_check(hipGetLastError());
 }
 
-template <typename E, int BM, int BN, int WM, int WN>
+template <typename E, int BM, int BN, int WM, int WN, int NS>
 void launch_grouped(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
 {
     const int64_t ntn = (gp.N + BN - 1) / BN;
     const int64_t grid = align_up(max_mtiles * ntn, 8);
-    gemm_kernel<E, BM, BN, WM, WN, true><<<dim3((unsigned)grid), dim3(256), gemm_smem_bytes<E, BM, BN>(), s>>>(gp);
+    gemm_kernel<E, BM, BN, WM, WN, NS, true><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
     hip_check(hipGetLastError());
 }
 
-template <typename E, int NSW>
-void launch_router_n(latentmoe_handle *h, const void *x, int T, float *logits, hipStream_t s)
+// Dense GEMMs: 256x256 tiles (8 waves) when they come close to filling the
+// 256 CUs once, 128x128 (4 waves, two workgroups per CU) otherwise.
+template <typename E>
+void dense_gemm(const GemmParams &gp, hipStream_t s)
+{
+    const int64_t big = ((gp.M + 255) / 256) * ((gp.N + 255) / 256);
+    if (big >= 192)
+        launch_dense<E, 256, 256, 4, 2, 2>(gp, s);
+    else
+        launch_dense<E, 128, 128, 2, 2, 2>(gp, s);
+}
+
+constexpr int kGroupBM = 128;
+
+template <typename E>
+void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
+{
+    launch_grouped<E, kGroupBM, 128, 2, 2, 2>(gp, max_mtiles, s);
+}
+
+template <int NPL>
+void launch_select_n(latentmoe_handle *h, int T, hipStream_t s)
 {
     const Plan &p = h->plan;
-    constexpr int NPL = NSW >= 2 ? NSW / 2 : 1;
     const int blocks = (T + kRouterTokens - 1) / kRouterTokens;
-    router_topk_kernel<E, NSW, NPL><<<dim3(blocks), dim3(256), router_smem_bytes((int)p.N, (int)p.K), s>>>(
-        static_cast<const E *>(x), static_cast<const E *>(h->wrT), h->cfg.has_router_bias ? h->bias : nullptr, T,
-        (int)p.d, (int)p.N, (int)p.K, logits, h->idx, h->gate, h->rank, h->chunk_counts);
+    router_select_kernel<NPL><<<dim3(blocks), dim3(64 * kSelectWaves), router_select_smem_bytes((int)p.N, (int)p.K),
+                                s>>>(h->logits, T, (int)p.N, (int)p.K, h->idx, h->gate, h->rank, h->chunk_counts);
     hip_check(hipGetLastError());
 }
 
-template <typename E, int NSW>
-void set_router_smem_n(int64_t bytes)
+void launch_select(latentmoe_handle *h, int T, hipStream_t s)
 {
-    constexpr int NPL = NSW >= 2 ? NSW / 2 : 1;
-    hip_check(hipFuncSetAttribute(reinterpret_cast<const void *>(router_topk_kernel<E, NSW, NPL>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes));
-}
-
-int router_nsw(int64_t N)
-{
-    const int64_t need = (N + 31) / 32;
-    int nsw = 1;
-    while (nsw < need)
-        nsw *= 2;
-    return nsw;
-}
-
-template <typename E>
-void set_router_smem(const Plan &p)
-{
-    const int64_t bytes = router_smem_bytes((int)p.N, (int)p.K);
-    switch (router_nsw(p.N)) {
-    case 1: set_router_smem_n<E, 1>(bytes); break;
-    case 2: set_router_smem_n<E, 2>(bytes); break;
-    case 4: set_router_smem_n<E, 4>(bytes); break;
-    case 8: set_router_smem_n<E, 8>(bytes); break;
-    case 16: set_router_smem_n<E, 16>(bytes); break;
-    default: set_router_smem_n<E, 32>(bytes); break;
-    }
-}
-
-template <typename E>
-void launch_router(latentmoe_handle *h, const void *x, int T, float *logits, hipStream_t s)
-{
-    switch (router_nsw(h->plan.N)) {
-    case 1: launch_router_n<E, 1>(h, x, T, logits, s); break;
-    case 2: launch_router_n<E, 2>(h, x, T, logits, s); break;
-    case 4: launch_router_n<E, 4>(h, x, T, logits, s); break;
-    case 8: launch_router_n<E, 8>(h, x, T, logits, s); break;
-    case 16: launch_router_n<E, 16>(h, x, T, logits, s); break;
-    default: launch_router_n<E, 32>(h, x, T, logits, s); break;
-    }
-}
-
-template <typename E>
-void set_all_smem(const Plan &p)
-{
-    set_router_smem<E>(p);
-    set_gemm_smem<E, kDenseBM, kDenseBN, 2, 2, false>();
-    set_gemm_smem<E, 64, kGroupBN, 2, 2, true>();
+    const int64_t npl = (h->plan.N + 63) / 64;
+    if (npl <= 1)
+        launch_select_n<1>(h, T, s);
+    else if (npl <= 2)
+        launch_select_n<2>(h, T, s);
+    else if (npl <= 4)
+        launch_select_n<4>(h, T, s);
+    else if (npl <= 8)
+        launch_select_n<8>(h, T, s);
+    else
+        launch_select_n<16>(h, T, s);
 }
 
 // ---- the forward -----------------------------------------------------------
@@ -408,24 +377,52 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     const int64_t P = (int64_t)T * K;
     const int nchunks = (T + kRouterTokens - 1) / kRouterTokens;
     const int es = p.esize;
-    const int gbm = choose_group_bm(T, K, N);
-    const int64_t max_mt = max_mtiles_for(P, N, gbm);
+    const int64_t max_mt = max_mtiles_for(P, N, kGroupBM);
     StageTimer tm{h, s, -1};
     if (h->prof && h->prof_used < h->prof_cap)
         tm.slot = h->prof_used++;
 
-    // 0: router + top-K' + chunk ranks
-    tm.begin(ST_ROUTER);
-    launch_router<E>(h, x, T, dbg ? dbg->logits : nullptr, s);
-    tm.end(ST_ROUTER);
-    // 1-3: dispatch order
+    // 0: [s | z | h_s] = x [W_r | W_down | W1_s]
+    GemmParams g{};
+    g.A = x;
+    g.lda = p.d;
+    g.a_bytes = (int64_t)T * p.d * es;
+    g.B = h->wcat1T;
+    g.ldb = p.d;
+    g.C32 = h->logits;
+    g.ldc32 = p.N;
+    g.bias32 = h->cfg.has_router_bias ? h->bias : nullptr;
+    g.c_split = N;
+    g.C = h->zh;
+    g.ldc = p.ld_zh;
+    g.M = T;
+    g.N = (int)p.n_x;
+    g.K = (int)p.d;
+    g.relu2_from = (int)p.l;
+    g.group_m = 8;
+    tm.begin(ST_GEMM_X);
+    dense_gemm<E>(g, s);
+    tm.end(ST_GEMM_X);
+    if (dbg && dbg->logits)
+        hip_check(hipMemcpyAsync(dbg->logits, h->logits, 4 * (size_t)T * N, hipMemcpyDeviceToDevice, s));
+    if (dbg && dbg->z)
+        copy2d(dbg->z, es * p.l, h->zh, es * p.ld_zh, es * p.l, T, s);
+    if (dbg && dbg->h_shared && p.S > 0)
+        copy2d(dbg->h_shared, es * (p.ld_zh - p.l), static_cast<char *>(h->zh) + es * p.l, es * p.ld_zh,
+               es * (p.ld_zh - p.l), T, s);
+
+    // 1: top-K', gates, chunk ranks
+    tm.begin(ST_SELECT);
+    launch_select(h, T, s);
+    tm.end(ST_SELECT);
+    // 2-4: dispatch order
     tm.begin(ST_SCAN);
     chunk_scan_kernel<<<dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s>>>(h->chunk_counts, nchunks, N,
                                                                             h->chunk_base, h->counts);
     hip_check(hipGetLastError());
     tm.end(ST_SCAN);
     tm.begin(ST_OFFSETS);
-    expert_offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(h->counts, N, gbm, h->offsets, h->tile_expert,
+    expert_offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(h->counts, N, kGroupBM, h->offsets, h->tile_expert,
                                                          h->tile_row0, h->n_mtiles);
     hip_check(hipGetLastError());
     tm.end(ST_OFFSETS);
@@ -435,32 +432,11 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     hip_check(hipGetLastError());
     tm.end(ST_FINALIZE);
 
-    // 4: [z | h_s] = x [W_down | W1_s]
-    GemmParams g{};
-    g.A = x;
-    g.lda = p.d;
-    g.B = h->wcat1T;
-    g.ldb = p.d;
-    g.C = h->zh;
-    g.ldc = p.ld_zh;
-    g.M = T;
-    g.N = (int)p.ld_zh;
-    g.K = (int)p.d;
-    g.relu2_from = (int)p.l;
-    g.group_m = 8;
-    tm.begin(ST_GEMM_DOWN);
-    launch_dense<E, kDenseBM, kDenseBN, 2, 2>(g, s);
-    tm.end(ST_GEMM_DOWN);
-    if (dbg && dbg->z)
-        copy2d(dbg->z, es * p.l, h->zh, es * p.ld_zh, es * p.l, T, s);
-    if (dbg && dbg->h_shared && p.S > 0)
-        copy2d(dbg->h_shared, es * (p.ld_zh - p.l), static_cast<char *>(h->zh) + es * p.l, es * p.ld_zh,
-               es * (p.ld_zh - p.l), T, s);
-
     // 5: H = relu(z[perm] W1_e)^2
     GemmParams g1{};
     g1.A = h->zh;
     g1.lda = p.ld_zh;
+    g1.a_bytes = (int64_t)T * p.ld_zh * es;
     g1.B = h->w1T;
     g1.ldb = p.l;
     g1.strideB = p.m * p.l;
@@ -475,13 +451,14 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g1.n_mtiles = h->n_mtiles;
     g1.offsets = h->offsets;
     tm.begin(ST_GEMM1);
-    launch_grouped<E, 64, kGroupBN, 2, 2>(g1, max_mt, s);
+    grouped_gemm<E>(g1, max_mt, s);
     tm.end(ST_GEMM1);
 
     // 6: Y = H W2_e
     GemmParams g2 = g1;
     g2.A = h->H;
     g2.lda = p.m;
+    g2.a_bytes = P * p.m * es;
     g2.B = h->w2T;
     g2.ldb = p.m;
     g2.strideB = p.l * p.m;
@@ -492,7 +469,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g2.relu2_from = 1 << 30;
     g2.gather = nullptr;
     tm.begin(ST_GEMM2);
-    launch_grouped<E, 64, kGroupBN, 2, 2>(g2, max_mt, s);
+    grouped_gemm<E>(g2, max_mt, s);
     tm.end(ST_GEMM2);
 
     // 7: u = sum_k gate Y[pos], written over z (z is dead after stage 5)
@@ -506,6 +483,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     GemmParams g3{};
     g3.A = h->zh;
     g3.lda = p.ld_zh;
+    g3.a_bytes = (int64_t)T * p.ld_zh * es;
     g3.B = h->wcat2T;
     g3.ldb = p.ld_zh;
     g3.C = y;
@@ -516,7 +494,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g3.relu2_from = 1 << 30;
     g3.group_m = 8;
     tm.begin(ST_GEMM_UP);
-    launch_dense<E, kDenseBM, kDenseBN, 2, 2>(g3, s);
+    dense_gemm<E>(g3, s);
     tm.end(ST_GEMM_UP);
 
     if (dbg) {
@@ -673,16 +651,14 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
         h->tile_expert = reinterpret_cast<int *>(b + L.off_te);
         h->tile_row0 = reinterpret_cast<int *>(b + L.off_tr);
         h->n_mtiles = reinterpret_cast<int *>(b + L.off_nmt);
+        h->logits = reinterpret_cast<float *>(b + L.off_logits);
         h->zh = b + L.off_zh;
         h->H = b + L.off_H;
         h->Yp = b + L.off_Yp;
-        if (p.dtype == LATENTMOE_DTYPE_BF16) {
-            set_all_smem<bf16>(p);
+        if (p.dtype == LATENTMOE_DTYPE_BF16)
             repack_weights<bf16>(h, w, s);
-        } else {
-            set_all_smem<float>(p);
+        else
             repack_weights<float>(h, w, s);
-        }
         hip_check(hipStreamSynchronize(s));
     } catch (const HipError &e) {
         g_last_hip_error = (int)e.e;

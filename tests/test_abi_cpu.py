@@ -96,7 +96,8 @@ def test_status_strings():
     for s in range(5):
         assert _abi.status_string(s)
     assert _abi.status_string(99) == "unknown status"
-    assert _abi.latentmoe_stage_name(0) == "router_topk"
+    assert _abi.latentmoe_stage_name(0) == "gemm_x_router_down_shared1"
+    assert _abi.latentmoe_stage_name(1) == "router_select"
     assert _abi.latentmoe_stage_name(99) == ""
 
 
