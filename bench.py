@@ -43,7 +43,6 @@ def stage_work(sh, T):
         # read the T x N' fp32 scores, write idx/gate/rank (12 bytes per slot)
         "router_select": ("byte", float(T * sh.n_experts * 4 + P * 12)),
         "dispatch_scan": ("byte", None),
-        "dispatch_offsets": ("byte", None),
         "dispatch_finalize": ("byte", None),
     }
 

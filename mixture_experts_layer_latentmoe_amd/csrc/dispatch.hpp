@@ -12,11 +12,16 @@
 //   pos[t, k]     = offsets[e] + #{t' < t : e in idx[t']}
 //   perm_token[pos[t, k]] = t
 //
-// The router kernel already left, per 32-token chunk c, the count of every
-// expert (chunk_counts[c][e]) and each pair's rank inside its chunk.  Here:
-//   chunk_scan_kernel      chunk_base[c][e] = sum_{c' < c} chunk_counts[c'][e], counts[e]
-//   expert_offsets_kernel  offsets, and the tile table of the grouped GEMMs
-//   finalize_kernel        pos = offsets[e] + chunk_base[c][e] + rank; perm_token
+// The selection kernel already left, per 32-token chunk c, the count of every
+// expert (chunk_counts[e][c], expert-major) and each pair's rank inside its
+// chunk.  Here:
+//   chunk_scan_kernel  one wave per expert: chunk_base[e][c] = sum_{c' < c}
+//                      chunk_counts[e][c'] (wave prefix sums), counts[e]
+//   finalize_kernel    every workgroup scans counts into offsets in LDS, then
+//                      pos = offsets[e] + chunk_base[e][c] + rank and
+//                      perm_token[pos] = t; workgroup 0 also publishes offsets
+//                      and the (expert, first row) tile table of the grouped
+//                      GEMMs
 // All integer, no atomics: the same idx always gives the same bits.
 #pragma once
 
@@ -24,90 +29,106 @@
 
 namespace lmoe {
 
-// Workgroup of 256 threads per 64 experts; wave w scans a quarter of the chunks.
+__device__ __forceinline__ int wave_incl_scan(int v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o)
+            v += u;
+    }
+    return v;
+}
+
+// 4 waves per workgroup, one expert per wave; a wave walks the expert's row
+// of chunk counts 256 at a time (4 per lane, 16-byte loads).
 __global__ __launch_bounds__(256) void chunk_scan_kernel(const int *__restrict__ chunk_counts, int nchunks,
-                                                         int N, int *__restrict__ chunk_base,
+                                                         int ld_chunks, int N, int *__restrict__ chunk_base,
                                                          int *__restrict__ counts)
 {
-    __shared__ int part[4][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * 64 + lane;
-    const int per = (nchunks + 3) / 4;
-    const int c_begin = min(nchunks, wave * per), c_end = min(nchunks, c_begin + per);
-    int sum = 0;
-    if (e < N)
-        for (int c = c_begin; c < c_end; ++c)
-            sum += chunk_counts[(int64_t)c * N + e];
-    part[wave][lane] = sum;
-    __syncthreads();
-    int run = 0;
-    for (int w = 0; w < wave; ++w)
-        run += part[w][lane];
-    if (e < N) {
-        for (int c = c_begin; c < c_end; ++c) {
-            const int64_t o = (int64_t)c * N + e;
-            const int v = chunk_counts[o];
-            chunk_base[o] = run;
-            run += v;
-        }
-        if (wave == 3)
-            counts[e] = run;
-    }
-}
-
-// One workgroup of 1024 threads (N' <= 1024): exclusive scans of the counts
-// and of the BM-row tile counts, then the (expert, first row) tile table.
-__global__ __launch_bounds__(1024) void expert_offsets_kernel(const int *__restrict__ counts, int N, int BM,
-                                                              int *__restrict__ offsets,
-                                                              int *__restrict__ tile_expert,
-                                                              int *__restrict__ tile_row0,
-                                                              int *__restrict__ n_mtiles)
-{
-    __shared__ int sc[1024];
-    __shared__ int st[1024];
-    const int e = threadIdx.x;
-    const int c = (e < N) ? counts[e] : 0;
-    const int nt = (c + BM - 1) / BM;
-    sc[e] = c;
-    st[e] = nt;
-    __syncthreads();
-    // Hillis-Steele inclusive scans
-    for (int o = 1; o < 1024; o <<= 1) {
-        const int a = (e >= o) ? sc[e - o] : 0;
-        const int b = (e >= o) ? st[e - o] : 0;
-        __syncthreads();
-        sc[e] += a;
-        st[e] += b;
-        __syncthreads();
-    }
-    const int excl_c = sc[e] - c, excl_t = st[e] - nt;
-    if (e < N) {
-        offsets[e] = excl_c;
-        for (int j = 0; j < nt; ++j) {
-            tile_expert[excl_t + j] = e;
-            tile_row0[excl_t + j] = j * BM;
-        }
-    }
-    if (e == 0) {
-        offsets[N] = sc[1023];
-        *n_mtiles = st[1023];
-    }
-}
-
-__global__ __launch_bounds__(256) void finalize_kernel(const int *__restrict__ idx, const int *__restrict__ rank,
-                                                       const int *__restrict__ chunk_base,
-                                                       const int *__restrict__ offsets, int T, int K, int N,
-                                                       int chunk_tokens, int *__restrict__ pos,
-                                                       int *__restrict__ perm)
-{
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= (int64_t)T * K)
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= N)
         return;
-    const int t = (int)(q / K);
-    const int e = idx[q];
-    const int p = offsets[e] + chunk_base[(int64_t)(t / chunk_tokens) * N + e] + rank[q];
-    pos[q] = p;
-    perm[p] = t;
+    const int *src = chunk_counts + (int64_t)e * ld_chunks;
+    int *dst = chunk_base + (int64_t)e * ld_chunks;
+    int carry = 0;
+    for (int c0 = 0; c0 < nchunks; c0 += 256) {
+        const int c = c0 + lane * 4;
+        int4 v = make_int4(0, 0, 0, 0);
+        if (c < nchunks)  // ld_chunks is a multiple of 4; entries past nchunks are ignored
+            v = *reinterpret_cast<const int4 *>(src + c);
+        if (c + 1 >= nchunks) v.y = 0;
+        if (c + 2 >= nchunks) v.z = 0;
+        if (c + 3 >= nchunks) v.w = 0;
+        const int tot = v.x + v.y + v.z + v.w;
+        const int incl = wave_incl_scan(tot, lane);
+        const int ex = carry + incl - tot;
+        if (c < nchunks)
+            *reinterpret_cast<int4 *>(dst + c) = make_int4(ex, ex + v.x, ex + v.x + v.y, ex + v.x + v.y + v.z);
+        carry += __shfl(incl, 63, 64);
+    }
+    if (lane == 0)
+        counts[e] = carry;
+}
+
+// 1024 threads; N' <= 1024.
+__global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ idx, const int *__restrict__ rank,
+                                                       const int *__restrict__ chunk_base,
+                                                       const int *__restrict__ counts, int T, int K, int N,
+                                                       int chunk_tokens, int ld_chunks, int BM,
+                                                       int *__restrict__ offsets, int *__restrict__ tile_expert,
+                                                       int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
+                                                       int *__restrict__ pos, int *__restrict__ perm)
+{
+    __shared__ int s_off[1024];
+    __shared__ int s_wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = (tid < N) ? counts[tid] : 0;
+    // block-wide exclusive scan of counts
+    const int incl = wave_incl_scan(c, lane);
+    if (lane == 63)
+        s_wsum[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w)
+        before += s_wsum[w];
+    const int excl = before + incl - c;
+    s_off[tid] = excl;
+    __syncthreads();
+
+    if (blockIdx.x == 0) {
+        if (tid < N)
+            offsets[tid] = excl;
+        if (tid == N - 1)
+            offsets[N] = excl + c;
+        // tile table: same scan over the tile counts
+        const int nt = (c + BM - 1) / BM;
+        const int tincl = wave_incl_scan(nt, lane);
+        __syncthreads();
+        if (lane == 63)
+            s_wsum[wave] = tincl;
+        __syncthreads();
+        int tbefore = 0;
+        for (int w = 0; w < wave; ++w)
+            tbefore += s_wsum[w];
+        const int texcl = tbefore + tincl - nt;
+        for (int j = 0; j < nt; ++j) {
+            tile_expert[texcl + j] = tid;
+            tile_row0[texcl + j] = j * BM;
+        }
+        if (tid == 1023)
+            *n_mtiles = texcl + nt;
+    }
+
+    const int64_t P = (int64_t)T * K;
+    for (int64_t q = (int64_t)blockIdx.x * 1024 + tid; q < P; q += (int64_t)gridDim.x * 1024) {
+        const int t = (int)(q / K);
+        const int e = idx[q];
+        const int p = s_off[e] + chunk_base[(int64_t)e * ld_chunks + t / chunk_tokens] + rank[q];
+        pos[q] = p;
+        perm[p] = t;
+    }
 }
 
 }  // namespace lmoe

@@ -12,12 +12,11 @@
 //                       the shared experts -- one MFMA pass over x
 //   1 router_select     top-K', gates, chunk ranks / counts
 //   2 dispatch_scan     per-expert scan over 32-token chunks, counts
-//   3 dispatch_offsets  offsets, grouped-GEMM tile table
-//   4 dispatch_finalize pos[t,k], perm_token[p]
-//   5 grouped_gemm1     H = relu(z[perm] W1_e)^2 per expert
-//   6 grouped_gemm2     Y = H W2_e per expert
-//   7 combine           u[t] = sum_k gate[t,k] Y[pos[t,k]], written over z
-//   8 gemm_up_shared2   y = [u | h_s] [W_up ; W2_s]
+//   3 dispatch_finalize offsets, grouped-GEMM tile table, pos[t,k], perm_token[p]
+//   4 grouped_gemm1     H = relu(z[perm] W1_e)^2 per expert
+//   5 grouped_gemm2     Y = H W2_e per expert
+//   6 combine           u[t] = sum_k gate[t,k] Y[pos[t,k]], written over z
+//   7 gemm_up_shared2   y = [u | h_s] [W_up ; W2_s]
 // Stages 0 and 8 fold the router and the always-on shared experts into the
 // down- and up-projection GEMMs: all of them read x (resp. produce y) at
 // width d, so one pass over x and one output write serve every path.
@@ -49,7 +48,6 @@ enum Stage {
     ST_GEMM_X = 0,
     ST_SELECT,
     ST_SCAN,
-    ST_OFFSETS,
     ST_FINALIZE,
     ST_GEMM1,
     ST_GEMM2,
@@ -59,8 +57,8 @@ enum Stage {
 };
 
 const char *kStageNames[ST_COUNT] = {"gemm_x_router_down_shared1", "router_select", "dispatch_scan",
-                                     "dispatch_offsets", "dispatch_finalize", "grouped_gemm1_relu2",
-                                     "grouped_gemm2", "combine", "gemm_up_shared2"};
+                                     "dispatch_finalize", "grouped_gemm1_relu2", "grouped_gemm2",
+                                     "combine", "gemm_up_shared2"};
 
 struct HipError {
     hipError_t e;
@@ -81,6 +79,7 @@ struct Plan {
     int64_t ld_zh;  // l + S*ms: row of [z|u , h_s]
     int64_t n_x;    // N' + l + S*ms: output columns of the pass over x
     int64_t nchunks_max;
+    int64_t ld_chunks;  // row length of the expert-major chunk arrays (multiple of 4)
     int64_t P_max;
     int64_t max_mtiles;  // tile table capacity (smallest grouped M tile)
 };
@@ -174,6 +173,7 @@ Plan make_plan(const latentmoe_config *c)
     p.ld_zh = p.l + p.S * p.ms;
     p.n_x = p.N + p.ld_zh;
     p.nchunks_max = (p.Tmax + kRouterTokens - 1) / kRouterTokens;
+    p.ld_chunks = align_up(p.nchunks_max, 4);
     p.P_max = p.Tmax * p.K;
     p.max_mtiles = max_mtiles_for(p.P_max, p.N, kMinGroupBM);
     return p;
@@ -198,8 +198,8 @@ Layout ws_layout(const Plan &p)
     L.off_rank = take(4 * p.P_max);
     L.off_pos = take(4 * p.P_max);
     L.off_perm = take(4 * p.P_max);
-    L.off_cc = take(4 * p.nchunks_max * p.N);
-    L.off_cb = take(4 * p.nchunks_max * p.N);
+    L.off_cc = take(4 * p.ld_chunks * p.N);
+    L.off_cb = take(4 * p.ld_chunks * p.N);
     L.off_counts = take(4 * p.N);
     L.off_offsets = take(4 * (p.N + 1));
     L.off_te = take(4 * p.max_mtiles);
@@ -324,7 +324,8 @@ void launch_select_n(latentmoe_handle *h, int T, hipStream_t s)
     const Plan &p = h->plan;
     const int blocks = (T + kRouterTokens - 1) / kRouterTokens;
     router_select_kernel<NPL><<<dim3(blocks), dim3(64 * kSelectWaves), router_select_smem_bytes((int)p.N, (int)p.K),
-                                s>>>(h->logits, T, (int)p.N, (int)p.K, h->idx, h->gate, h->rank, h->chunk_counts);
+                                s>>>(h->logits, T, (int)p.N, (int)p.K, h->idx, h->gate, h->rank, h->chunk_counts,
+                                     (int)p.ld_chunks);
     hip_check(hipGetLastError());
 }
 
@@ -417,18 +418,17 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     tm.end(ST_SELECT);
     // 2-4: dispatch order
     tm.begin(ST_SCAN);
-    chunk_scan_kernel<<<dim3((unsigned)((N + 63) / 64)), dim3(256), 0, s>>>(h->chunk_counts, nchunks, N,
-                                                                            h->chunk_base, h->counts);
+    chunk_scan_kernel<<<dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s>>>(h->chunk_counts, nchunks, (int)p.ld_chunks,
+                                                                          N, h->chunk_base, h->counts);
     hip_check(hipGetLastError());
     tm.end(ST_SCAN);
-    tm.begin(ST_OFFSETS);
-    expert_offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(h->counts, N, kGroupBM, h->offsets, h->tile_expert,
-                                                         h->tile_row0, h->n_mtiles);
-    hip_check(hipGetLastError());
-    tm.end(ST_OFFSETS);
     tm.begin(ST_FINALIZE);
-    finalize_kernel<<<dim3((unsigned)((P + 255) / 256)), dim3(256), 0, s>>>(
-        h->idx, h->rank, h->chunk_base, h->offsets, T, K, N, kRouterTokens, h->pos, h->perm);
+    {
+        const int64_t blocks = std::min<int64_t>((P + 1023) / 1024, 256);
+        finalize_kernel<<<dim3((unsigned)blocks), dim3(1024), 0, s>>>(
+            h->idx, h->rank, h->chunk_base, h->counts, T, K, N, kRouterTokens, (int)p.ld_chunks, kGroupBM,
+            h->offsets, h->tile_expert, h->tile_row0, h->n_mtiles, h->pos, h->perm);
+    }
     hip_check(hipGetLastError());
     tm.end(ST_FINALIZE);
 

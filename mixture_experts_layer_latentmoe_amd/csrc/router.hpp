@@ -10,17 +10,19 @@
 // The scores s = x W_r (+ b) come from the same MFMA pass over x that
 // produces z and the shared-expert hidden layer (their weights are one
 // concatenated matrix), stored in fp32.  This kernel owns 32 tokens (one
-// dispatch chunk) with 8 waves:
-//   1. each wave selects the top K' of a row with K' rounds of a wave-wide
-//      maximum over 64-bit keys (order-preserving bits of the score, then the
-//      complemented expert index, so equal scores go to the lower index);
-//      -0.0 is folded into +0.0 first, so signed zeros tie;
-//   2. gate_k = exp(s_k - s_max) / sum_j exp(s_j - s_max) over the selected
+// dispatch chunk), 16 waves, two tokens per wave:
+//   1. scores become order-preserving 32-bit keys (-0.0 folded into +0.0, so
+//      signed zeros tie); a 32-round radix search, counting with wave ballots,
+//      finds the K'-th largest key; every key above it is selected, and of the
+//      keys equal to it the lowest expert indices fill the remaining slots;
+//   2. the selected keys are ranked (score descending, index ascending) by
+//      comparing each against the others through LDS;
+//   3. gate_k = exp(s_k - s_max) / sum_j exp(s_j - s_max) over the selected
 //      set, which is the renormalised softmax (its denominator cancels);
-//   3. a 32-bit mask per expert marks which tokens of the chunk chose it;
+//   4. a 32-bit mask per expert marks which tokens of the chunk chose it;
 //      popcounts give each (token, slot) its rank inside the chunk and the
 //      chunk's count per expert -- integer-exact, independent of the order of
-//      the atomic ORs.
+//      the atomic ORs.  Counts are stored expert-major: [N'][ld_chunks].
 #pragma once
 
 #include "common.hpp"
@@ -28,25 +30,16 @@
 namespace lmoe {
 
 constexpr int kRouterTokens = 32;
-constexpr int kSelectWaves = 8;
+constexpr int kSelectWaves = 16;
 
-__device__ __forceinline__ unsigned long long score_key(float v, int e)
+__device__ __forceinline__ unsigned ordered_key(float v)
 {
     v = (v == 0.f) ? 0.f : v;  // -0.0 and +0.0 tie
-    unsigned u = __float_as_uint(v);
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)u << 32) | (unsigned)(~(unsigned)e);
+    const unsigned u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // > 0 for every finite v
 }
 
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const unsigned long long q = __shfl_xor(k, o, 64);
-        k = q > k ? q : k;
-    }
-    return k;
-}
+__device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
 
 __device__ __forceinline__ float wave_sum_f32(float v)
 {
@@ -56,58 +49,96 @@ __device__ __forceinline__ float wave_sum_f32(float v)
     return v;
 }
 
-// NPL = ceil(N' / 64) scores held per lane.
+// NPL = ceil(N' / 64) scores held per lane (expert e = lane + 64 j).
 template <int NPL>
 __global__ __launch_bounds__(64 * kSelectWaves) void router_select_kernel(
     const float *__restrict__ scores, int T, int N, int K, int *__restrict__ idx_out, float *__restrict__ gate_out,
-    int *__restrict__ rank_out, int *__restrict__ chunk_counts)
+    int *__restrict__ rank_out, int *__restrict__ chunk_counts, int ld_chunks)
 {
     extern __shared__ int rsmem[];
-    int *s_idx = rsmem;                                            // [32][K]
+    int *s_idx = rsmem;                                                          // [32][K]
     unsigned *s_mask = reinterpret_cast<unsigned *>(rsmem + kRouterTokens * K);  // [N]
+    unsigned *s_key = s_mask + N;                                                // [16 waves][K]
+    int *s_exp = reinterpret_cast<int *>(s_key + kSelectWaves * K);              // [16 waves][K]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t0 = blockIdx.x * kRouterTokens;
     for (int e = tid; e < N; e += 64 * kSelectWaves)
         s_mask[e] = 0u;
+    unsigned *wkey = s_key + wave * K;
+    int *wexp = s_exp + wave * K;
+    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     for (int r = wave; r < kRouterTokens; r += kSelectWaves) {
         const int t = t0 + r;
         if (t >= T)
             break;
         const float *row = scores + (int64_t)t * N;
-        unsigned long long key[NPL];
+        unsigned key[NPL];
+        float val[NPL];
 #pragma unroll
         for (int j = 0; j < NPL; ++j) {
             const int e = lane + 64 * j;
-            key[j] = (e < N) ? score_key(row[e], e) : 0ull;
+            val[j] = (e < N) ? row[e] : 0.f;
+            key[j] = (e < N) ? ordered_key(val[j]) : 0u;
         }
-        unsigned long long mine = 0ull;
-        for (int k = 0; k < K; ++k) {
-            unsigned long long best = key[0];
+        // 1. the K'-th largest key: largest th with #{key >= th} >= K'
+        unsigned th = 0u;
+        for (int b = 31; b >= 0; --b) {
+            const unsigned cand = th | (1u << b);
+            int cnt = 0;
 #pragma unroll
-            for (int j = 1; j < NPL; ++j)
-                best = key[j] > best ? key[j] : best;
-            best = wave_max_u64(best);
-            if (lane == k)
-                mine = best;
-            const int e = (int)(~(unsigned)(best & 0xffffffffull));
-            if ((e & 63) == lane) {
+            for (int j = 0; j < NPL; ++j)
+                cnt += wave_count(key[j] >= cand);
+            if (cnt >= K)
+                th = cand;
+        }
+        int need = K;
 #pragma unroll
-                for (int j = 0; j < NPL; ++j)
-                    if (j == (e >> 6))
-                        key[j] = 0ull;
+        for (int j = 0; j < NPL; ++j)
+            need -= wave_count(key[j] > th);
+        // selection, compacted into LDS slots in (j, lane) order
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) {
+            const bool tie = key[j] == th;
+            const unsigned long long tmask = __ballot(tie);
+            const int tie_rank = __popcll(tmask & lt_mask);   // among this j's ties, lower lanes first
+            const bool sel = key[j] > th || (tie && tie_rank < need);
+            need -= min(need, (int)__popcll(tmask));
+            const unsigned long long smask = __ballot(sel);
+            if (sel) {
+                const int slot = base + __popcll(smask & lt_mask);
+                wkey[slot] = key[j];
+                wexp[slot] = lane + 64 * j;
+            }
+            base += __popcll(smask);
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        // 2. rank of slot `lane` by (key descending, index ascending)
+        unsigned mk = 0u;
+        int me = 0x7fffffff, rank = 0;
+        if (lane < K) {
+            mk = wkey[lane];
+            me = wexp[lane];
+            for (int q = 0; q < K; ++q) {
+                const unsigned ok = wkey[q];
+                const int oe = wexp[q];
+                rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
             }
         }
-        const int e_mine = (int)(~(unsigned)(mine & 0xffffffffull));
-        const float s_mine = (lane < K) ? row[e_mine] : 0.f;
-        const float s_top = __shfl(s_mine, 0, 64);
+        // 3. gates
+        const float s_mine = (lane < K) ? row[me < N ? me : 0] : 0.f;
+        const float s_top = __shfl(s_mine, __ffsll((long long)__ballot(lane < K && rank == 0)) - 1, 64);
         const float g = (lane < K) ? expf(s_mine - s_top) : 0.f;
         const float gsum = wave_sum_f32(g);
         if (lane < K) {
-            idx_out[(int64_t)t * K + lane] = e_mine;
-            gate_out[(int64_t)t * K + lane] = g / gsum;
-            s_idx[r * K + lane] = e_mine;
+            idx_out[(int64_t)t * K + rank] = me;
+            gate_out[(int64_t)t * K + rank] = g / gsum;
+            s_idx[r * K + rank] = me;
         }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
     __syncthreads();
 
@@ -123,12 +154,13 @@ __global__ __launch_bounds__(64 * kSelectWaves) void router_select_kernel(
             rank_out[(int64_t)t0 * K + q] = __popc(s_mask[s_idx[q]] & ((1u << r) - 1u));
     }
     for (int e = tid; e < N; e += 64 * kSelectWaves)
-        chunk_counts[(int64_t)blockIdx.x * N + e] = __popc(s_mask[e]);
+        chunk_counts[(int64_t)e * ld_chunks + blockIdx.x] = __popc(s_mask[e]);
 }
 
 inline size_t router_select_smem_bytes(int N, int K)
 {
-    return sizeof(int) * (size_t)kRouterTokens * K + sizeof(unsigned) * (size_t)N;
+    return sizeof(int) * (size_t)kRouterTokens * K + sizeof(unsigned) * (size_t)N +
+           2 * sizeof(int) * (size_t)kSelectWaves * K;
 }
 
 }  // namespace lmoe

@@ -100,6 +100,31 @@ def test_zero_router_ties_fill_first_experts():
     G.check_stages(out, wl, ref, toks, np.ones(len(toks), dtype=bool))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_exact_score_ties_follow_index_order(dtype):
+    """Router weights in {-1/4, 0, 1/4} and x in {-1, 0, 1}: every score is a
+    multiple of 1/4, exact in fp32 and fp64 alike, with many exact ties.  The
+    selection, its slot order (ties to the lower index) and the dispatch
+    permutation must equal the oracle's on every token."""
+    sh = shape(T=200, d=256, l=128, m=128, n_experts=64, top_k=8, n_shared=1, m_shared=128, dtype=dtype)
+    rng = np.random.default_rng(17)
+    arr = random_arrays(sh, rng)
+    arr["w_router"] = (rng.integers(-1, 2, size=(256, 64)) * 0.25).astype(np.float32)
+    arr["x"] = rng.integers(-1, 2, size=(200, 256)).astype(np.float32)
+    wl = workload_from_arrays(sh, arr)
+    out = G.run_gpu(wl)
+    ref = G.oracle_routing(wl)
+    assert np.array_equal(out["logits"].astype(np.float64), ref.logits)
+    srt = -np.sort(-ref.logits, axis=1)
+    assert np.mean(np.any(srt[:, :8] == srt[:, 1:9], axis=1)) > 0.5   # ties are common
+    assert np.array_equal(out["idx"], ref.idx)
+    np.testing.assert_allclose(out["gate"], ref.gate, rtol=1e-5, atol=1e-7)
+    G.check_dispatch_properties(out, 8, 64)
+    dp = oracle.dispatch(ref.idx, 64)
+    assert np.array_equal(out["pos"], dp.pos) and np.array_equal(out["perm_token"], dp.perm)
+    assert np.array_equal(out["counts"], dp.counts) and np.array_equal(out["offsets"], dp.offsets)
+
+
 @pytest.mark.parametrize("cfg", [
     dict(T=70, d=128, l=64, m=128, n_experts=16, top_k=1, n_shared=1, m_shared=64, alpha=2, variant="eff"),
     dict(T=45, d=128, l=64, m=64, n_experts=16, top_k=16, n_shared=1, m_shared=64, alpha=2, variant="eff"),
