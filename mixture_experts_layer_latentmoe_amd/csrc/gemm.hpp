@@ -209,6 +209,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
             for (int q = 0; q < 16; ++q)
                 acc[i][j][q] = 0.f;
 
+    // A wave whose whole tile is padding (rows past the valid range or
+    // columns past N) still loads and syncs but skips its MFMAs, leaving the
+    // SIMD's matrix pipe to the other wave on it.
+    const bool wave_live = (wm * WTM < rows_valid) && (n0 + wn * WTN < p.N);
     constexpr int NI = NIA + NIB;
     const int nk = p.K / BK;
     LMOE_TILE_DMA(sA0, sB0, 0u)
@@ -228,7 +232,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         __builtin_amdgcn_sched_barrier(0);                                                                    \
         if (kt + NS - 1 < nk)                                                                                 \
             LMOE_TILE_DMA(NA, NB, (unsigned)(kt + NS - 1) * 128u)                                          \
-        tile_mma<E, TM, TN, WTM, WTN>(acc, SA, SB, wm, wn, lane);                                            \
+        if (wave_live)                                                                                        \
+            tile_mma<E, TM, TN, WTM, WTN>(acc, SA, SB, wm, wn, lane);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
         if (++kt >= nk)                                                                                       \
             break;                                                                                            \
