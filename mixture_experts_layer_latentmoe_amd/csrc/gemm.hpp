@@ -5,9 +5,11 @@
 // B is held transposed (B^T[N, K], K contiguous), the layout the weights are
 // repacked into once at create time, so A and B tiles are loaded the same way:
 // 16-byte chunks of K-contiguous rows.  A k-tile is 128 bytes of K (64 bf16 or
-// 32 fp32 elements); in LDS a tile row is 8 chunks of 16 bytes, chunk c stored
-// at position c ^ (row & 7) so that both the 16-byte writes of a row and the
-// 16-row fragment reads of one chunk column hit distinct banks.
+// 32 fp32 elements); in LDS a tile row is 8 chunks of 16 bytes, chunk c of row
+// r stored at position c ^ ((r >> 1) & 7).  A 16-lane group of a fragment read
+// touches 16 consecutive rows at one chunk column; with 64 banks of 4 bytes,
+// row parity and the swizzled position then give 16 distinct 16-byte bank
+// groups (the plain c ^ (r & 7) maps rows r and r + 8 to the same banks).
 //
 // Global loads are buffer loads: a row outside the valid range gets an
 // offset beyond the buffer's size, and the hardware returns zeros for it, so
@@ -91,12 +93,12 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int r = wm * WTM + i * 32 + (lane & 31);
-            af[i] = a[r * 8 + (c ^ (r & 7))];
+            af[i] = a[r * 8 + (c ^ ((r >> 1) & 7))];
         }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int r = wn * WTN + j * 32 + (lane & 31);
-            bfr[j] = b[r * 8 + (c ^ (r & 7))];
+            bfr[j] = b[r * 8 + (c ^ ((r >> 1) & 7))];
         }
         // B fragment first: the tile's rows are output columns, so a lane
         // owns runs of 4 consecutive output columns of output row lane % 32.
@@ -110,8 +112,8 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
 
 // k-tile kt of A and B straight into LDS (buffer loads with the LDS bit: lane
 // l of a wave writes 16 bytes at the wave's base + 16 l; rows out of range
-// read as zeros).  Position P of a tile holds row P / 8, chunk
-// (P % 8) ^ (row % 8); instruction i of wave w fills positions
+// read as zeros).  Position P of a tile holds row r = P / 8, chunk
+// (P % 8) ^ ((r / 2) % 8); instruction i of wave w fills positions
 // (i * NW + w) * 64 .. +63.
 #define LMOE_TILE_DMA(SA, SB, KOFF)                                                                       \
     {                                                                                                      \
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     unsigned a_off[NIA], b_off[NIB];
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
-        const int P = (i * NW + wave) * 64 + lane, r = P >> 3, c = (P & 7) ^ (r & 7);
+        const int P = (i * NW + wave) * 64 + lane, r = P >> 3, c = (P & 7) ^ ((r >> 1) & 7);
         a_off[i] = kOOB;
         if (r < rows_valid) {
             int64_t arow = row_base + r;
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     }
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
-        const int P = (i * NW + wave) * 64 + lane, r = P >> 3, c = (P & 7) ^ (r & 7);
+        const int P = (i * NW + wave) * 64 + lane, r = P >> 3, c = (P & 7) ^ ((r >> 1) & 7);
         b_off[i] = (n0 + r < p.N) ? (unsigned)((int64_t)(n0 + r) * p.ldb * (int64_t)sizeof(E)) + c * 16 : kOOB;
     }
 
