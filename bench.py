@@ -47,6 +47,29 @@ def stage_work(sh, T):
     }
 
 
+def kernel_source_sha() -> str:
+    import glob
+    import hashlib
+    src = sorted(glob.glob(os.path.join(ROOT, "mixture_experts_layer_latentmoe_amd", "csrc", "*")))
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in src)).hexdigest()[:16]
+
+
+def profiled_traffic(cfg: str, stage: str):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 counter
+    summary (FETCH_SIZE / WRITE_SIZE scaled by a copy kernel of known size),
+    or None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{cfg}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha, val = None, None
+    for line in open(path):
+        if line.startswith("# kernel sources sha256[:16] of csrc/*:"):
+            sha = line.split(":")[-1].strip()
+        if line.startswith(f"traffic_bytes[{stage}]:"):
+            val = float(line.split(":")[-1])
+    return val if (sha == kernel_source_sha() and val is not None) else None
+
+
 def cpu_baseline(wl, target_s=12.0):
     """The oracle as it stands, on all host threads, on a bounded sample."""
     from oracle import oracle
@@ -75,6 +98,9 @@ def main():
     ap.add_argument("--config", default="readme_acc")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain elementwise copy of 256 MiB (3 launches) so that profiler "
+                         "byte counters can be scaled by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this layer is measured on one "
@@ -135,13 +161,22 @@ def main():
         if kind == "flop":
             ach = amt / avg_s / 1e12
             roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK[sh.dtype],
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK[sh.dtype], 4), "traffic": None}
+                    "unit": "TFLOP/s", "frac": round(ach / PEAK[sh.dtype], 4),
+                    "traffic": profiled_traffic(sh.name, dom)}
         else:
             ach = amt / avg_s / 1e9
             roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": profiled_traffic(sh.name, dom)}
     total_flop = sum(a for k, (kd, a) in work.items() if kd == "flop")
     layer.close()
+    if args.copy_calibration:
+        # reads 256 MiB and writes 256 MiB per launch
+        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.add(a, 0.0, out=b)
+        torch.cuda.synchronize()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
     out = {

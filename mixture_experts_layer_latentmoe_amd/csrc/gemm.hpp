@@ -47,6 +47,10 @@ struct GemmParams {
     int M, N, K;        // M: dense rows (unused in grouped mode)
     int relu2_from;     // first column of C (after the split) that gets relu^2
     int group_m;        // dense: tiles of this many M-tiles are walked together
+    int splitk;         // dense: > 1 splits K into this many contiguous k-tile ranges;
+                        // raw fp32 sums go to partial[split][M][N] and a reduce
+                        // kernel applies the epilogue
+    float *partial;
     // grouped mode
     const int *gather;       // dispatch row -> A row, or nullptr (A rows = dispatch rows)
     const int *tile_expert;  // [tiles]
@@ -124,8 +128,10 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
     }
 
 // NT = 64 * WM * WN threads; NS LDS stages (2 or 3), one barrier per k-tile;
-// tiles kt+1 .. kt+NS-1 are in flight while tile kt is multiplied.
-template <typename E, int BM, int BN, int WM, int WN, int NS, bool GROUPED, int MINB = 1>
+// tiles kt+1 .. kt+NS-1 are in flight while tile kt is multiplied.  STAGE only
+// names the layer stage, so that each stage is its own kernel symbol in
+// profiles.
+template <typename E, int BM, int BN, int WM, int WN, int NS, bool GROUPED, int MINB = 1, int STAGE = 0>
 __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmParams p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -137,13 +143,13 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     constexpr int NIA = BM * 8 / NT, NIB = BN * 8 / NT;  // LDS-DMA instructions per thread
     static_assert(TM >= 1 && TN >= 1 && NIA >= 1 && NIB >= 1, "tile shape");
     static_assert(NIA * NT == BM * 8 && NIB * NT == BN * 8, "tile shape");
-    static_assert(NS == 2 || NS == 3, "stages");
+    static_assert(NS >= 2 && NS <= 4, "stages");
 
-    __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[NS > 2 ? BM * 8 : 1];
-    __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[NS > 2 ? BN * 8 : 1];
+    __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[NS > 2 ? BM * 8 : 1], sA3[NS > 3 ? BM * 8 : 1];
+    __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[NS > 2 ? BN * 8 : 1], sB3[NS > 3 ? BN * 8 : 1];
 
     const int ntn = (p.N + BN - 1) / BN;
-    int tm, tn, rows_valid, expert = 0;
+    int tm, tn, rows_valid, expert = 0, split = 0;
     int64_t row_base; // first output row (dense: M row; grouped: dispatch row)
     if constexpr (GROUPED) {
         const int total = *p.n_mtiles * ntn;
@@ -160,9 +166,12 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         row_base = (int64_t)start + r0;
     } else {
         const int ntm = (p.M + BM - 1) / BM;
-        const int t = xcd_logical_tile(blockIdx.x, ntm * ntn);
-        if (t < 0)
+        const int S = p.splitk > 1 ? p.splitk : 1;
+        const int t2 = xcd_logical_tile(blockIdx.x, ntm * ntn * S);
+        if (t2 < 0)
             return;
+        const int t = t2 / S;
+        split = t2 - t * S;
         const int gm = p.group_m;
         const int in_group = gm * ntn;
         const int g = t / in_group;
@@ -216,46 +225,86 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     // SIMD's matrix pipe to the other wave on it.
     const bool wave_live = (wm * WTM < rows_valid) && (n0 + wn * WTN < p.N);
     constexpr int NI = NIA + NIB;
-    const int nk = p.K / BK;
-    LMOE_TILE_DMA(sA0, sB0, 0u)
-    if (NS > 2 && nk > 1)
-        LMOE_TILE_DMA(sA1, sB1, 128u)
+    // this workgroup's k-tiles: [kt0, kt0 + nkl)
+    int kt0 = 0, nkl = p.K / BK;
+    if (!GROUPED && p.splitk > 1) {
+        const int per = (nkl + p.splitk - 1) / p.splitk;
+        kt0 = split * per;
+        nkl = min(per, nkl - kt0);
+    }
+    LMOE_TILE_DMA(sA0, sB0, (unsigned)kt0 * 128u)
+    if (NS > 2 && nkl > 1)
+        LMOE_TILE_DMA(sA1, sB1, (unsigned)(kt0 + 1) * 128u)
+    if (NS > 3 && nkl > 2)
+        LMOE_TILE_DMA(sA2, sB2, (unsigned)(kt0 + 2) * 128u)
 
-// One k-tile step: wait until tile kt is in LDS for every wave (and every
-// wave is done with the stage about to be refilled), refill it with tile
-// kt + NS - 1, multiply tile kt.
+// One k-tile step j: wait until tile j is in LDS for every wave (the tiles
+// issued after it may stay in flight) and every wave is done with the stage
+// about to be refilled; refill it with tile j + NS - 1; multiply tile j.
 #define LMOE_KSTEP(SA, SB, NA, NB)                                                                            \
     {                                                                                                         \
-        if (NS > 2 && kt + 1 < nk)                                                                            \
+        const int ahead = min(NS - 2, nkl - 1 - j);                                                           \
+        if (NS > 3 && ahead >= 2)                                                                             \
+            wait_vm_lgkm0<2 * NI>();                                                                          \
+        else if (NS > 2 && ahead >= 1)                                                                        \
             wait_vm_lgkm0<NI>();                                                                              \
         else                                                                                                  \
             wait_vm_lgkm0<0>();                                                                               \
         __builtin_amdgcn_s_barrier();                                                                         \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
-        if (kt + NS - 1 < nk)                                                                                 \
-            LMOE_TILE_DMA(NA, NB, (unsigned)(kt + NS - 1) * 128u)                                          \
+        if (j + NS - 1 < nkl)                                                                                 \
+            LMOE_TILE_DMA(NA, NB, (unsigned)(kt0 + j + NS - 1) * 128u)                                     \
         if (wave_live)                                                                                        \
             tile_mma<E, TM, TN, WTM, WTN>(acc, SA, SB, wm, wn, lane);                                        \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
-        if (++kt >= nk)                                                                                       \
+        if (++j >= nkl)                                                                                       \
             break;                                                                                            \
     }
 
-    int kt = 0;
+    int j = 0;
     if constexpr (NS == 2) {
         for (;;) {
             LMOE_KSTEP(sA0, sB0, sA1, sB1)
             LMOE_KSTEP(sA1, sB1, sA0, sB0)
         }
-    } else {
+    } else if constexpr (NS == 3) {
         for (;;) {
             LMOE_KSTEP(sA0, sB0, sA2, sB2)
             LMOE_KSTEP(sA1, sB1, sA0, sB0)
             LMOE_KSTEP(sA2, sB2, sA1, sB1)
         }
+    } else {
+        for (;;) {
+            LMOE_KSTEP(sA0, sB0, sA3, sB3)
+            LMOE_KSTEP(sA1, sB1, sA0, sB0)
+            LMOE_KSTEP(sA2, sB2, sA1, sB1)
+            LMOE_KSTEP(sA3, sB3, sA2, sB2)
+        }
     }
 #undef LMOE_KSTEP
 #undef LMOE_TILE_DMA
+
+    if (!GROUPED && p.splitk > 1) {
+        // raw fp32 partial sums; the reduce kernel applies the epilogue
+        float *P = p.partial + (int64_t)split * p.M * p.N;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int rl = wm * WTM + i * 32 + (lane & 31);
+            if (rl >= rows_valid)
+                continue;
+            const int64_t row = row_base + rl;
+#pragma unroll
+            for (int jj = 0; jj < TN; ++jj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int col = n0 + wn * WTN + jj * 32 + 8 * g + 4 * (lane >> 5);
+                    if (col < p.N)
+                        store4(P + row * p.N + col, acc[i][jj][4 * g], acc[i][jj][4 * g + 1], acc[i][jj][4 * g + 2],
+                               acc[i][jj][4 * g + 3]);
+                }
+        }
+        return;
+    }
 
     E *C = static_cast<E *>(p.C);
 #pragma unroll
@@ -265,13 +314,13 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
             continue;
         const int64_t row = row_base + rl;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
+        for (int jn = 0; jn < TN; ++jn) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+                const int col = n0 + wn * WTN + jn * 32 + 8 * g + 4 * (lane >> 5);
                 if (col >= p.N)
                     continue;
-                float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                float v[4] = {acc[i][jn][4 * g], acc[i][jn][4 * g + 1], acc[i][jn][4 * g + 2], acc[i][jn][4 * g + 3]};
                 if (col < p.c_split) {
                     if (p.bias32) {
 #pragma unroll
@@ -293,6 +342,41 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         }
     }
 #endif
+}
+
+// Split-K epilogue: out = epilogue(sum_{s < S} partial[s]) in fixed split
+// order, four columns per thread; same epilogue as the GEMM kernel.
+template <typename E>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one group of 4 columns
+    const int groups = p.N / 4;
+    if (q >= (int64_t)p.M * groups)
+        return;
+    const int64_t row = q / groups;
+    const int col = (int)(q - row * groups) * 4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < p.splitk; ++s) {
+        const float4 x = *reinterpret_cast<const float4 *>(p.partial + ((int64_t)s * p.M + row) * p.N + col);
+        v[0] += x.x;
+        v[1] += x.y;
+        v[2] += x.z;
+        v[3] += x.w;
+    }
+    if (col < p.c_split) {
+        if (p.bias32)
+            for (int r = 0; r < 4; ++r)
+                v[r] += p.bias32[col + r];
+        store4(p.C32 + row * p.ldc32 + col, v[0], v[1], v[2], v[3]);
+        return;
+    }
+    const int mc = col - p.c_split;
+    for (int r = 0; r < 4; ++r)
+        if (mc + r >= p.relu2_from) {
+            const float t = fmaxf(v[r], 0.f);
+            v[r] = t * t;
+        }
+    store4(static_cast<E *>(p.C) + row * p.ldc + mc, v[0], v[1], v[2], v[3]);
 }
 
 template <int BM, int BN, int NS>

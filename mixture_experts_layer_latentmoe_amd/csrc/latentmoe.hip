@@ -84,7 +84,8 @@ struct Plan {
     int64_t max_mtiles;  // tile table capacity (smallest grouped M tile)
 };
 
-constexpr int kMinGroupBM = 32;
+constexpr int kGroupBM = 128, kGroupBMSmall = 32, kMinGroupBM = 32;
+constexpr int kSplitKMaxRows = 256, kSplitKMax = 16;
 
 int64_t max_mtiles_for(int64_t P, int64_t N, int bm) { return (P + bm - 1) / bm + std::min<int64_t>(N, P); }
 
@@ -105,6 +106,8 @@ struct latentmoe_handle {
     int *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
     int *tile_expert = nullptr, *tile_row0 = nullptr, *n_mtiles = nullptr;
     void *zh = nullptr, *H = nullptr, *Yp = nullptr;
+    float *partial = nullptr;
+    int64_t partial_cap = 0;
     // profiling
     bool prof = false;
     int prof_cap = 0, prof_used = 0;
@@ -179,9 +182,16 @@ Plan make_plan(const latentmoe_config *c)
     return p;
 }
 
+// fp32 partial sums of split-K GEMMs: up to kSplitKMax splits of the widest
+// dense output, for up to kSplitKMaxRows rows
+int64_t split_partial_floats(const Plan &p)
+{
+    return (int64_t)kSplitKMax * std::min<int64_t>(p.Tmax, kSplitKMaxRows) * std::max(p.n_x, p.d);
+}
+
 struct Layout {
     int64_t off_idx, off_gate, off_rank, off_pos, off_perm, off_cc, off_cb, off_counts, off_offsets, off_te, off_tr,
-        off_nmt, off_logits, off_zh, off_H, off_Yp, total;
+        off_nmt, off_logits, off_zh, off_H, off_Yp, off_part, total;
 };
 
 Layout ws_layout(const Plan &p)
@@ -209,6 +219,7 @@ Layout ws_layout(const Plan &p)
     L.off_zh = take((int64_t)p.esize * p.Tmax * p.ld_zh);
     L.off_H = take((int64_t)p.esize * p.P_max * p.m);
     L.off_Yp = take((int64_t)p.esize * p.P_max * p.l);
+    L.off_part = take(4 * split_partial_floats(p));
     L.total = o;
     return L;
 }
@@ -280,43 +291,85 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
 
 // ---- kernel launch helpers -------------------------------------------------
 
-template <typename E, int BM, int BN, int WM, int WN, int NS>
+// GEMM stage tags (one kernel symbol per layer stage)
+constexpr int kTagX = 0, kTagG1 = 1, kTagG2 = 2, kTagUp = 3;
+
+template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG>
 void launch_dense(const GemmParams &gp, hipStream_t s)
 {
     const int64_t ntm = (gp.M + BM - 1) / BM, ntn = (gp.N + BN - 1) / BN;
     const int64_t grid = align_up(ntm * ntn, 8);
-    gemm_kernel<E, BM, BN, WM, WN, NS, false><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
+    gemm_kernel<E, BM, BN, WM, WN, NS, false, 1, TAG><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
     hip_check(hipGetLastError());
 }
 
-template <typename E, int BM, int BN, int WM, int WN, int NS>
+template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG>
 void launch_grouped(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
 {
     const int64_t ntn = (gp.N + BN - 1) / BN;
     const int64_t grid = align_up(max_mtiles * ntn, 8);
-    gemm_kernel<E, BM, BN, WM, WN, NS, true><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
+    gemm_kernel<E, BM, BN, WM, WN, NS, true, 1, TAG><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
     hip_check(hipGetLastError());
 }
 
+template <typename E, int TAG>
+void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_t s);
+
 // Dense GEMMs: 256x256 tiles (8 waves) when they come close to filling the
-// 256 CUs once, 128x128 (4 waves, two workgroups per CU) otherwise.
-template <typename E>
-void dense_gemm(const GemmParams &gp, hipStream_t s)
+// 256 CUs once, 128x128 (4 waves, two workgroups per CU) when those do; for
+// few rows (decode) 64x128 tiles with K split so that ~512 workgroups stream
+// the weights, followed by a fixed-order reduce that applies the epilogue.
+template <typename E, int TAG>
+void dense_gemm(const GemmParams &gp, float *partial, int64_t cap_floats, hipStream_t s)
 {
     const int64_t big = ((gp.M + 255) / 256) * ((gp.N + 255) / 256);
+    const int64_t mid = ((gp.M + 127) / 128) * ((gp.N + 127) / 128);
     if (big >= 192)
-        launch_dense<E, 256, 256, 4, 2, 2>(gp, s);
+        launch_dense<E, 256, 256, 4, 2, 2, TAG>(gp, s);
+    else if (mid >= 256 || gp.M > kSplitKMaxRows)
+        launch_dense<E, 128, 128, 2, 2, 2, TAG>(gp, s);
     else
-        launch_dense<E, 128, 128, 2, 2, 2>(gp, s);
+        launch_splitk<E, TAG>(gp, partial, cap_floats, s);
 }
 
-constexpr int kGroupBM = 128;
-
-template <typename E>
-void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
+template <typename E, int TAG>
+void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_t s)
 {
-    launch_grouped<E, kGroupBM, 128, 2, 2, 2>(gp, max_mtiles, s);
+    constexpr int BM = 64, BN = 128;
+    const int nk = gp.K / (128 / (int)sizeof(E));
+    const int64_t tiles = ((gp.M + BM - 1) / BM) * ((gp.N + BN - 1) / BN);
+    int S = (int)std::min<int64_t>((512 + tiles - 1) / tiles, kSplitKMax);
+    S = std::max(1, std::min(S, nk / 2));
+    while (S > 1 && (int64_t)S * gp.M * gp.N > cap_floats)
+        --S;
+    if (S <= 1) {
+        gp.splitk = 1;
+        launch_dense<E, BM, BN, 2, 2, 3, TAG>(gp, s);
+        return;
+    }
+    const int per = (nk + S - 1) / S;
+    gp.splitk = (nk + per - 1) / per;  // every split gets at least one k-tile
+    gp.partial = partial;
+    const int64_t grid = align_up(tiles * gp.splitk, 8);
+    gemm_kernel<E, BM, BN, 2, 2, 3, false, 1, TAG><<<dim3((unsigned)grid), dim3(256), 0, s>>>(gp);
+    hip_check(hipGetLastError());
+    const int64_t groups = (int64_t)gp.M * (gp.N / 4);
+    splitk_reduce_kernel<E><<<dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s>>>(gp);
+    hip_check(hipGetLastError());
 }
+
+// Grouped GEMMs: 128x128 tiles; when experts average few rows (decode),
+// 32x128 tiles with four LDS stages so that more weight bytes are in flight.
+template <typename E, int TAG>
+void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, hipStream_t s)
+{
+    if (bm == kGroupBMSmall)
+        launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG>(gp, max_mtiles, s);
+    else
+        launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG>(gp, max_mtiles, s);
+}
+
+int group_bm_for(int64_t P, int64_t N) { return (P / N < 32) ? kGroupBMSmall : kGroupBM; }
 
 template <int NPL>
 void launch_select_n(latentmoe_handle *h, int T, hipStream_t s)
@@ -378,7 +431,8 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     const int64_t P = (int64_t)T * K;
     const int nchunks = (T + kRouterTokens - 1) / kRouterTokens;
     const int es = p.esize;
-    const int64_t max_mt = max_mtiles_for(P, N, kGroupBM);
+    const int gbm = group_bm_for(P, N);
+    const int64_t max_mt = max_mtiles_for(P, N, gbm);
     StageTimer tm{h, s, -1};
     if (h->prof && h->prof_used < h->prof_cap)
         tm.slot = h->prof_used++;
@@ -402,7 +456,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g.relu2_from = (int)p.l;
     g.group_m = 8;
     tm.begin(ST_GEMM_X);
-    dense_gemm<E>(g, s);
+    dense_gemm<E, kTagX>(g, h->partial, h->partial_cap, s);
     tm.end(ST_GEMM_X);
     if (dbg && dbg->logits)
         hip_check(hipMemcpyAsync(dbg->logits, h->logits, 4 * (size_t)T * N, hipMemcpyDeviceToDevice, s));
@@ -426,7 +480,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     {
         const int64_t blocks = std::min<int64_t>((P + 1023) / 1024, 256);
         finalize_kernel<<<dim3((unsigned)blocks), dim3(1024), 0, s>>>(
-            h->idx, h->rank, h->chunk_base, h->counts, T, K, N, kRouterTokens, (int)p.ld_chunks, kGroupBM,
+            h->idx, h->rank, h->chunk_base, h->counts, T, K, N, kRouterTokens, (int)p.ld_chunks, gbm,
             h->offsets, h->tile_expert, h->tile_row0, h->n_mtiles, h->pos, h->perm);
     }
     hip_check(hipGetLastError());
@@ -451,7 +505,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g1.n_mtiles = h->n_mtiles;
     g1.offsets = h->offsets;
     tm.begin(ST_GEMM1);
-    grouped_gemm<E>(g1, max_mt, s);
+    grouped_gemm<E, kTagG1>(g1, max_mt, gbm, s);
     tm.end(ST_GEMM1);
 
     // 6: Y = H W2_e
@@ -469,7 +523,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g2.relu2_from = 1 << 30;
     g2.gather = nullptr;
     tm.begin(ST_GEMM2);
-    grouped_gemm<E>(g2, max_mt, s);
+    grouped_gemm<E, kTagG2>(g2, max_mt, gbm, s);
     tm.end(ST_GEMM2);
 
     // 7: u = sum_k gate Y[pos], written over z (z is dead after stage 5)
@@ -494,7 +548,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g3.relu2_from = 1 << 30;
     g3.group_m = 8;
     tm.begin(ST_GEMM_UP);
-    dense_gemm<E>(g3, s);
+    dense_gemm<E, kTagUp>(g3, h->partial, h->partial_cap, s);
     tm.end(ST_GEMM_UP);
 
     if (dbg) {
@@ -655,6 +709,8 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
         h->zh = b + L.off_zh;
         h->H = b + L.off_H;
         h->Yp = b + L.off_Yp;
+        h->partial = reinterpret_cast<float *>(b + L.off_part);
+        h->partial_cap = split_partial_floats(p);
         if (p.dtype == LATENTMOE_DTYPE_BF16)
             repack_weights<bf16>(h, w, s);
         else
