@@ -27,24 +27,45 @@ PEAK = {"bf16": 2500.0, "f32": 157.3}      # dense MFMA TFLOP/s (MI355X publishe
 HBM_PEAK_GBS = 8000.0
 
 
-def stage_work(sh, T):
-    """Algorithmic work per launch of each stage: (kind, amount)."""
+def stage_work(sh, T, n_active):
+    """Algorithmic work per launch of each stage: (flop, bytes).
+
+    bytes counts every operand once: weights, activations read, outputs
+    written.  n_active = experts that receive at least one token (the grouped
+    GEMMs stream only those experts' weights).  None = not counted."""
     P = T * sh.top_k
     es = 2 if sh.dtype == "bf16" else 4
-    ldzh = sh.l + sh.n_shared * sh.m_shared
+    ms = sh.n_shared * sh.m_shared
+    ldzh = sh.l + ms
+    N, d, l, m = sh.n_experts, sh.d, sh.l, sh.m
     return {
-        # one pass over x: router scores, z and the shared-expert hidden layer
-        "gemm_x_router_down_shared1": ("flop", 2.0 * T * sh.d * (sh.n_experts + ldzh)),
-        "grouped_gemm1_relu2": ("flop", 2.0 * P * sh.l * sh.m),
-        "grouped_gemm2": ("flop", 2.0 * P * sh.m * sh.l),
-        "gemm_up_shared2": ("flop", 2.0 * T * ldzh * sh.d),
+        # one pass over x: router scores (fp32 out), z and the shared-expert hidden layer
+        "gemm_x_router_down_shared1": (2.0 * T * d * (N + ldzh),
+                                       es * (T * d + d * (N + ldzh) + T * ldzh) + 4.0 * T * N),
+        "grouped_gemm1_relu2": (2.0 * P * l * m, es * (n_active * l * m + P * l + P * m) + 4.0 * P),
+        "grouped_gemm2": (2.0 * P * m * l, es * (n_active * m * l + P * m + P * l)),
+        "gemm_up_shared2": (2.0 * T * ldzh * d, es * (ldzh * d + T * ldzh + T * d)),
         # gather P rows of l, write T rows of l, read pos and gate
-        "combine": ("byte", float(P * sh.l * es + T * sh.l * es + P * 8)),
+        "combine": (None, float(P * l * es + T * l * es + P * 8)),
         # read the T x N' fp32 scores, write idx/gate/rank (12 bytes per slot)
-        "router_select": ("byte", float(T * sh.n_experts * 4 + P * 12)),
-        "dispatch_scan": ("byte", None),
-        "dispatch_finalize": ("byte", None),
+        "router_select": (None, float(T * N * 4 + P * 12)),
+        "dispatch_scan": (None, None),
+        "dispatch_finalize": (None, None),
     }
+
+
+def roofline_of(flop, nbytes, avg_s, dtype):
+    """Position of one kernel against the roof that bounds it: MFMA when its
+    flops take longer at peak than its bytes at HBM peak, else HBM."""
+    t_mfma = flop / (PEAK[dtype] * 1e12) if flop else 0.0
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) if nbytes else 0.0
+    if flop and t_mfma >= t_hbm:
+        ach = flop / avg_s / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK[dtype], "unit": "TFLOP/s",
+                "frac": round(ach / PEAK[dtype], 4)}
+    ach = nbytes / avg_s / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4)}
 
 
 def kernel_source_sha() -> str:
@@ -139,36 +160,30 @@ def main():
 
     ms_per_step = dt / args.steps * 1e3
     value = T * args.steps / dt
-    work = stage_work(sh, T)
+    counts = layer.forward_debug(x, want=("counts",))["counts"].cpu().numpy()
+    n_active = int((counts > 0).sum())
+    work = stage_work(sh, T, n_active)
     stage_out = {}
     roof = None
     if stages:
         for name, (ms, n) in stages.items():
             if n:
                 avg_us = ms / n * 1e3
-                kind, amt = work.get(name, ("byte", None))
+                flop, nbytes = work.get(name, (None, None))
                 e = {"avg_us": round(avg_us, 2), "launches": n}
-                if amt is not None:
-                    if kind == "flop":
-                        e["tflops"] = round(amt / (avg_us * 1e-6) / 1e12, 1)
-                    else:
-                        e["gbs"] = round(amt / (avg_us * 1e-6) / 1e9, 1)
+                if flop:
+                    e["tflops"] = round(flop / (avg_us * 1e-6) / 1e12, 1)
+                if nbytes:
+                    e["gbs"] = round(nbytes / (avg_us * 1e-6) / 1e9, 1)
+                if flop or nbytes:
+                    r = roofline_of(flop, nbytes, avg_us * 1e-6, sh.dtype)
+                    e["bound"], e["frac"] = r["bound"], r["frac"]
                 stage_out[name] = e
-        dom = max((k for k in stage_out if work.get(k, ("", None))[1] is not None),
-                  key=lambda k: stage_out[k]["avg_us"])
-        kind, amt = work[dom]
-        avg_s = stage_out[dom]["avg_us"] * 1e-6
-        if kind == "flop":
-            ach = amt / avg_s / 1e12
-            roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK[sh.dtype],
-                    "unit": "TFLOP/s", "frac": round(ach / PEAK[sh.dtype], 4),
-                    "traffic": profiled_traffic(sh.name, dom)}
-        else:
-            ach = amt / avg_s / 1e9
-            roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": profiled_traffic(sh.name, dom)}
-    total_flop = sum(a for k, (kd, a) in work.items() if kd == "flop")
+        dom = max((k for k in stage_out if "frac" in stage_out[k]), key=lambda k: stage_out[k]["avg_us"])
+        flop, nbytes = work[dom]
+        roof = {"kernel": dom, **roofline_of(flop, nbytes, stage_out[dom]["avg_us"] * 1e-6, sh.dtype),
+                "traffic": profiled_traffic(sh.name, dom)}
+    total_flop = sum(f for f, _ in work.values() if f)
     layer.close()
     if args.copy_calibration:
         # reads 256 MiB and writes 256 MiB per launch
@@ -186,7 +201,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{sh.name}: LatentMoE layer forward, T={T} d={sh.d} l={sh.l} m={sh.m} "
                                f"N'={sh.n_experts} K'={sh.top_k} S={sh.n_shared}x{sh.m_shared} "
-                               f"{sh.variant} {sh.dtype}", "tokens": T},
+                               f"{sh.variant} {sh.dtype}", "tokens": T, "experts_with_tokens": n_active},
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
         "roofline": roof, "cpu_baseline": cpu, "stages": stage_out,
     }
