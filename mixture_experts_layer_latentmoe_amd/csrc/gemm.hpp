@@ -85,6 +85,71 @@ template <int N> __device__ __forceinline__ void wait_vm_lgkm0()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
+// Output tile of one workgroup.  Dense: rows [row_base, row_base +
+// rows_valid) of M; grouped: dispatch rows of one expert.  split: the K range
+// of a split-K workgroup.
+struct TileInfo {
+    int n0, rows_valid, expert, split;
+    int64_t row_base;
+};
+
+// Logical tile t (no split-K) -> output tile.  Grouped: t walks the device
+// tile table, N-tiles fastest.  Dense: tiles are walked in groups of group_m
+// M-tiles, so that tiles in flight together share A and B panels.
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ void tile_coords(const GemmParams &p, int t, int ntn, TileInfo &ti)
+{
+    int tm, tn;
+    ti.expert = 0;
+    ti.split = 0;
+    if constexpr (GROUPED) {
+        tm = t / ntn;
+        tn = t - tm * ntn;
+        ti.expert = p.tile_expert[tm];
+        const int r0 = p.tile_row0[tm];
+        const int start = p.offsets[ti.expert];
+        const int cnt = p.offsets[ti.expert + 1] - start;
+        ti.rows_valid = min(BM, cnt - r0);
+        ti.row_base = (int64_t)start + r0;
+    } else {
+        const int ntm = (p.M + BM - 1) / BM;
+        const int gm = p.group_m;
+        const int in_group = gm * ntn;
+        const int g = t / in_group;
+        const int first = g * gm;
+        const int gsize = min(ntm - first, gm);
+        const int r = t - g * in_group;
+        tm = first + r % gsize;
+        tn = r / gsize;
+        ti.rows_valid = min(BM, p.M - tm * BM);
+        ti.row_base = (int64_t)tm * BM;
+    }
+    ti.n0 = tn * BN;
+}
+
+// The tile of this workgroup (one tile per workgroup, split-K aware).
+template <int BM, int BN, bool GROUPED>
+__device__ __forceinline__ bool locate_tile(const GemmParams &p, TileInfo &ti)
+{
+    const int ntn = (p.N + BN - 1) / BN;
+    if constexpr (GROUPED) {
+        const int t = xcd_logical_tile(blockIdx.x, *p.n_mtiles * ntn);
+        if (t < 0)
+            return false;
+        tile_coords<BM, BN, true>(p, t, ntn, ti);
+    } else {
+        const int ntm = (p.M + BM - 1) / BM;
+        const int S = p.splitk > 1 ? p.splitk : 1;
+        const int t2 = xcd_logical_tile(blockIdx.x, ntm * ntn * S);
+        if (t2 < 0)
+            return false;
+        const int t = t2 / S;
+        tile_coords<BM, BN, false>(p, t, ntn, ti);
+        ti.split = t2 - t * S;
+    }
+    return true;
+}
+
 // Multiply one LDS k-tile (128 bytes of K: four k-steps of 32 bytes) into the
 // wave's 32x32 accumulator tiles.
 template <typename E, int TM, int TN, int WTM, int WTN>
@@ -111,6 +176,105 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = Mfma32<E>::run(bfr[j], af[i], acc[i][j]);
+    }
+}
+
+// Epilogue straight from the accumulators: each lane stores runs of four
+// output columns.  Columns below c_split go to C32 in fp32 (+ bias32), the
+// rest to C, with relu^2 from relu2_from on.
+template <typename E, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_tile_direct(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t row_base,
+                                                  int rows_valid, int n0, int wm, int wn, int lane)
+{
+    E *C = static_cast<E *>(p.C);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int rl = wm * WTM + i * 32 + (lane & 31);
+        if (rl >= rows_valid)
+            continue;
+        const int64_t row = row_base + rl;
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int col = n0 + wn * WTN + jn * 32 + 8 * g + 4 * (lane >> 5);
+                if (col >= p.N)
+                    continue;
+                float v[4] = {acc[i][jn][4 * g], acc[i][jn][4 * g + 1], acc[i][jn][4 * g + 2], acc[i][jn][4 * g + 3]};
+                if (col < p.c_split) {
+                    if (p.bias32) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] += p.bias32[col + r];
+                    }
+                    store4(p.C32 + row * p.ldc32 + col, v[0], v[1], v[2], v[3]);
+                    continue;
+                }
+                const int mc = col - p.c_split;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (mc + r >= p.relu2_from) {
+                        const float t = fmaxf(v[r], 0.f);
+                        v[r] = t * t;
+                    }
+                store4(C + row * p.ldc + mc, v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
+}
+
+// Epilogue through LDS: each wave converts its block 32 rows at a time into
+// its own area `stg` (32 rows x WTN elements of E), then writes whole
+// 16-byte chunks of output rows -- a store instruction covers a few full
+// rows instead of 16 bytes in each of 32 rows.  Same arithmetic as
+// store_tile_direct; for tiles without fp32 router columns (n0 >= c_split).
+// Chunk c of staged row r sits at position c ^ (r % CPR).
+template <typename E, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t row_base,
+                                                  int rows_valid, int n0, int wm, int wn, int lane, uint4 *stg)
+{
+    constexpr int ES = (int)sizeof(E);
+    constexpr int CPR = WTN * ES / 16;  // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPR;       // staged rows per store instruction
+    static_assert(CPR >= 1 && CPR <= 64 && (CPR & (CPR - 1)) == 0, "staged row");
+    const int lr = lane & 31, lc = lane >> 5;
+    const int cbase = n0 + wn * WTN - p.c_split;  // first C column of this wave
+    const int rows_here = rows_valid - wm * WTM;
+    const int cw = lane % CPR;
+    const bool col_ok = n0 + wn * WTN + cw * (16 / ES) < p.N;
+    E *C = static_cast<E *>(p.C);
+    char *sb = reinterpret_cast<char *>(stg);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        if (i * 32 >= rows_here)  // uniform: nothing left to store
+            break;
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int cc = jn * 32 + 8 * g + 4 * lc;  // column inside the wave block
+                float v[4] = {acc[i][jn][4 * g], acc[i][jn][4 * g + 1], acc[i][jn][4 * g + 2], acc[i][jn][4 * g + 3]};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (cbase + cc + r >= p.relu2_from) {
+                        const float t = fmaxf(v[r], 0.f);
+                        v[r] = t * t;
+                    }
+                const int byte = cc * ES, ch = byte / 16;
+                store4(reinterpret_cast<E *>(sb + (lr * CPR + (ch ^ (lr & (CPR - 1)))) * 16 + byte % 16), v[0], v[1],
+                       v[2], v[3]);
+            }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r0 = 0; r0 < 32; r0 += RPI) {
+            const int rl = r0 + lane / CPR;
+            const uint4 v = stg[rl * CPR + (cw ^ (rl & (CPR - 1)))];
+            if (col_ok && i * 32 + rl < rows_here)
+                *reinterpret_cast<uint4 *>(C + (row_base + wm * WTM + i * 32 + rl) * p.ldc + cbase + cw * (16 / ES)) = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -148,42 +312,12 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[NS > 2 ? BM * 8 : 1], sA3[NS > 3 ? BM * 8 : 1];
     __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[NS > 2 ? BN * 8 : 1], sB3[NS > 3 ? BN * 8 : 1];
 
-    const int ntn = (p.N + BN - 1) / BN;
-    int tm, tn, rows_valid, expert = 0, split = 0;
-    int64_t row_base; // first output row (dense: M row; grouped: dispatch row)
-    if constexpr (GROUPED) {
-        const int total = *p.n_mtiles * ntn;
-        const int t = xcd_logical_tile(blockIdx.x, total);
-        if (t < 0)
-            return;
-        tm = t / ntn;
-        tn = t - tm * ntn;
-        expert = p.tile_expert[tm];
-        const int r0 = p.tile_row0[tm];
-        const int start = p.offsets[expert];
-        const int cnt = p.offsets[expert + 1] - start;
-        rows_valid = min(BM, cnt - r0);
-        row_base = (int64_t)start + r0;
-    } else {
-        const int ntm = (p.M + BM - 1) / BM;
-        const int S = p.splitk > 1 ? p.splitk : 1;
-        const int t2 = xcd_logical_tile(blockIdx.x, ntm * ntn * S);
-        if (t2 < 0)
-            return;
-        const int t = t2 / S;
-        split = t2 - t * S;
-        const int gm = p.group_m;
-        const int in_group = gm * ntn;
-        const int g = t / in_group;
-        const int first = g * gm;
-        const int gsize = min(ntm - first, gm);
-        const int r = t - g * in_group;
-        tm = first + r % gsize;
-        tn = r / gsize;
-        rows_valid = min(BM, p.M - tm * BM);
-        row_base = (int64_t)tm * BM;
-    }
-    const int n0 = tn * BN;
+    TileInfo ti;
+    if (!locate_tile<BM, BN, GROUPED>(p, ti))
+        return;
+    const int rows_valid = ti.rows_valid, expert = ti.expert, split = ti.split;
+    const int64_t row_base = ti.row_base;
+    const int n0 = ti.n0;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,7 +416,6 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         }
     }
 #undef LMOE_KSTEP
-#undef LMOE_TILE_DMA
 
     if (!GROUPED && p.splitk > 1) {
         // raw fp32 partial sums; the reduce kernel applies the epilogue
@@ -306,40 +439,20 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         return;
     }
 
-    E *C = static_cast<E *>(p.C);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int rl = wm * WTM + i * 32 + (lane & 31);
-        if (rl >= rows_valid)
-            continue;
-        const int64_t row = row_base + rl;
-#pragma unroll
-        for (int jn = 0; jn < TN; ++jn) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = n0 + wn * WTN + jn * 32 + 8 * g + 4 * (lane >> 5);
-                if (col >= p.N)
-                    continue;
-                float v[4] = {acc[i][jn][4 * g], acc[i][jn][4 * g + 1], acc[i][jn][4 * g + 2], acc[i][jn][4 * g + 3]};
-                if (col < p.c_split) {
-                    if (p.bias32) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            v[r] += p.bias32[col + r];
-                    }
-                    store4(p.C32 + row * p.ldc32 + col, v[0], v[1], v[2], v[3]);
-                    continue;
-                }
-                const int mc = col - p.c_split;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (mc + r >= p.relu2_from) {
-                        const float t = fmaxf(v[r], 0.f);
-                        v[r] = t * t;
-                    }
-                store4(C + row * p.ldc + mc, v[0], v[1], v[2], v[3]);
-            }
-        }
+    if (sizeof(E) != 2 || n0 < p.c_split) {  // fp32 outputs: straight from the registers
+        store_tile_direct<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane);
+        return;
+    }
+    if constexpr (sizeof(E) == 2) {
+        // every wave is done with the k-tiles (no load is in flight after the
+        // last k-step): the A stage arrays hold the waves' epilogue areas
+        constexpr int WAVE_U = 32 * WTN * 2 / 16;  // 16-byte units per wave area
+        constexpr int PER_ARR = (BM * 8) / WAVE_U;  // areas per A stage array
+        static_assert(PER_ARR >= 1 && NW <= 2 * PER_ARR, "epilogue areas fit in sA0 and sA1");
+        wait_vm_lgkm0<0>();
+        __builtin_amdgcn_s_barrier();
+        uint4 *stg = (wave < PER_ARR ? sA0 : sA1) + (wave % PER_ARR) * WAVE_U;
+        store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg);
     }
 #endif
 }
@@ -378,6 +491,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p)
         }
     store4(static_cast<E *>(p.C) + row * p.ldc + mc, v[0], v[1], v[2], v[3]);
 }
+
+#undef LMOE_TILE_DMA
 
 template <int BM, int BN, int NS>
 constexpr size_t gemm_lds_bytes()
