@@ -161,13 +161,17 @@ const char *latentmoe_status_string(int status);
 int latentmoe_last_hip_error(void);
 
 /* Per-stage kernel timing with HIP events recorded on the forward's stream.
- * profile_begin reserves events for up to max_forwards forward calls;
- * profile_end waits for them and writes, for each stage s < *n_stages, the
- * total milliseconds in ms[s] and the number of timed launches in
- * launches[s] (host arrays of length LATENTMOE_MAX_STAGES), and the stage
- * names via latentmoe_stage_name. */
+ * profile_begin reserves events for up to max_forwards forward calls and
+ * times the stages whose bit is set in stage_mask (bit s = stage s; each
+ * timed stage costs two event records per forward, so a caller measuring
+ * throughput times only the stage it needs); profile_end waits for them and
+ * writes, for each stage s < *n_stages, the total milliseconds in ms[s] and
+ * the number of timed launches in launches[s] (host arrays of length
+ * LATENTMOE_MAX_STAGES), and the stage names via latentmoe_stage_name.
+ * Errors: LATENTMOE_ERR_INVALID_ARGUMENT for a null handle, max_forwards
+ * outside [1, 100000] or an empty mask. */
 #define LATENTMOE_MAX_STAGES 16
-int latentmoe_profile_begin(latentmoe_handle *h, int max_forwards);
+int latentmoe_profile_begin(latentmoe_handle *h, int max_forwards, uint32_t stage_mask);
 int latentmoe_profile_end(latentmoe_handle *h, double *ms, int32_t *launches, int32_t *n_stages);
 const char *latentmoe_stage_name(int stage);
 

@@ -89,7 +89,7 @@ def lib():
         L.latentmoe_status_string.argtypes = [C.c_int]
         L.latentmoe_status_string.restype = C.c_char_p
         L.latentmoe_last_hip_error.argtypes = []
-        L.latentmoe_profile_begin.argtypes = [_vp, C.c_int]
+        L.latentmoe_profile_begin.argtypes = [_vp, C.c_int, C.c_uint32]
         L.latentmoe_profile_end.argtypes = [_vp, P(C.c_double), P(_i32), P(_i32)]
         L.latentmoe_stage_name.argtypes = [C.c_int]
         L.latentmoe_stage_name.restype = C.c_char_p
@@ -149,8 +149,12 @@ def latentmoe_destroy(handle: int) -> None:
     _check("latentmoe_destroy", lib().latentmoe_destroy(_vp(handle)))
 
 
-def latentmoe_profile_begin(handle: int, max_forwards: int) -> None:
-    _check("latentmoe_profile_begin", lib().latentmoe_profile_begin(_vp(handle), int(max_forwards)))
+ALL_STAGES = 0xFFFF
+
+
+def latentmoe_profile_begin(handle: int, max_forwards: int, stage_mask: int = ALL_STAGES) -> None:
+    _check("latentmoe_profile_begin",
+           lib().latentmoe_profile_begin(_vp(handle), int(max_forwards), int(stage_mask) & 0xFFFFFFFF))
 
 
 def latentmoe_profile_end(handle: int) -> dict:

@@ -111,6 +111,7 @@ struct latentmoe_handle {
     // profiling
     bool prof = false;
     int prof_cap = 0, prof_used = 0;
+    uint32_t prof_mask = 0;  // stages timed
     std::vector<hipEvent_t> ev;  // [prof_cap][ST_COUNT][2]
     std::vector<int> ev_used;    // [prof_cap][ST_COUNT]
 };
@@ -405,12 +406,12 @@ struct StageTimer {
     int slot;
     void begin(int st)
     {
-        if (slot >= 0)
+        if (slot >= 0 && ((h->prof_mask >> st) & 1u))
             hip_check(hipEventRecord(h->ev[((size_t)slot * ST_COUNT + st) * 2], s));
     }
     void end(int st)
     {
-        if (slot >= 0) {
+        if (slot >= 0 && ((h->prof_mask >> st) & 1u)) {
             hip_check(hipEventRecord(h->ev[((size_t)slot * ST_COUNT + st) * 2 + 1], s));
             h->ev_used[(size_t)slot * ST_COUNT + st] = 1;
         }
@@ -757,9 +758,9 @@ int latentmoe_destroy(latentmoe_handle *h)
     return LATENTMOE_OK;
 }
 
-int latentmoe_profile_begin(latentmoe_handle *h, int max_forwards)
+int latentmoe_profile_begin(latentmoe_handle *h, int max_forwards, uint32_t stage_mask)
 {
-    if (!h || max_forwards < 1 || max_forwards > 100000)
+    if (!h || max_forwards < 1 || max_forwards > 100000 || (stage_mask & ((1u << ST_COUNT) - 1u)) == 0)
         return LATENTMOE_ERR_INVALID_ARGUMENT;
     try {
         for (hipEvent_t e : h->ev)
@@ -774,6 +775,7 @@ int latentmoe_profile_begin(latentmoe_handle *h, int max_forwards)
         return LATENTMOE_ERR_HIP;
     }
     h->prof = true;
+    h->prof_mask = stage_mask & ((1u << ST_COUNT) - 1u);
     h->prof_cap = max_forwards;
     h->prof_used = 0;
     return LATENTMOE_OK;

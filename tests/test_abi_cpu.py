@@ -89,7 +89,7 @@ def test_null_arguments_rejected_before_any_gpu_call():
     assert L.latentmoe_create(ctypes.byref(cfg), ctypes.byref(w), None, None) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
     assert L.latentmoe_forward(None, None, None, 1, None, None) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
     assert L.latentmoe_destroy(None) == _abi.LATENTMOE_OK
-    assert L.latentmoe_profile_begin(None, 1) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
+    assert L.latentmoe_profile_begin(None, 1, 0xFFFF) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
 
 
 def test_status_strings():

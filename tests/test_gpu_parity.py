@@ -170,3 +170,30 @@ def test_forward_argument_errors():
             _abi.LATENTMOE_ERR_INVALID_ARGUMENT
     finally:
         layer.close()
+
+
+def test_profile_stage_mask_times_only_selected_stages():
+    wl = make_workload(get_config("tiny_f32"), T=64)
+    layer = LatentMoE.from_workload(wl, max_tokens=64)
+    try:
+        x = to_device(wl.tensors["x"], "f32", "cuda:0")
+        y = torch.empty_like(x)
+        names = [_abi.latentmoe_stage_name(i) for i in range(_abi.LATENTMOE_MAX_STAGES)]
+        names = [n for n in names if n]
+        sel = names.index("grouped_gemm1_relu2")
+        L = _abi.lib()
+        import ctypes
+        assert L.latentmoe_profile_begin(ctypes.c_void_p(layer.handle), 4, 0) == \
+            _abi.LATENTMOE_ERR_INVALID_ARGUMENT  # empty mask
+        _abi.latentmoe_profile_begin(layer.handle, 4, 1 << sel)
+        for _ in range(3):
+            layer.forward(x, y)
+        st = _abi.latentmoe_profile_end(layer.handle)
+        assert st["grouped_gemm1_relu2"][1] == 3 and st["grouped_gemm1_relu2"][0] > 0
+        assert all(n == 0 for k, (ms, n) in st.items() if k != "grouped_gemm1_relu2")
+        # the mask changes no result
+        ref = G.run_gpu(wl)["y"]
+        layer.forward(x, y)
+        assert np.array_equal(y.cpu().numpy(), ref)
+    finally:
+        layer.close()
