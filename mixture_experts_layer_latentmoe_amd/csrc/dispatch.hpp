@@ -12,7 +12,7 @@
 //   pos[t, k]     = offsets[e] + #{t' < t : e in idx[t']}
 //   perm_token[pos[t, k]] = t
 //
-// The selection kernel already left, per 32-token chunk c, the count of every
+// The selection kernel already left, per chunk c of 16 tokens, the count of every
 // expert (chunk_counts[e][c], expert-major) and each pair's rank inside its
 // chunk.  Here:
 //   chunk_scan_kernel  one wave per expert: chunk_base[e][c] = sum_{c' < c}

@@ -9,8 +9,9 @@
 //
 // The scores s = x W_r (+ b) come from the same MFMA pass over x that
 // produces z and the shared-expert hidden layer (their weights are one
-// concatenated matrix), stored in fp32.  This kernel owns 32 tokens (one
-// dispatch chunk), 16 waves, two tokens per wave:
+// concatenated matrix), stored in fp32.  This kernel owns 16 tokens (one
+// dispatch chunk), 16 waves, one token per wave -- small chunks keep every
+// CU busy at a few thousand tokens:
 //   1. scores become order-preserving 32-bit keys (-0.0 folded into +0.0, so
 //      signed zeros tie); a 32-round radix search, counting with wave ballots,
 //      finds the K'-th largest key; every key above it is selected, and of the
@@ -19,7 +20,7 @@
 //      comparing each against the others through LDS;
 //   3. gate_k = exp(s_k - s_max) / sum_j exp(s_j - s_max) over the selected
 //      set, which is the renormalised softmax (its denominator cancels);
-//   4. a 32-bit mask per expert marks which tokens of the chunk chose it;
+//   4. a bit mask per expert marks which tokens of the chunk chose it;
 //      popcounts give each (token, slot) its rank inside the chunk and the
 //      chunk's count per expert -- integer-exact, independent of the order of
 //      the atomic ORs.  Counts are stored expert-major: [N'][ld_chunks].
@@ -29,7 +30,7 @@
 
 namespace lmoe {
 
-constexpr int kRouterTokens = 32;
+constexpr int kRouterTokens = 16;  // tokens per workgroup = one dispatch chunk
 constexpr int kSelectWaves = 16;
 
 __device__ __forceinline__ unsigned ordered_key(float v)
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(64 * kSelectWaves) void router_select_kernel(
     int *__restrict__ rank_out, int *__restrict__ chunk_counts, int ld_chunks)
 {
     extern __shared__ int rsmem[];
-    int *s_idx = rsmem;                                                          // [32][K]
+    int *s_idx = rsmem;                                                          // [kRouterTokens][K]
     unsigned *s_mask = reinterpret_cast<unsigned *>(rsmem + kRouterTokens * K);  // [N]
     unsigned *s_key = s_mask + N;                                                // [16 waves][K]
     int *s_exp = reinterpret_cast<int *>(s_key + kSelectWaves * K);              // [16 waves][K]
