@@ -22,6 +22,8 @@
 //                      perm_token[pos] = t; workgroup 0 also publishes offsets
 //                      and the (expert, first row) tile table of the grouped
 //                      GEMMs
+//   dispatch_small_kernel  both in one workgroup when a batch has at most 64
+//                      chunks (decode-sized batches)
 // All integer, no atomics: the same idx always gives the same bits.
 #pragma once
 
@@ -72,19 +74,18 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int *__restrict__
         counts[e] = carry;
 }
 
-// 1024 threads; N' <= 1024.
-__global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ idx, const int *__restrict__ rank,
-                                                       const int *__restrict__ chunk_base,
-                                                       const int *__restrict__ counts, int T, int K, int N,
-                                                       int chunk_tokens, int ld_chunks, int BM,
-                                                       int *__restrict__ offsets, int *__restrict__ tile_expert,
-                                                       int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
-                                                       int *__restrict__ pos, int *__restrict__ perm)
+// The part of the order every workgroup computes: an exclusive scan of the
+// counts into offsets (in LDS), then pos/perm for the pairs q = q0, q0 + qs,
+// ...; `lead` also publishes offsets and the (expert, first row) tile table.
+// 1024 threads, N' <= 1024; c = counts[threadIdx.x] (0 past N').
+__device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int64_t qs, const int *__restrict__ idx,
+                                               const int *__restrict__ rank, const int *__restrict__ chunk_base, int T,
+                                               int K, int N, int chunk_tokens, int ld_chunks, int BM,
+                                               int *__restrict__ offsets, int *__restrict__ tile_expert,
+                                               int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
+                                               int *__restrict__ pos, int *__restrict__ perm, int *s_off, int *s_wsum)
 {
-    __shared__ int s_off[1024];
-    __shared__ int s_wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int c = (tid < N) ? counts[tid] : 0;
     // block-wide exclusive scan of counts
     const int incl = wave_incl_scan(c, lane);
     if (lane == 63)
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ 
     s_off[tid] = excl;
     __syncthreads();
 
-    if (blockIdx.x == 0) {
+    if (lead) {
         if (tid < N)
             offsets[tid] = excl;
         if (tid == N - 1)
@@ -122,13 +123,78 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ 
     }
 
     const int64_t P = (int64_t)T * K;
-    for (int64_t q = (int64_t)blockIdx.x * 1024 + tid; q < P; q += (int64_t)gridDim.x * 1024) {
+    for (int64_t q = q0; q < P; q += qs) {
         const int t = (int)(q / K);
         const int e = idx[q];
         const int p = s_off[e] + chunk_base[(int64_t)e * ld_chunks + t / chunk_tokens] + rank[q];
         pos[q] = p;
         perm[p] = t;
     }
+}
+
+// 1024 threads; N' <= 1024.  Every workgroup scans the counts; workgroup 0
+// publishes offsets and the tile table; all share the pairs.
+__global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ idx, const int *__restrict__ rank,
+                                                       const int *__restrict__ chunk_base,
+                                                       const int *__restrict__ counts, int T, int K, int N,
+                                                       int chunk_tokens, int ld_chunks, int BM,
+                                                       int *__restrict__ offsets, int *__restrict__ tile_expert,
+                                                       int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
+                                                       int *__restrict__ pos, int *__restrict__ perm)
+{
+    __shared__ int s_off[1024];
+    __shared__ int s_wsum[16];
+    const int tid = threadIdx.x;
+    const int c = (tid < N) ? counts[tid] : 0;
+    finalize_block(c, blockIdx.x == 0, (int64_t)blockIdx.x * 1024 + tid, (int64_t)gridDim.x * 1024, idx, rank,
+                   chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, offsets, tile_expert, tile_row0, n_mtiles, pos,
+                   perm, s_off, s_wsum);
+}
+
+// Small batches (at most 64 chunks): the chunk scan and finalize in one
+// workgroup of 1024 threads -- one launch instead of two.  A wave scans an
+// expert's chunk counts with one lane per chunk; the chunk bases it writes
+// are read back by other waves of this workgroup after the barrier.
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restrict__ chunk_counts, int nchunks,
+                                                             const int *__restrict__ idx, const int *__restrict__ rank,
+                                                             int T, int K, int N, int chunk_tokens, int ld_chunks,
+                                                             int BM, int *__restrict__ chunk_base,
+                                                             int *__restrict__ counts, int *__restrict__ offsets,
+                                                             int *__restrict__ tile_expert, int *__restrict__ tile_row0,
+                                                             int *__restrict__ n_mtiles, int *__restrict__ pos,
+                                                             int *__restrict__ perm)
+{
+    __shared__ int s_off[1024];
+    __shared__ int s_wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // a wave's experts e = wave + 16 u, up to 16 at a time with every load
+    // issued before the scans (a chain of dependent loads would dominate)
+    for (int e0 = wave; e0 < N; e0 += 16 * 16) {
+        int v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = e0 + 16 * u;
+            v[u] = (e < N && lane < nchunks) ? chunk_counts[(int64_t)e * ld_chunks + lane] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = e0 + 16 * u;
+            if (e >= N)
+                break;
+            const int incl = wave_incl_scan(v[u], lane);
+            if (lane < nchunks)
+                chunk_base[(int64_t)e * ld_chunks + lane] = incl - v[u];
+            if (lane == 63) {
+                s_off[e] = incl;
+                counts[e] = incl;
+            }
+        }
+    }
+    __syncthreads();
+    const int c = (tid < N) ? s_off[tid] : 0;
+    __syncthreads();  // s_off is reused for the offsets
+    finalize_block(c, true, tid, 1024, idx, rank, chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, offsets,
+                   tile_expert, tile_row0, n_mtiles, pos, perm, s_off, s_wsum);
 }
 
 }  // namespace lmoe

@@ -471,21 +471,29 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     tm.begin(ST_SELECT);
     launch_select(h, T, s);
     tm.end(ST_SELECT);
-    // 2-4: dispatch order
-    tm.begin(ST_SCAN);
-    chunk_scan_kernel<<<dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s>>>(h->chunk_counts, nchunks, (int)p.ld_chunks,
-                                                                          N, h->chunk_base, h->counts);
-    hip_check(hipGetLastError());
-    tm.end(ST_SCAN);
-    tm.begin(ST_FINALIZE);
-    {
+    // 2-4: dispatch order (small batches: one workgroup, one launch)
+    if (nchunks <= 64) {
+        tm.begin(ST_FINALIZE);
+        dispatch_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(
+            h->chunk_counts, nchunks, h->idx, h->rank, T, K, N, kRouterTokens, (int)p.ld_chunks, gbm, h->chunk_base,
+            h->counts, h->offsets, h->tile_expert, h->tile_row0, h->n_mtiles, h->pos, h->perm);
+        hip_check(hipGetLastError());
+        tm.end(ST_FINALIZE);
+    } else {
+        tm.begin(ST_SCAN);
+        chunk_scan_kernel<<<dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s>>>(h->chunk_counts, nchunks,
+                                                                              (int)p.ld_chunks, N, h->chunk_base,
+                                                                              h->counts);
+        hip_check(hipGetLastError());
+        tm.end(ST_SCAN);
+        tm.begin(ST_FINALIZE);
         const int64_t blocks = std::min<int64_t>((P + 1023) / 1024, 256);
         finalize_kernel<<<dim3((unsigned)blocks), dim3(1024), 0, s>>>(
             h->idx, h->rank, h->chunk_base, h->counts, T, K, N, kRouterTokens, (int)p.ld_chunks, gbm,
             h->offsets, h->tile_expert, h->tile_row0, h->n_mtiles, h->pos, h->perm);
+        hip_check(hipGetLastError());
+        tm.end(ST_FINALIZE);
     }
-    hip_check(hipGetLastError());
-    tm.end(ST_FINALIZE);
 
     // 5: H = relu(z[perm] W1_e)^2
     GemmParams g1{};
