@@ -16,6 +16,8 @@ _TORCH = {"bf16": torch.bfloat16, "f32": torch.float32}
 def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
     """float32 array, or uint16 array of bf16 bits, -> device tensor."""
     a = np.ascontiguousarray(a)
+    if not a.flags.writeable:  # torch wants writable memory; the copy is on the host only
+        a = a.copy()
     if a.dtype == np.uint16:
         assert dtype == "bf16"
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)

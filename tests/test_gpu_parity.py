@@ -131,10 +131,15 @@ def test_exact_score_ties_follow_index_order(dtype):
     dict(T=64, d=128, l=64, m=128, n_experts=32, top_k=4, n_shared=0, m_shared=0, alpha=2),
     dict(T=99, d=256, l=64, m=320, n_experts=64, top_k=8, n_shared=3, m_shared=192, alpha=4),
     dict(T=40, d=128, l=128, m=64, n_experts=16, top_k=2, n_shared=1, m_shared=64, alpha=1),
+    # dispatch at its limits: 1024 experts over 64 chunks (one-workgroup path),
+    # then 65 chunks and 1008 experts (two-kernel path, a partial last batch)
+    dict(T=1024, d=128, l=64, m=64, n_experts=1024, top_k=8, n_shared=1, m_shared=64, alpha=2),
+    dict(T=1040, d=128, l=64, m=64, n_experts=1008, top_k=6, n_shared=0, m_shared=0, alpha=2, variant="eff"),
 ])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_shape_edge_cases(cfg, dtype):
-    """K' = 1, K' = N', no shared expert, odd tile multiples, alpha = 1."""
+    """K' = 1, K' = N', no shared expert, odd tile multiples, alpha = 1, the
+    largest expert count."""
     sh = shape(dtype=dtype, **cfg)
     _full_check(random_workload(sh, seed=cfg["T"]))
 
