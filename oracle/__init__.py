@@ -19,7 +19,10 @@ mixture; K' = 1 gives gate 1; zero router gives experts 0..K'-1 at 1/K';
 standard MoE reduction at alpha 1 with identity projections); invariants
 (gates sum to 1, distinct indices, dispatch is a bijection, degree-2
 homogeneity of the routed and shared paths under fixed routing, token
-permutation equivariance, expert relabelling invariance); and every worked
-number of the explainer page for ``cost.py``.  No function here is left
+permutation equivariance, expert relabelling invariance); every worked
+number of the explainer page for ``cost.py``; and for FP8 (E4M3) expert banks
+the format's defining values, all 256 byte values against torch's
+float8_e4m3fn, equality with the bf16 path at power-of-two scales, and the
+dense brute force with arbitrary per-column scales.  No function here is left
 parity-unpinned.
 """

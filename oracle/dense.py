@@ -68,6 +68,20 @@ def layer_dense(x, w_router, b_router, w_down, w1, w2, w_up, w1_s, w2_s, K):
     return {"logits": s, "G": G, "z": z, "u": u, "y": y}
 
 
+def expert_bank_f64(wl, name):
+    """W1 or W2 of a workload in float64.  FP8 (E4M3) banks are decoded with
+    torch's float8_e4m3fn type -- a decoder independent of the C oracle's --
+    and scaled per expert and output column: W[e, i, j] = decode(q) * s[e, j]
+    (exact in float64)."""
+    if wl.shape.expert_dtype != "fp8":
+        return wl.f64(name)
+    import torch
+    q = np.ascontiguousarray(wl.tensors[name], dtype=np.uint8)
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    sc = np.asarray(wl.tensors[name + "_scale"], dtype=np.float64)
+    return dec * sc[:, None, :]
+
+
 def layer_dense_from_workload(wl, tokens=None):
     f = wl.f64
     x = f("x") if tokens is None else f("x")[np.asarray(tokens)]
@@ -76,8 +90,8 @@ def layer_dense_from_workload(wl, tokens=None):
     S = wl.shape.n_shared
     w1s = f("w1_s") if S > 0 else np.zeros((0, wl.shape.d, 1))
     w2s = f("w2_s") if S > 0 else np.zeros((0, 1, wl.shape.d))
-    return layer_dense(x, f("w_router"), b, f("w_down"), f("w1"), f("w2"), f("w_up"),
-                       w1s, w2s, wl.shape.top_k)
+    return layer_dense(x, f("w_router"), b, f("w_down"), expert_bank_f64(wl, "w1"),
+                       expert_bank_f64(wl, "w2"), f("w_up"), w1s, w2s, wl.shape.top_k)
 
 
 def dispatch_argsort(idx: np.ndarray, N: int):

@@ -35,6 +35,15 @@
  * Arithmetic: every stored value (bf16 bits or float32) is widened exactly
  * to double and all sums are in double in plain index order.  No blocking,
  * fusion or reordering beyond the definition above.
+ *
+ * FP8 expert banks (the explainer's byte-count section prices expert weights
+ * in FP8 and gives no scale convention; the reading taken here): W1 and W2
+ * may be stored as OCP 8-bit floats of the E4M3 kind (1 sign bit, 4 exponent
+ * bits of bias 7, 3 mantissa bits; exponent field 0 holds the subnormals
+ * 2^-6 * mantissa/8; exponent 15 with mantissa 7 is NaN; no infinities; the
+ * largest finite value is 448) with one float32 scale per expert and output
+ * column: W_e[i][j] = decode(q_e[i][j]) * scale_e[j], formed exactly in
+ * double.
  */
 #include <math.h>
 #include <stdint.h>
@@ -46,8 +55,9 @@
 
 typedef struct {
     int64_t d, l, m, m_s, n_shared, n_experts, top_k;
-    int32_t bf16;     /* 1: tensors hold bf16 bit patterns, 0: float32 */
-    int32_t has_bias; /* 1: b_router is used */
+    int32_t bf16;       /* 1: tensors hold bf16 bit patterns, 0: float32 */
+    int32_t has_bias;   /* 1: b_router is used */
+    int32_t expert_fp8; /* 1: w1 and w2 hold E4M3 bytes with per-column scales */
 } orc_shape;
 
 typedef struct {
@@ -60,6 +70,8 @@ typedef struct {
     const void *w_up;     /* [l, d] */
     const void *w1_s;     /* [S, d, m_s] */
     const void *w2_s;     /* [S, m_s, d] */
+    const float *w1_scale;/* [N', m]  (FP8 expert banks only) */
+    const float *w2_scale;/* [N', l]  (FP8 expert banks only) */
 } orc_tensors;
 
 /* Optional per-token outputs; any pointer may be NULL.  Row r of each array
@@ -85,6 +97,44 @@ static double ld_elem(const void *base, int64_t i, int bf16)
         return (double)f;
     }
     return (double)((const float *)base)[i];
+}
+
+/* Value of an E4M3 byte (see the header). */
+static double fp8_e4m3(uint8_t q)
+{
+    const int sign = q >> 7, e = (q >> 3) & 15, mant = q & 7;
+    double v;
+    if (e == 15 && mant == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)mant / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)mant / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* The decode alone, for pinning it: out[i] = value of q[i]. */
+int orc_fp8_decode(const uint8_t *q, int64_t n, double *out)
+{
+    if (!q || !out || n < 0)
+        return -1;
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = fp8_e4m3(q[i]);
+    return 0;
+}
+
+/* out[j] = sum_i in[i] * (decode(Q[off + i*cols + j]) * scale[j]) */
+static void matvec_fp8(const double *in, const uint8_t *Q, int64_t off, int64_t rows,
+                       int64_t cols, const float *scale, double *out)
+{
+    for (int64_t j = 0; j < cols; ++j)
+        out[j] = 0.0;
+    for (int64_t i = 0; i < rows; ++i) {
+        const double a = in[i];
+        const int64_t row = off + i * cols;
+        for (int64_t j = 0; j < cols; ++j)
+            out[j] += a * (fp8_e4m3(Q[row + j]) * (double)scale[j]);
+    }
 }
 
 /* out[j] = sum_i in[i] * W[off + i*cols + j]  (W row-major [rows, cols]) */
@@ -162,6 +212,8 @@ int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
                 const orc_outputs *out, int n_threads)
 {
     if (check_shape(c) || !w || !tokens || !out)
+        return -1;
+    if (c->expert_fp8 && (!w->w1_scale || !w->w2_scale))
         return -1;
     for (int64_t r = 0; r < n_tok; ++r)
         if (tokens[r] < 0 || tokens[r] >= T)
@@ -242,12 +294,18 @@ int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
                 u[j] = 0.0;
             for (int64_t k = 0; k < K; ++k) {
                 const int64_t e = sel[k];
-                matvec(z, w->w1, e * l * m, l, m, bf, a);
+                if (c->expert_fp8)
+                    matvec_fp8(z, (const uint8_t *)w->w1, e * l * m, l, m, w->w1_scale + e * m, a);
+                else
+                    matvec(z, w->w1, e * l * m, l, m, bf, a);
                 for (int64_t j = 0; j < m; ++j)
                     a[j] = sq_relu(a[j]);
                 if (out->h)
                     memcpy(out->h + (r * K + k) * m, a, sizeof(double) * (size_t)m);
-                matvec(a, w->w2, e * m * l, m, l, bf, o);
+                if (c->expert_fp8)
+                    matvec_fp8(a, (const uint8_t *)w->w2, e * m * l, m, l, w->w2_scale + e * l, o);
+                else
+                    matvec(a, w->w2, e * m * l, m, l, bf, o);
                 if (out->o)
                     memcpy(out->o + (r * K + k) * l, o, sizeof(double) * (size_t)l);
                 for (int64_t j = 0; j < l; ++j)

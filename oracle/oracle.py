@@ -27,12 +27,12 @@ _vp = C.c_void_p
 class _Shape(C.Structure):
     _fields_ = [("d", _i64), ("l", _i64), ("m", _i64), ("m_s", _i64),
                 ("n_shared", _i64), ("n_experts", _i64), ("top_k", _i64),
-                ("bf16", _i32), ("has_bias", _i32)]
+                ("bf16", _i32), ("has_bias", _i32), ("expert_fp8", _i32)]
 
 
 class _Tensors(C.Structure):
     _fields_ = [(n, _vp) for n in ("x", "w_router", "b_router", "w_down", "w1",
-                                   "w2", "w_up", "w1_s", "w2_s")]
+                                   "w2", "w_up", "w1_s", "w2_s", "w1_scale", "w2_scale")]
 
 
 class _Outputs(C.Structure):
@@ -60,6 +60,8 @@ def lib():
         L.orc_dispatch.restype = C.c_int
         L.orc_max_threads.argtypes = []
         L.orc_max_threads.restype = C.c_int
+        L.orc_fp8_decode.argtypes = [_vp, _i64, _vp]
+        L.orc_fp8_decode.restype = C.c_int
         _lib = L
     return _lib
 
@@ -98,13 +100,23 @@ def forward(wl, tokens: Optional[Sequence[int]] = None, want=("y",),
     """
     sh = wl.shape
     bf16 = sh.dtype == "bf16"
+    fp8 = sh.expert_dtype == "fp8"
     T = sh.T
     tok = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
     n = tok.shape[0]
     N, K, l, m, d = sh.n_experts, sh.top_k, sh.l, sh.m, sh.d
     S, ms = sh.n_shared, sh.m_shared
     t = {k: (None if wl.tensors.get(k) is None else _storage(wl.tensors[k], bf16))
-         for k in ("x", "w_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s")}
+         for k in ("x", "w_router", "w_down", "w_up", "w1_s", "w2_s")}
+    for k in ("w1", "w2"):
+        if fp8:
+            t[k] = np.ascontiguousarray(wl.tensors[k], dtype=np.uint8)
+            sc = np.ascontiguousarray(wl.tensors[k + "_scale"], dtype=np.float32)
+            assert sc.shape == (N, m if k == "w1" else l)
+            t[k + "_scale"] = sc
+        else:
+            t[k] = _storage(wl.tensors[k], bf16)
+            t[k + "_scale"] = None
     b = wl.tensors.get("b_router")
     if b is not None:
         b = np.ascontiguousarray(b, dtype=np.float32)
@@ -117,10 +129,11 @@ def forward(wl, tokens: Optional[Sequence[int]] = None, want=("y",),
         setattr(res, name, arr)
         setattr(outs, name, arr.ctypes.data)
     cs = _Shape(d, l, m, ms if S > 0 else 0, S, N, K, 1 if bf16 else 0,
-                1 if (sh.has_bias and b is not None) else 0)
+                1 if (sh.has_bias and b is not None) else 0, 1 if fp8 else 0)
     ct = _Tensors(_ptr(t["x"]), _ptr(t["w_router"]), _ptr(b), _ptr(t["w_down"]),
                   _ptr(t["w1"]), _ptr(t["w2"]), _ptr(t["w_up"]),
-                  _ptr(t["w1_s"]) if S > 0 else None, _ptr(t["w2_s"]) if S > 0 else None)
+                  _ptr(t["w1_s"]) if S > 0 else None, _ptr(t["w2_s"]) if S > 0 else None,
+                  _ptr(t["w1_scale"]), _ptr(t["w2_scale"]))
     forced = None
     if idx_in is not None:
         forced = np.ascontiguousarray(idx_in, dtype=np.int32)
@@ -180,3 +193,13 @@ def dispatch(idx: np.ndarray, N: int) -> Dispatch:
 
 def max_threads() -> int:
     return int(lib().orc_max_threads())
+
+
+def fp8_decode(q: np.ndarray) -> np.ndarray:
+    """The oracle's own E4M3 decode of every byte of ``q`` (float64)."""
+    a = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.zeros(a.shape, dtype=np.float64)
+    rc = lib().orc_fp8_decode(a.ctypes.data, a.size, out.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("orc_fp8_decode failed")
+    return out

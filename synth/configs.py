@@ -19,6 +19,9 @@ Shapes follow the pages:
                          d 2560, 16384 tokens, and a router bias
                          b_e = 2 ln(Zipf_1.1 weight of rank e+1) that makes
                          expert loads heavily imbalanced.
+  * ``decode_eff_fp8`` -- decode_eff with W1/W2 quantized to FP8 E4M3 (the
+                         explainer's byte-count section prices expert weights
+                         in FP8): half the expert bytes per decoded token.
 """
 
 from dataclasses import dataclass
@@ -42,6 +45,7 @@ class LayerShape:
     seed: int         # seed of the weights
     x_seed: Optional[int] = None   # seed of x if it differs from ``seed``
     zipf_s: Optional[float] = None  # router bias exponent (None: no bias)
+    expert_dtype: Optional[str] = None  # "fp8": W1/W2 as E4M3 bytes + per-column scales
 
     @property
     def P(self) -> int:
@@ -76,6 +80,12 @@ CONFIGS = {
                             n_experts=512, top_k=16, n_shared=1, m_shared=1024,
                             alpha=4, variant="acc", dtype="bf16", seed=4,
                             zipf_s=1.1),
+    # decode_eff with the routed-expert banks in FP8 (E4M3, one scale per
+    # expert and output column), the format the explainer's byte count uses
+    "decode_eff_fp8": LayerShape("decode_eff_fp8", T=64, d=2048, l=512, m=1408,
+                                 n_experts=256, top_k=6, n_shared=2, m_shared=1408,
+                                 alpha=4, variant="eff", dtype="bf16", seed=1,
+                                 x_seed=2, expert_dtype="fp8"),
 }
 
 CONFIG_ORDER = ["tiny_f32", "readme_acc", "decode_eff", "wide_prefill", "zipf_skew"]

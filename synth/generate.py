@@ -18,6 +18,12 @@ All draws are float32.  For bf16 workloads each tensor is rounded to bf16
 (round to nearest, ties to even) once; the rounded values are canonical.
 Large expert banks are drawn one expert at a time, in expert order, from the
 same generator.
+
+FP8 expert banks (``expert_dtype="fp8"``): each expert's W1 and W2 float32
+draw is quantized per output column j: scale_j = max_i |W[i, j]| / 448 (the
+largest finite E4M3 value) and q[i, j] = E4M3(W[i, j] / scale_j), rounded to
+nearest even by torch's float8_e4m3fn conversion.  The bytes q and the
+float32 scales are the canonical inputs; the other tensors stay bf16.
 """
 
 from dataclasses import dataclass, field
@@ -71,6 +77,8 @@ class Workload:
         a = self.tensors[name]
         if a is None:
             return None
+        if a.dtype == np.uint8:
+            raise TypeError(f"{name} holds FP8 bytes; their values need the per-column scales")
         if a.dtype == np.uint16:
             return bf16_bits_to_f32(a)
         return a
@@ -104,6 +112,27 @@ def _bank(rng, n, shape, fan_in, dtype) -> np.ndarray:
     return out
 
 
+def quantize_e4m3_columns(w: np.ndarray):
+    """w [in, out] float32 -> (q uint8 [in, out], scale float32 [out]):
+    scale_j = max_i |w[i, j]| / 448 (1 for an all-zero column) and
+    q = E4M3(w / scale), nearest-even, by torch's float8_e4m3fn conversion."""
+    import torch
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w), axis=0)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = torch.from_numpy(w / scale[None, :]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return np.ascontiguousarray(q), scale
+
+
+def _bank_fp8(rng, n, shape, fan_in):
+    """Like _bank, each expert quantized per output column (see the header)."""
+    q = np.empty((n,) + tuple(shape), dtype=np.uint8)
+    sc = np.empty((n, shape[1]), dtype=np.float32)
+    for e in range(n):
+        q[e], sc[e] = quantize_e4m3_columns(_normal(rng, shape, fan_in))
+    return q, sc
+
+
 def zipf_router_bias(n_experts: int, s: float) -> np.ndarray:
     r = np.arange(1, n_experts + 1, dtype=np.float64)
     w = r ** (-s)
@@ -117,15 +146,19 @@ def _children(seed: int):
 
 @lru_cache(maxsize=4)
 def _weights(shape_key: tuple) -> Dict[str, np.ndarray]:
-    (d, l, m, n_e, S, m_s, dtype, seed, zipf_s) = shape_key
+    (d, l, m, n_e, S, m_s, dtype, seed, zipf_s, expert_dtype) = shape_key
     ch = _children(seed)
     g = {name: np.random.default_rng(c) for name, c in zip(_ORDER, ch)}
     w = {}
     w["w_router"] = _store(_normal(g["w_router"], (d, n_e), d), dtype)
     w["b_router"] = None if zipf_s is None else zipf_router_bias(n_e, zipf_s)
     w["w_down"] = _store(_normal(g["w_down"], (d, l), d), dtype)
-    w["w1"] = _bank(g["w1"], n_e, (l, m), l, dtype)
-    w["w2"] = _bank(g["w2"], n_e, (m, l), m, dtype)
+    if expert_dtype == "fp8":
+        w["w1"], w["w1_scale"] = _bank_fp8(g["w1"], n_e, (l, m), l)
+        w["w2"], w["w2_scale"] = _bank_fp8(g["w2"], n_e, (m, l), m)
+    else:
+        w["w1"] = _bank(g["w1"], n_e, (l, m), l, dtype)
+        w["w2"] = _bank(g["w2"], n_e, (m, l), m, dtype)
     w["w_up"] = _store(_normal(g["w_up"], (l, d), l), dtype)
     w["w1_s"] = _bank(g["w1_s"], S, (d, m_s), d, dtype)
     w["w2_s"] = _bank(g["w2_s"], S, (m_s, d), m_s, dtype)
@@ -146,7 +179,7 @@ def make_workload(shape: LayerShape, T: Optional[int] = None,
                   x_seed: Optional[int] = None) -> Workload:
     """Weights from ``shape.seed``; x from ``x_seed`` (default: the shape's)."""
     key = (shape.d, shape.l, shape.m, shape.n_experts, shape.n_shared,
-           shape.m_shared, shape.dtype, shape.seed, shape.zipf_s)
+           shape.m_shared, shape.dtype, shape.seed, shape.zipf_s, shape.expert_dtype)
     w = _weights(key)
     x = make_x(shape, T, x_seed)
     t = dict(w)

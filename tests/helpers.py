@@ -7,10 +7,11 @@ from synth.generate import f32_to_bf16_bits
 
 
 def shape(name="custom", T=8, d=8, l=4, m=6, n_experts=4, top_k=2, n_shared=1,
-          m_shared=5, alpha=2, variant="acc", dtype="f32", seed=0, zipf_s=None):
+          m_shared=5, alpha=2, variant="acc", dtype="f32", seed=0, zipf_s=None, expert_dtype=None):
     return LayerShape(name, T=T, d=d, l=l, m=m, n_experts=n_experts, top_k=top_k,
                       n_shared=n_shared, m_shared=m_shared, alpha=alpha,
-                      variant=variant, dtype=dtype, seed=seed, zipf_s=zipf_s)
+                      variant=variant, dtype=dtype, seed=seed, zipf_s=zipf_s,
+                      expert_dtype=expert_dtype)
 
 
 def workload_from_arrays(sh: LayerShape, arrays: dict) -> Workload:
@@ -63,3 +64,25 @@ def near_tie_mask(logits: np.ndarray, K: int, gap: float = 1e-3) -> np.ndarray:
         return np.zeros(logits.shape[0], dtype=bool)
     srt = -np.sort(-logits, axis=1)
     return (srt[:, K - 1] - srt[:, K]) < gap
+
+
+def random_fp8_workload(sh: LayerShape, seed=0, pow2_scales=False) -> Workload:
+    """A random workload whose W1/W2 are FP8 (E4M3) banks with per-column
+    scales (the input recipe's quantizer), the rest as for random_workload.
+    pow2_scales: replace every scale by a power of two (varying per expert and
+    column), so that decode(q) * scale is exact in bf16."""
+    from synth.generate import quantize_e4m3_columns
+    assert sh.expert_dtype == "fp8"
+    rng = np.random.default_rng(seed)
+    arrays = random_arrays(sh, rng)
+    t = dict(workload_from_arrays(sh, arrays).tensors)
+    for k in ("w1", "w2"):
+        w = arrays[k]
+        q = np.empty(w.shape, dtype=np.uint8)
+        sc = np.empty((w.shape[0], w.shape[2]), dtype=np.float32)
+        for e in range(w.shape[0]):
+            q[e], sc[e] = quantize_e4m3_columns(w[e])
+        if pow2_scales:
+            sc = np.ldexp(np.float32(1.0), rng.integers(-9, -3, size=sc.shape)).astype(np.float32)
+        t[k], t[k + "_scale"] = q, sc
+    return Workload(sh, t)
