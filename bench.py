@@ -35,6 +35,8 @@ def stage_work(sh, T, n_active):
     GEMMs stream only those experts' weights).  None = not counted."""
     P = T * sh.top_k
     es = 2 if sh.dtype == "bf16" else 4
+    fp8 = sh.expert_dtype == "fp8"
+    ew = 1 if fp8 else es            # bytes per routed-expert weight
     ms = sh.n_shared * sh.m_shared
     ldzh = sh.l + ms
     N, d, l, m = sh.n_experts, sh.d, sh.l, sh.m
@@ -42,8 +44,11 @@ def stage_work(sh, T, n_active):
         # one pass over x: router scores (fp32 out), z and the shared-expert hidden layer
         "gemm_x_router_down_shared1": (2.0 * T * d * (N + ldzh),
                                        es * (T * d + d * (N + ldzh) + T * ldzh) + 4.0 * T * N),
-        "grouped_gemm1_relu2": (2.0 * P * l * m, es * (n_active * l * m + P * l + P * m) + 4.0 * P),
-        "grouped_gemm2": (2.0 * P * m * l, es * (n_active * m * l + P * m + P * l)),
+        # expert weights (+ their fp32 column scales for E4M3 banks), rows in and out
+        "grouped_gemm1_relu2": (2.0 * P * l * m, ew * n_active * l * m + (4.0 * n_active * m if fp8 else 0.0)
+                                + es * (P * l + P * m) + 4.0 * P),
+        "grouped_gemm2": (2.0 * P * m * l, ew * n_active * m * l + (4.0 * n_active * l if fp8 else 0.0)
+                          + es * (P * m + P * l)),
         "gemm_up_shared2": (2.0 * T * ldzh * d, es * (ldzh * d + T * ldzh + T * d)),
         # gather P rows of l, write T rows of l, read pos and gate
         "combine": (None, float(P * l * es + T * l * es + P * 8)),
@@ -217,7 +222,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{sh.name}: LatentMoE layer forward, T={T} d={sh.d} l={sh.l} m={sh.m} "
                                f"N'={sh.n_experts} K'={sh.top_k} S={sh.n_shared}x{sh.m_shared} "
-                               f"{sh.variant} {sh.dtype}", "tokens": T, "experts_with_tokens": n_active},
+                               f"{sh.variant} {sh.dtype}"
+                               + (" (routed experts E4M3 + per-column scales)" if sh.expert_dtype == "fp8" else ""),
+                   "tokens": T, "experts_with_tokens": n_active},
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
         "roofline": roof, "cpu_baseline": cpu, "stages": stage_out,
         "stages_note": "per-stage HIP-event times from an untimed pass of min(steps, 10) forwards; "

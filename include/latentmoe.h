@@ -51,6 +51,18 @@ typedef enum latentmoe_variant { LATENTMOE_VARIANT_ACC = 0, LATENTMOE_VARIANT_EF
  * intermediates.  F32: fp32 tensors and intermediates throughout. */
 typedef enum latentmoe_dtype { LATENTMOE_DTYPE_F32 = 0, LATENTMOE_DTYPE_BF16 = 1 } latentmoe_dtype;
 
+/* Storage of the routed-expert banks W1 and W2.  AS_DTYPE: the config dtype.
+ * FP8_E4M3 (bf16 configs only; the explainer's byte-count section prices
+ * expert weights in FP8): OCP E4M3 bytes (bias 7, subnormals at exponent 0,
+ * NaN at exponent 15 / mantissa 7, no infinities) with one fp32 scale per
+ * expert and output column, W[e][i][j] = value(q[e][i][j]) * scale[e][j].
+ * Expert GEMMs then read half the bytes; the values are widened exactly to
+ * bf16 for the matrix cores and the scale is applied to the fp32 sums. */
+typedef enum latentmoe_expert_format {
+    LATENTMOE_EXPERT_AS_DTYPE = 0,
+    LATENTMOE_EXPERT_FP8_E4M3 = 1
+} latentmoe_expert_format;
+
 typedef struct latentmoe_config {
     int64_t d;          /* model width */
     int64_t l;          /* latent width; l * alpha == d */
@@ -64,12 +76,13 @@ typedef struct latentmoe_config {
     int32_t dtype;      /* latentmoe_dtype */
     int64_t max_tokens; /* largest T a forward call may pass; sizes the workspace */
     int32_t has_router_bias; /* 1: b_router is added to the scores before softmax */
-    int32_t reserved;
+    int32_t expert_format;   /* latentmoe_expert_format */
 } latentmoe_config;
 
-/* Device pointers, in the config's dtype except b_router (always fp32).
- * latentmoe_create copies and repacks them; the caller may free or change
- * them once it returns. */
+/* Device pointers, in the config's dtype except b_router and the scales
+ * (always fp32) and W1/W2 under LATENTMOE_EXPERT_FP8_E4M3 (one byte per
+ * weight).  latentmoe_create copies and repacks them; the caller may free or
+ * change them once it returns. */
 typedef struct latentmoe_weights {
     const void *w_router;   /* [d, N'] */
     const float *b_router;  /* [N'] or NULL */
@@ -79,6 +92,8 @@ typedef struct latentmoe_weights {
     const void *w_up;       /* [l, d] */
     const void *w1_shared;  /* [S, d, m_shared] (NULL when S == 0) */
     const void *w2_shared;  /* [S, m_shared, d] (NULL when S == 0) */
+    const float *w1_scale;  /* [N', m] FP8 expert banks only, else NULL */
+    const float *w2_scale;  /* [N', l] FP8 expert banks only, else NULL */
 } latentmoe_weights;
 
 /* Optional device buffers that a forward call fills with its intermediate

@@ -25,6 +25,11 @@
 // Epilogue: the first c_split columns (router scores) are stored in fp32 with
 // a per-column bias; the rest go to C, where columns >= relu2_from get
 // relu(v)^2 (squared-ReLU expert activation), rounded to E.
+//
+// E4M3 expert weights (grouped GEMMs of a bf16 layer): B tiles hold the bytes
+// (64 per row and k-tile), fragments are widened to bf16 in registers (exact:
+// every E4M3 value is a bf16 value) and the per-column fp32 scale multiplies
+// the fp32 sums before the epilogue, which equals multiplying the weights.
 #pragma once
 
 #include "common.hpp"
@@ -57,6 +62,7 @@ struct GemmParams {
     const int *tile_row0;    // [tiles] first row of the tile inside its expert
     const int *n_mtiles;     // device scalar: number of valid M tiles
     const int *offsets;      // [N'+1] first dispatch row of each expert
+    const float *scaleB;     // grouped, E4M3 B: [N'][N] scale of each expert's output column
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -152,7 +158,22 @@ __device__ __forceinline__ bool locate_tile(const GemmParams &p, TileInfo &ti)
 
 // Multiply one LDS k-tile (128 bytes of K: four k-steps of 32 bytes) into the
 // wave's 32x32 accumulator tiles.
-template <typename E, int TM, int TN, int WTM, int WTN>
+// Eight E4M3 bytes (K order) -> eight bf16 (exact: every E4M3 value is a
+// bf16 value), element 0 in the low half of the first word.
+__device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 v)
+{
+    uint4 r;
+    r.x = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, false));
+    r.y = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, true));
+    r.z = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, false));
+    r.w = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, true));
+    return r;
+}
+
+// BQ8: the B tile holds E4M3 bytes, 64 per row and k-tile (4 chunks of 16,
+// chunk c of row r at c ^ ((r >> 2) & 3)); a fragment is 8 bytes, widened to
+// bf16 in registers.
+template <typename E, int TM, int TN, int WTM, int WTN, bool BQ8 = false>
 __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, const uint4 *b, int wm, int wn, int lane)
 {
 #pragma unroll
@@ -167,7 +188,10 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int r = wn * WTN + j * 32 + (lane & 31);
-            bfr[j] = b[r * 8 + (c ^ ((r >> 1) & 7))];
+            if constexpr (BQ8)
+                bfr[j] = e4m3x8_to_bf16(reinterpret_cast<const uint2 *>(b + r * 4 + (s ^ ((r >> 2) & 3)))[lane >> 5]);
+            else
+                bfr[j] = b[r * 8 + (c ^ ((r >> 1) & 7))];
         }
         // B fragment first: the tile's rows are output columns, so a lane
         // owns runs of 4 consecutive output columns of output row lane % 32.
@@ -184,7 +208,8 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
 // rest to C, with relu^2 from relu2_from on.
 template <typename E, int TM, int TN, int WTM, int WTN>
 __device__ __forceinline__ void store_tile_direct(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t row_base,
-                                                  int rows_valid, int n0, int wm, int wn, int lane)
+                                                  int rows_valid, int n0, int wm, int wn, int lane,
+                                                  const float *cs = nullptr)
 {
     E *C = static_cast<E *>(p.C);
 #pragma unroll
@@ -201,6 +226,11 @@ __device__ __forceinline__ void store_tile_direct(const GemmParams &p, const f32
                 if (col >= p.N)
                     continue;
                 float v[4] = {acc[i][jn][4 * g], acc[i][jn][4 * g + 1], acc[i][jn][4 * g + 2], acc[i][jn][4 * g + 3]};
+                if (cs) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] *= cs[col + r];
+                }
                 if (col < p.c_split) {
                     if (p.bias32) {
 #pragma unroll
@@ -231,7 +261,8 @@ __device__ __forceinline__ void store_tile_direct(const GemmParams &p, const f32
 // Chunk c of staged row r sits at position c ^ (r % CPR).
 template <typename E, int TM, int TN, int WTM, int WTN>
 __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t row_base,
-                                                  int rows_valid, int n0, int wm, int wn, int lane, uint4 *stg)
+                                                  int rows_valid, int n0, int wm, int wn, int lane, uint4 *stg,
+                                                  const float *cs = nullptr)
 {
     constexpr int ES = (int)sizeof(E);
     constexpr int CPR = WTN * ES / 16;  // 16-byte chunks per staged row
@@ -254,6 +285,12 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
             for (int g = 0; g < 4; ++g) {
                 const int cc = jn * 32 + 8 * g + 4 * lc;  // column inside the wave block
                 float v[4] = {acc[i][jn][4 * g], acc[i][jn][4 * g + 1], acc[i][jn][4 * g + 2], acc[i][jn][4 * g + 3]};
+                if (cs) {
+                    const int col = n0 + wn * WTN + cc;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] *= (col + r < p.N) ? cs[col + r] : 0.f;
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (cbase + cc + r >= p.relu2_from) {
@@ -278,24 +315,27 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
     }
 }
 
-// k-tile kt of A and B straight into LDS (buffer loads with the LDS bit: lane
+// k-tile KT of A and B straight into LDS (buffer loads with the LDS bit: lane
 // l of a wave writes 16 bytes at the wave's base + 16 l; rows out of range
-// read as zeros).  Position P of a tile holds row r = P / 8, chunk
-// (P % 8) ^ ((r / 2) % 8); instruction i of wave w fills positions
-// (i * NW + w) * 64 .. +63.
-#define LMOE_TILE_DMA(SA, SB, KOFF)                                                                       \
+// read as zeros).  Position P of an A tile holds row r = P / 8, chunk
+// (P % 8) ^ ((r / 2) % 8); of a B tile row P / CHB, chunk (P % CHB) ^ the
+// B swizzle; instruction i of wave w fills positions (i * NW + w) * 64 .. +63.
+#define LMOE_TILE_DMA(SA, SB, KT)                                                                         \
     {                                                                                                      \
+        const unsigned kt_ = (unsigned)(KT);                                                               \
         _Pragma("unroll") for (int i_ = 0; i_ < NIA; ++i_) __builtin_amdgcn_raw_ptr_buffer_load_lds(       \
-            ra_rsrc, LMOE_LDS((SA) + (i_ * NW + wave) * 64), 16, a_off[i_] + (KOFF), 0, 0, 0);              \
+            ra_rsrc, LMOE_LDS((SA) + (i_ * NW + wave) * 64), 16, a_off[i_] + kt_ * 128u, 0, 0, 0);          \
         _Pragma("unroll") for (int i_ = 0; i_ < NIB; ++i_) __builtin_amdgcn_raw_ptr_buffer_load_lds(       \
-            rb_rsrc, LMOE_LDS((SB) + (i_ * NW + wave) * 64), 16, b_off[i_] + (KOFF), 0, 0, 0);              \
+            rb_rsrc, LMOE_LDS((SB) + (i_ * NW + wave) * 64), 16, b_off[i_] + kt_ * (CHB * 16u), 0, 0, 0);   \
     }
 
 // NT = 64 * WM * WN threads; NS LDS stages (2 or 3), one barrier per k-tile;
 // tiles kt+1 .. kt+NS-1 are in flight while tile kt is multiplied.  STAGE only
 // names the layer stage, so that each stage is its own kernel symbol in
-// profiles.
-template <typename E, int BM, int BN, int WM, int WN, int NS, bool GROUPED, int MINB = 1, int STAGE = 0>
+// profiles.  BQ8: B holds E4M3 bytes (grouped, bf16 only; see tile_mma) with
+// per-column scales p.scaleB.
+template <typename E, int BM, int BN, int WM, int WN, int NS, bool GROUPED, int MINB = 1, int STAGE = 0,
+          bool BQ8 = false>
 __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmParams p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -304,13 +344,16 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     constexpr int BK = 8 * VEC;                 // elements per k-tile
     constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
     constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
-    constexpr int NIA = BM * 8 / NT, NIB = BN * 8 / NT;  // LDS-DMA instructions per thread
+    constexpr int CHB = BQ8 ? 4 : 8;           // 16-byte chunks per B row and k-tile
+    constexpr int EB = BQ8 ? 1 : (int)sizeof(E); // bytes per B element
+    constexpr int NIA = BM * 8 / NT, NIB = BN * CHB / NT;  // LDS-DMA instructions per thread
     static_assert(TM >= 1 && TN >= 1 && NIA >= 1 && NIB >= 1, "tile shape");
-    static_assert(NIA * NT == BM * 8 && NIB * NT == BN * 8, "tile shape");
+    static_assert(NIA * NT == BM * 8 && NIB * NT == BN * CHB, "tile shape");
     static_assert(NS >= 2 && NS <= 4, "stages");
+    static_assert(!BQ8 || (GROUPED && sizeof(E) == 2), "E4M3 B operands: grouped bf16 GEMMs");
 
     __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[NS > 2 ? BM * 8 : 1], sA3[NS > 3 ? BM * 8 : 1];
-    __shared__ uint4 sB0[BN * 8], sB1[BN * 8], sB2[NS > 2 ? BN * 8 : 1], sB3[NS > 3 ? BN * 8 : 1];
+    __shared__ uint4 sB0[BN * CHB], sB1[BN * CHB], sB2[NS > 2 ? BN * CHB : 1], sB3[NS > 3 ? BN * CHB : 1];
 
     TileInfo ti;
     if (!locate_tile<BM, BN, GROUPED>(p, ti))
@@ -325,8 +368,8 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
 
     // Buffer descriptors and this thread's source offsets (fixed for the K loop).
     const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(p.A, p.a_bytes);
-    const char *Bexp = static_cast<const char *>(p.B) + (int64_t)expert * p.strideB * (int64_t)sizeof(E);
-    const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bexp, (int64_t)p.N * p.ldb * (int64_t)sizeof(E));
+    const char *Bexp = static_cast<const char *>(p.B) + (int64_t)expert * p.strideB * EB;
+    const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bexp, (int64_t)p.N * p.ldb * EB);
     unsigned a_off[NIA], b_off[NIB];
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
@@ -341,8 +384,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     }
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
-        const int P = (i * NW + wave) * 64 + lane, r = P >> 3, c = (P & 7) ^ ((r >> 1) & 7);
-        b_off[i] = (n0 + r < p.N) ? (unsigned)((int64_t)(n0 + r) * p.ldb * (int64_t)sizeof(E)) + c * 16 : kOOB;
+        const int P = (i * NW + wave) * 64 + lane, r = P / CHB;
+        const int c = BQ8 ? (P % CHB) ^ ((r >> 2) & 3) : (P & 7) ^ ((r >> 1) & 7);
+        b_off[i] = (n0 + r < p.N) ? (unsigned)((int64_t)(n0 + r) * p.ldb * EB) + c * 16 : kOOB;
     }
 
     f32x16 acc[TM][TN];
@@ -366,11 +410,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         kt0 = split * per;
         nkl = min(per, nkl - kt0);
     }
-    LMOE_TILE_DMA(sA0, sB0, (unsigned)kt0 * 128u)
+    LMOE_TILE_DMA(sA0, sB0, kt0)
     if (NS > 2 && nkl > 1)
-        LMOE_TILE_DMA(sA1, sB1, (unsigned)(kt0 + 1) * 128u)
+        LMOE_TILE_DMA(sA1, sB1, kt0 + 1)
     if (NS > 3 && nkl > 2)
-        LMOE_TILE_DMA(sA2, sB2, (unsigned)(kt0 + 2) * 128u)
+        LMOE_TILE_DMA(sA2, sB2, kt0 + 2)
 
 // One k-tile step j: wait until tile j is in LDS for every wave (the tiles
 // issued after it may stay in flight) and every wave is done with the stage
@@ -387,9 +431,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         __builtin_amdgcn_s_barrier();                                                                         \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
         if (j + NS - 1 < nkl)                                                                                 \
-            LMOE_TILE_DMA(NA, NB, (unsigned)(kt0 + j + NS - 1) * 128u)                                     \
+            LMOE_TILE_DMA(NA, NB, kt0 + j + NS - 1)                                                       \
         if (wave_live)                                                                                        \
-            tile_mma<E, TM, TN, WTM, WTN>(acc, SA, SB, wm, wn, lane);                                        \
+            tile_mma<E, TM, TN, WTM, WTN, BQ8>(acc, SA, SB, wm, wn, lane);                                   \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
         if (++j >= nkl)                                                                                       \
             break;                                                                                            \
@@ -439,8 +483,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         return;
     }
 
+    const float *cs = (BQ8 && p.scaleB) ? p.scaleB + (int64_t)expert * p.N : nullptr;  // column scales
     if (sizeof(E) != 2 || n0 < p.c_split) {  // fp32 outputs: straight from the registers
-        store_tile_direct<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane);
+        store_tile_direct<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, cs);
         return;
     }
     if constexpr (sizeof(E) == 2) {
@@ -452,7 +497,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
         uint4 *stg = (wave < PER_ARR ? sA0 : sA1) + (wave % PER_ARR) * WAVE_U;
-        store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg);
+        store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg, cs);
     }
 #endif
 }

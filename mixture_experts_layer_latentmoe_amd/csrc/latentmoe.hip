@@ -76,6 +76,8 @@ struct Plan {
     int64_t d, l, m, ms, S, N, K, alpha, Tmax;
     int dtype;      // latentmoe_dtype
     int esize;      // bytes per element
+    bool fp8;       // routed-expert banks W1/W2 as E4M3 bytes + per-column scales
+    int wesize;     // bytes per W1/W2 element
     int64_t ld_zh;  // l + S*ms: row of [z|u , h_s]
     int64_t n_x;    // N' + l + S*ms: output columns of the pass over x
     int64_t nchunks_max;
@@ -98,6 +100,7 @@ struct latentmoe_handle {
     // repacked weights (one allocation)
     void *wbuf = nullptr;
     void *wcat1T = nullptr, *w1T = nullptr, *w2T = nullptr, *wcat2T = nullptr;
+    float *s1 = nullptr, *s2 = nullptr;  // E4M3 column scales [N', m], [N', l]
     float *bias = nullptr;
     // workspace (one allocation)
     void *ws = nullptr;
@@ -139,7 +142,11 @@ int validate(const latentmoe_config *c)
         return LATENTMOE_ERR_INVALID_ARGUMENT;
     if (c->n_shared > 0 && c->m_shared <= 0)
         return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->expert_format != LATENTMOE_EXPERT_AS_DTYPE && c->expert_format != LATENTMOE_EXPERT_FP8_E4M3)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
     // kernel support
+    if (c->expert_format == LATENTMOE_EXPERT_FP8_E4M3 && c->dtype != LATENTMOE_DTYPE_BF16)
+        return LATENTMOE_ERR_UNSUPPORTED;
     if (c->d % 64 || c->l % 64 || c->m % 64 || (c->n_shared > 0 && c->m_shared % 64))
         return LATENTMOE_ERR_UNSUPPORTED;
     if (c->n_experts % 16 || c->n_experts > 1024 || c->top_k > 64)
@@ -174,6 +181,8 @@ Plan make_plan(const latentmoe_config *c)
     p.Tmax = c->max_tokens;
     p.dtype = c->dtype;
     p.esize = c->dtype == LATENTMOE_DTYPE_BF16 ? 2 : 4;
+    p.fp8 = c->expert_format == LATENTMOE_EXPERT_FP8_E4M3;
+    p.wesize = p.fp8 ? 1 : p.esize;
     p.ld_zh = p.l + p.S * p.ms;
     p.n_x = p.N + p.ld_zh;
     p.nchunks_max = (p.Tmax + kRouterTokens - 1) / kRouterTokens;
@@ -226,7 +235,7 @@ Layout ws_layout(const Plan &p)
 }
 
 struct WLayout {
-    int64_t off_c1, off_w1, off_w2, off_c2, off_bias, total;
+    int64_t off_c1, off_w1, off_w2, off_c2, off_bias, off_s1, off_s2, total;
 };
 
 WLayout w_layout(const Plan &p)
@@ -240,10 +249,12 @@ WLayout w_layout(const Plan &p)
     };
     const int64_t es = p.esize;
     L.off_c1 = take(es * p.n_x * p.d);
-    L.off_w1 = take(es * p.N * p.m * p.l);
-    L.off_w2 = take(es * p.N * p.l * p.m);
+    L.off_w1 = take(p.wesize * p.N * p.m * p.l);
+    L.off_w2 = take(p.wesize * p.N * p.l * p.m);
     L.off_c2 = take(es * p.d * p.ld_zh);
     L.off_bias = take(4 * p.N);
+    L.off_s1 = take(p.fp8 ? 4 * p.N * p.m : 0);
+    L.off_s2 = take(p.fp8 ? 4 * p.N * p.l : 0);
     L.total = o;
     return L;
 }
@@ -265,8 +276,8 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
     char *base = static_cast<char *>(h->wbuf);
     const WLayout L = w_layout(p);
     E *c1 = reinterpret_cast<E *>(base + L.off_c1);
-    E *w1 = reinterpret_cast<E *>(base + L.off_w1);
-    E *w2 = reinterpret_cast<E *>(base + L.off_w2);
+    char *w1 = base + L.off_w1;
+    char *w2 = base + L.off_w2;
     E *c2 = reinterpret_cast<E *>(base + L.off_c2);
     // [W_r | W_down | W1_s] [d, N' + l + S m_s] -> K-contiguous rows:
     // W_r^T (N' rows), W_down^T (l rows), then W1_s[j]^T (m_s rows each)
@@ -274,9 +285,19 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
     launch_transpose<E>(w->w_down, p.d, p.l, 1, 0, c1 + p.N * p.d, p.d, 0, s);
     if (p.S > 0)
         launch_transpose<E>(w->w1_shared, p.d, p.ms, p.S, p.d * p.ms, c1 + (p.N + p.l) * p.d, p.d, p.ms * p.d, s);
-    // W1 [N', l, m] -> [N', m, l];  W2 [N', m, l] -> [N', l, m]
-    launch_transpose<E>(w->w1, p.l, p.m, p.N, p.l * p.m, w1, p.l, p.m * p.l, s);
-    launch_transpose<E>(w->w2, p.m, p.l, p.N, p.m * p.l, w2, p.m, p.l * p.m, s);
+    // W1 [N', l, m] -> [N', m, l];  W2 [N', m, l] -> [N', l, m]  (E4M3 banks:
+    // the same transposes of bytes; their scales are copied as they are)
+    if (p.fp8) {
+        launch_transpose<uint8_t>(w->w1, p.l, p.m, p.N, p.l * p.m, w1, p.l, p.m * p.l, s);
+        launch_transpose<uint8_t>(w->w2, p.m, p.l, p.N, p.m * p.l, w2, p.m, p.l * p.m, s);
+        h->s1 = reinterpret_cast<float *>(base + L.off_s1);
+        h->s2 = reinterpret_cast<float *>(base + L.off_s2);
+        hip_check(hipMemcpyAsync(h->s1, w->w1_scale, 4 * p.N * p.m, hipMemcpyDeviceToDevice, s));
+        hip_check(hipMemcpyAsync(h->s2, w->w2_scale, 4 * p.N * p.l, hipMemcpyDeviceToDevice, s));
+    } else {
+        launch_transpose<E>(w->w1, p.l, p.m, p.N, p.l * p.m, w1, p.l, p.m * p.l, s);
+        launch_transpose<E>(w->w2, p.m, p.l, p.N, p.m * p.l, w2, p.m, p.l * p.m, s);
+    }
     // [W_up ; W2_s] -> [d, l + S m_s]: row i holds W_up[:, i] then W2_s[j][:, i]
     launch_transpose<E>(w->w_up, p.l, p.d, 1, 0, c2, p.ld_zh, 0, s);
     if (p.S > 0)
@@ -304,12 +325,12 @@ void launch_dense(const GemmParams &gp, hipStream_t s)
     hip_check(hipGetLastError());
 }
 
-template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG>
+template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG, bool BQ8>
 void launch_grouped(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
 {
     const int64_t ntn = (gp.N + BN - 1) / BN;
     const int64_t grid = align_up(max_mtiles * ntn, 8);
-    gemm_kernel<E, BM, BN, WM, WN, NS, true, 1, TAG><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
+    gemm_kernel<E, BM, BN, WM, WN, NS, true, 1, TAG, BQ8><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
     hip_check(hipGetLastError());
 }
 
@@ -361,13 +382,23 @@ void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_
 
 // Grouped GEMMs: 128x128 tiles; when experts average few rows (decode),
 // 32x128 tiles with four LDS stages so that more weight bytes are in flight.
+// fp8: the weights (B) are E4M3 bytes with column scales in gp.scaleB.
 template <typename E, int TAG>
-void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, hipStream_t s)
+void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hipStream_t s)
 {
+    if constexpr (sizeof(E) == 2) {
+        if (fp8) {
+            if (bm == kGroupBMSmall)
+                launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, true>(gp, max_mtiles, s);
+            else
+                launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG, true>(gp, max_mtiles, s);
+            return;
+        }
+    }
     if (bm == kGroupBMSmall)
-        launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG>(gp, max_mtiles, s);
+        launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, false>(gp, max_mtiles, s);
     else
-        launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG>(gp, max_mtiles, s);
+        launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG, false>(gp, max_mtiles, s);
 }
 
 int group_bm_for(int64_t P, int64_t N) { return (P / N < 32) ? kGroupBMSmall : kGroupBM; }
@@ -513,8 +544,9 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g1.tile_row0 = h->tile_row0;
     g1.n_mtiles = h->n_mtiles;
     g1.offsets = h->offsets;
+    g1.scaleB = h->s1;
     tm.begin(ST_GEMM1);
-    grouped_gemm<E, kTagG1>(g1, max_mt, gbm, s);
+    grouped_gemm<E, kTagG1>(g1, max_mt, gbm, p.fp8, s);
     tm.end(ST_GEMM1);
 
     // 6: Y = H W2_e
@@ -531,8 +563,9 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g2.K = (int)p.m;
     g2.relu2_from = 1 << 30;
     g2.gather = nullptr;
+    g2.scaleB = h->s2;
     tm.begin(ST_GEMM2);
-    grouped_gemm<E, kTagG2>(g2, max_mt, gbm, s);
+    grouped_gemm<E, kTagG2>(g2, max_mt, gbm, p.fp8, s);
     tm.end(ST_GEMM2);
 
     // 7: u = sum_k gate Y[pos], written over z (z is dead after stage 5)
@@ -679,6 +712,8 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
     if (cfg->n_shared > 0 && (!w->w1_shared || !w->w2_shared))
         return LATENTMOE_ERR_INVALID_ARGUMENT;
     if (cfg->has_router_bias && !w->b_router)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (cfg->expert_format == LATENTMOE_EXPERT_FP8_E4M3 && (!w->w1_scale || !w->w2_scale))
         return LATENTMOE_ERR_INVALID_ARGUMENT;
     latentmoe_handle *h = new (std::nothrow) latentmoe_handle();
     if (!h)

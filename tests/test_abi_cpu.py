@@ -33,7 +33,7 @@ def test_library_exports_every_declared_function():
 def _cfg(sh, **over):
     kw = dict(d=sh.d, l=sh.l, m=sh.m, n_experts=sh.n_experts, top_k=sh.top_k, alpha=sh.alpha,
               n_shared=sh.n_shared, m_shared=sh.m_shared, variant=sh.variant, dtype=sh.dtype,
-              max_tokens=sh.T, has_router_bias=sh.has_bias)
+              max_tokens=sh.T, has_router_bias=sh.has_bias, expert_dtype=sh.expert_dtype)
     kw.update(over)
     return _abi.make_config(**kw)
 
@@ -61,6 +61,27 @@ def test_named_configs_validate(name):
 ])
 def test_invalid_configs_are_rejected(over, status):
     assert _abi.latentmoe_validate_config(_cfg(CONFIGS["readme_acc"], **over)) == status
+
+
+def test_expert_format_checks():
+    c = _cfg(CONFIGS["readme_acc"])
+    c.expert_format = 7
+    assert _abi.latentmoe_validate_config(c) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
+    # E4M3 expert banks need a bf16 layer
+    c = _cfg(CONFIGS["tiny_f32"], expert_dtype="fp8")
+    assert _abi.latentmoe_validate_config(c) == _abi.LATENTMOE_ERR_UNSUPPORTED
+    assert _abi.latentmoe_validate_config(_cfg(CONFIGS["decode_eff_fp8"])) == _abi.LATENTMOE_OK
+
+
+def test_fp8_create_needs_scales_before_any_gpu_call():
+    L = _abi.lib()
+    cfg = _cfg(CONFIGS["decode_eff_fp8"])
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the check comes first
+    w = _abi.latentmoe_weights(fake, None, fake, fake, fake, fake, fake, fake, None, None)
+    h = ctypes.c_void_p(0)
+    assert L.latentmoe_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(h)) == \
+        _abi.LATENTMOE_ERR_INVALID_ARGUMENT
+    assert h.value is None
 
 
 def test_eff_variant_allows_any_topk():

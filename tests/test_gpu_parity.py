@@ -208,3 +208,28 @@ def test_profile_stage_mask_times_only_selected_stages():
         assert np.array_equal(y.cpu().numpy(), ref)
     finally:
         layer.close()
+
+
+# --------------------------------------------------------------------------
+# FP8 (E4M3) expert banks with per-column scales
+# --------------------------------------------------------------------------
+def test_fp8_decode_full_size():
+    # 64 tokens: the 32-row grouped tiles with E4M3 weight tiles
+    _full_check(make_workload(get_config("decode_eff_fp8")), 64)
+
+
+@pytest.mark.parametrize("T", [300, 7])
+def test_fp8_readme_widths(T):
+    # 300 tokens x 6 slots: the 128x128 grouped tiles; 7 tokens: a single
+    # partial tile per expert
+    _full_check(make_workload(get_config("decode_eff_fp8"), T=T))
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=96, d=128, l=64, m=192, n_experts=16, top_k=4, n_shared=1, m_shared=64, alpha=2),
+    dict(T=33, d=256, l=128, m=64, n_experts=32, top_k=8, n_shared=0, m_shared=0, alpha=2),
+])
+def test_fp8_shape_edge_cases(cfg):
+    from tests.helpers import random_fp8_workload
+    sh = shape(dtype="bf16", expert_dtype="fp8", **cfg)
+    _full_check(random_fp8_workload(sh, seed=cfg["T"]))
