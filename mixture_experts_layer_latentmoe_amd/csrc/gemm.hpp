@@ -42,6 +42,10 @@ struct GemmParams {
     int64_t a_bytes;    // size of the A buffer in bytes (range of the loads)
     const void *B;      // B^T rows: [N][ldb]
     int64_t ldb;        // elements
+    int64_t b_kstep;    // bytes from one k-tile of a B row to the next; 0: rows are
+                        // K-contiguous (one k-tile = 128 bytes, 64 for E4M3).  The
+                        // k-tiled layout [K / BK][N][BK] has ldb = BK and
+                        // b_kstep = N * BK * bytes per element
     int64_t strideB;    // elements between experts (grouped)
     void *C;            // columns [c_split, N) go to C[row][col - c_split]
     int64_t ldc;        // elements
@@ -63,6 +67,8 @@ struct GemmParams {
     const int *n_mtiles;     // device scalar: number of valid M tiles
     const int *offsets;      // [N'+1] first dispatch row of each expert
     const float *scaleB;     // grouped, E4M3 B: [N'][N] scale of each expert's output column
+    // dense, few rows: B again in fragment-major 1 KiB blocks (fragmajor_kernel)
+    const void *Bfrag;
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -203,15 +209,39 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
     }
 }
 
+// Epilogue of four consecutive output columns col .. col + 3 of one row.
+// Columns below c_split go to C32 in fp32 (+ bias32), the rest to C, with
+// relu^2 from relu2_from on.  c_split is a multiple of 4, so a group never
+// straddles it.
+template <typename E>
+__device__ __forceinline__ void store_out4(const GemmParams &p, int64_t row, int col, float (&v)[4])
+{
+    if (col < p.c_split) {
+        if (p.bias32) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v[r] += p.bias32[col + r];
+        }
+        store4(p.C32 + row * p.ldc32 + col, v[0], v[1], v[2], v[3]);
+        return;
+    }
+    const int mc = col - p.c_split;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (mc + r >= p.relu2_from) {
+            const float t = fmaxf(v[r], 0.f);
+            v[r] = t * t;
+        }
+    store4(static_cast<E *>(p.C) + row * p.ldc + mc, v[0], v[1], v[2], v[3]);
+}
+
 // Epilogue straight from the accumulators: each lane stores runs of four
-// output columns.  Columns below c_split go to C32 in fp32 (+ bias32), the
-// rest to C, with relu^2 from relu2_from on.
+// output columns (times the column scales cs, if any).
 template <typename E, int TM, int TN, int WTM, int WTN>
 __device__ __forceinline__ void store_tile_direct(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t row_base,
                                                   int rows_valid, int n0, int wm, int wn, int lane,
                                                   const float *cs = nullptr)
 {
-    E *C = static_cast<E *>(p.C);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         const int rl = wm * WTM + i * 32 + (lane & 31);
@@ -231,23 +261,7 @@ __device__ __forceinline__ void store_tile_direct(const GemmParams &p, const f32
                     for (int r = 0; r < 4; ++r)
                         v[r] *= cs[col + r];
                 }
-                if (col < p.c_split) {
-                    if (p.bias32) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            v[r] += p.bias32[col + r];
-                    }
-                    store4(p.C32 + row * p.ldc32 + col, v[0], v[1], v[2], v[3]);
-                    continue;
-                }
-                const int mc = col - p.c_split;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (mc + r >= p.relu2_from) {
-                        const float t = fmaxf(v[r], 0.f);
-                        v[r] = t * t;
-                    }
-                store4(C + row * p.ldc + mc, v[0], v[1], v[2], v[3]);
+                store_out4<E>(p, row, col, v);
             }
         }
     }
@@ -315,19 +329,44 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
     }
 }
 
-// k-tile KT of A and B straight into LDS (buffer loads with the LDS bit: lane
-// l of a wave writes 16 bytes at the wave's base + 16 l; rows out of range
-// read as zeros).  Position P of an A tile holds row r = P / 8, chunk
-// (P % 8) ^ ((r / 2) % 8); of a B tile row P / CHB, chunk (P % CHB) ^ the
-// B swizzle; instruction i of wave w fills positions (i * NW + w) * 64 .. +63.
-#define LMOE_TILE_DMA(SA, SB, KT)                                                                         \
-    {                                                                                                      \
-        const unsigned kt_ = (unsigned)(KT);                                                               \
-        _Pragma("unroll") for (int i_ = 0; i_ < NIA; ++i_) __builtin_amdgcn_raw_ptr_buffer_load_lds(       \
-            ra_rsrc, LMOE_LDS((SA) + (i_ * NW + wave) * 64), 16, a_off[i_] + kt_ * 128u, 0, 0, 0);          \
-        _Pragma("unroll") for (int i_ = 0; i_ < NIB; ++i_) __builtin_amdgcn_raw_ptr_buffer_load_lds(       \
-            rb_rsrc, LMOE_LDS((SB) + (i_ * NW + wave) * 64), 16, b_off[i_] + kt_ * (CHB * 16u), 0, 0, 0);   \
-    }
+// k-tile kt of A and B straight into the LDS stages na, nb (buffer loads with
+// the LDS bit: lane l of a wave writes 16 bytes at the wave's base + 16 l;
+// rows out of range read as zeros).  Position P of an A tile holds row
+// r = P / 8, chunk (P % 8) ^ ((r / 2) % 8); of a B tile row P / CHB, chunk
+// (P % CHB) ^ the B swizzle; instruction i of wave w fills positions
+// (i * NW + w) * 64 .. +63.  With issue false every load is out of range and
+// reads nothing: the instructions still go out, so that the number of loads
+// in flight after a tile does not depend on the data.
+template <int NIA, int NIB, int NW>
+__device__ __forceinline__ void tile_dma(uint4 *na, uint4 *nb, bool issue, unsigned kt, __amdgpu_buffer_rsrc_t ra,
+                                         __amdgpu_buffer_rsrc_t rb, const unsigned (&a_off)[NIA],
+                                         const unsigned (&b_off)[NIB], unsigned bks, int wave)
+{
+#pragma unroll
+    for (int i = 0; i < NIA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LMOE_LDS(na + (i * NW + wave) * 64), 16,
+                                                 issue ? a_off[i] + kt * 128u : kOOB, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < NIB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LMOE_LDS(nb + (i * NW + wave) * 64), 16,
+                                                 issue ? b_off[i] + kt * bks : kOOB, 0, 0, 0);
+}
+
+// One k-step: the refill of stages na, nb with tile kt, then (if live) the
+// tile held in sa, sb into the accumulators.  The four stages are different
+// LDS arrays; the restrict qualifiers tell the compiler so, which keeps it
+// from making the reads of sa, sb wait for the DMA into na, nb.
+template <typename E, int TM, int TN, int WTM, int WTN, bool BQ8, int NIA, int NIB, int NW>
+__device__ __forceinline__ void dma_mma(uint4 *__restrict__ na, uint4 *__restrict__ nb, const uint4 *__restrict__ sa,
+                                        const uint4 *__restrict__ sb, bool issue, unsigned kt,
+                                        __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                        const unsigned (&a_off)[NIA], const unsigned (&b_off)[NIB], unsigned bks,
+                                        int wave, bool live, f32x16 (&acc)[TM][TN], int wm, int wn, int lane)
+{
+    tile_dma<NIA, NIB, NW>(na, nb, issue, kt, ra, rb, a_off, b_off, bks, wave);
+    if (live)
+        tile_mma<E, TM, TN, WTM, WTN, BQ8>(acc, sa, sb, wm, wn, lane);
+}
 
 // NT = 64 * WM * WN threads; NS LDS stages (2 or 3), one barrier per k-tile;
 // tiles kt+1 .. kt+NS-1 are in flight while tile kt is multiplied.  STAGE only
@@ -369,7 +408,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     // Buffer descriptors and this thread's source offsets (fixed for the K loop).
     const __amdgpu_buffer_rsrc_t ra_rsrc = make_rsrc(p.A, p.a_bytes);
     const char *Bexp = static_cast<const char *>(p.B) + (int64_t)expert * p.strideB * EB;
-    const __amdgpu_buffer_rsrc_t rb_rsrc = make_rsrc(Bexp, (int64_t)p.N * p.ldb * EB);
+    const unsigned bks = p.b_kstep ? (unsigned)p.b_kstep : CHB * 16u;  // bytes per k-tile step of B
+    const __amdgpu_buffer_rsrc_t rb_rsrc =
+        make_rsrc(Bexp, p.b_kstep ? (int64_t)(p.K / BK) * p.b_kstep : (int64_t)p.N * p.ldb * EB);
     unsigned a_off[NIA], b_off[NIB];
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
@@ -410,30 +451,24 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         kt0 = split * per;
         nkl = min(per, nkl - kt0);
     }
-    LMOE_TILE_DMA(sA0, sB0, kt0)
-    if (NS > 2 && nkl > 1)
-        LMOE_TILE_DMA(sA1, sB1, kt0 + 1)
-    if (NS > 3 && nkl > 2)
-        LMOE_TILE_DMA(sA2, sB2, kt0 + 2)
+    tile_dma<NIA, NIB, NW>(sA0, sB0, true, kt0, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
+    if constexpr (NS > 2)
+        tile_dma<NIA, NIB, NW>(sA1, sB1, nkl > 1, kt0 + 1, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
+    if constexpr (NS > 3)
+        tile_dma<NIA, NIB, NW>(sA2, sB2, nkl > 2, kt0 + 2, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
 
-// One k-tile step j: wait until tile j is in LDS for every wave (the tiles
-// issued after it may stay in flight) and every wave is done with the stage
-// about to be refilled; refill it with tile j + NS - 1; multiply tile j.
+// One k-tile step j: wait until tile j is in LDS for every wave (the NS - 2
+// tiles issued after it, real or out of range, may stay in flight) and every
+// wave is done with the stage about to be refilled; refill it with tile
+// j + NS - 1; multiply tile j.
 #define LMOE_KSTEP(SA, SB, NA, NB)                                                                            \
     {                                                                                                         \
-        const int ahead = min(NS - 2, nkl - 1 - j);                                                           \
-        if (NS > 3 && ahead >= 2)                                                                             \
-            wait_vm_lgkm0<2 * NI>();                                                                          \
-        else if (NS > 2 && ahead >= 1)                                                                        \
-            wait_vm_lgkm0<NI>();                                                                              \
-        else                                                                                                  \
-            wait_vm_lgkm0<0>();                                                                               \
+        wait_vm_lgkm0<(NS - 2) * NI>();                                                                       \
         __builtin_amdgcn_s_barrier();                                                                         \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
-        if (j + NS - 1 < nkl)                                                                                 \
-            LMOE_TILE_DMA(NA, NB, kt0 + j + NS - 1)                                                       \
-        if (wave_live)                                                                                        \
-            tile_mma<E, TM, TN, WTM, WTN, BQ8>(acc, SA, SB, wm, wn, lane);                                   \
+        dma_mma<E, TM, TN, WTM, WTN, BQ8, NIA, NIB, NW>(NA, NB, SA, SB, j + NS - 1 < nkl,                    \
+                                                        (unsigned)(kt0 + j + NS - 1), ra_rsrc, rb_rsrc, a_off, \
+                                                        b_off, bks, wave, wave_live, acc, wm, wn, lane);      \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
         if (++j >= nkl)                                                                                       \
             break;                                                                                            \
@@ -490,13 +525,15 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     }
     if constexpr (sizeof(E) == 2) {
         // every wave is done with the k-tiles (no load is in flight after the
-        // last k-step): the A stage arrays hold the waves' epilogue areas
+        // last k-step): the first two A (else B) stage arrays hold the waves'
+        // epilogue areas
         constexpr int WAVE_U = 32 * WTN * 2 / 16;  // 16-byte units per wave area
-        constexpr int PER_ARR = (BM * 8) / WAVE_U;  // areas per A stage array
-        static_assert(PER_ARR >= 1 && NW <= 2 * PER_ARR, "epilogue areas fit in sA0 and sA1");
+        constexpr bool IN_A = NW <= 2 * ((BM * 8) / WAVE_U);
+        constexpr int PER_ARR = (IN_A ? BM * 8 : BN * CHB) / WAVE_U;  // areas per stage array
+        static_assert(PER_ARR >= 1 && NW <= 2 * PER_ARR, "epilogue areas fit in two stage arrays");
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
-        uint4 *stg = (wave < PER_ARR ? sA0 : sA1) + (wave % PER_ARR) * WAVE_U;
+        uint4 *stg = (IN_A ? (wave < PER_ARR ? sA0 : sA1) : (wave < PER_ARR ? sB0 : sB1)) + (wave % PER_ARR) * WAVE_U;
         store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg, cs);
     }
 #endif
@@ -521,23 +558,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p)
         v[2] += x.z;
         v[3] += x.w;
     }
-    if (col < p.c_split) {
-        if (p.bias32)
-            for (int r = 0; r < 4; ++r)
-                v[r] += p.bias32[col + r];
-        store4(p.C32 + row * p.ldc32 + col, v[0], v[1], v[2], v[3]);
-        return;
-    }
-    const int mc = col - p.c_split;
-    for (int r = 0; r < 4; ++r)
-        if (mc + r >= p.relu2_from) {
-            const float t = fmaxf(v[r], 0.f);
-            v[r] = t * t;
-        }
-    store4(static_cast<E *>(p.C) + row * p.ldc + mc, v[0], v[1], v[2], v[3]);
+    store_out4<E>(p, row, col, v);
 }
 
-#undef LMOE_TILE_DMA
 
 template <int BM, int BN, int NS>
 constexpr size_t gemm_lds_bytes()

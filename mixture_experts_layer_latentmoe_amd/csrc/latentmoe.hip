@@ -37,6 +37,7 @@
 #include "gemm.hpp"
 #include "repack.hpp"
 #include "router.hpp"
+#include "skinny.hpp"
 
 using namespace lmoe;
 
@@ -78,6 +79,7 @@ struct Plan {
     int esize;      // bytes per element
     bool fp8;       // routed-expert banks W1/W2 as E4M3 bytes + per-column scales
     int wesize;     // bytes per W1/W2 element
+    int bk_b;       // elements per k-tile of the W1/W2 B tiles (128 bytes, 64 for E4M3)
     int64_t ld_zh;  // l + S*ms: row of [z|u , h_s]
     int64_t n_x;    // N' + l + S*ms: output columns of the pass over x
     int64_t nchunks_max;
@@ -100,6 +102,7 @@ struct latentmoe_handle {
     // repacked weights (one allocation)
     void *wbuf = nullptr;
     void *wcat1T = nullptr, *w1T = nullptr, *w2T = nullptr, *wcat2T = nullptr;
+    void *frag1 = nullptr, *frag2 = nullptr;  // fragment-major copies of wcat1T, wcat2T
     float *s1 = nullptr, *s2 = nullptr;  // E4M3 column scales [N', m], [N', l]
     float *bias = nullptr;
     // workspace (one allocation)
@@ -162,7 +165,9 @@ int validate(const latentmoe_config *c)
     const int64_t ld_zh = c->l + c->n_shared * ms;
     const int64_t lim = (int64_t(1) << 31) - 1;
     if (c->max_tokens * c->d * es > lim || c->max_tokens * ld_zh * es > lim || P * c->m * es > lim ||
-        (c->n_experts + ld_zh) * c->d * es > lim || c->d * ld_zh * es > lim || c->max_tokens * c->n_experts * 4 > lim)
+        (c->n_experts + ld_zh) * c->d * es > lim || c->d * ld_zh * es > lim || c->max_tokens * c->n_experts * 4 > lim ||
+        c->l * c->m * es > lim ||  // one expert's W1 or W2
+        (c->n_experts + ld_zh + 31) * c->d * es > lim)  // fragment-major copy (rows padded to 32)
         return LATENTMOE_ERR_UNSUPPORTED;
     return LATENTMOE_OK;
 }
@@ -183,6 +188,7 @@ Plan make_plan(const latentmoe_config *c)
     p.esize = c->dtype == LATENTMOE_DTYPE_BF16 ? 2 : 4;
     p.fp8 = c->expert_format == LATENTMOE_EXPERT_FP8_E4M3;
     p.wesize = p.fp8 ? 1 : p.esize;
+    p.bk_b = p.fp8 ? 64 : 128 / p.esize;
     p.ld_zh = p.l + p.S * p.ms;
     p.n_x = p.N + p.ld_zh;
     p.nchunks_max = (p.Tmax + kRouterTokens - 1) / kRouterTokens;
@@ -235,7 +241,7 @@ Layout ws_layout(const Plan &p)
 }
 
 struct WLayout {
-    int64_t off_c1, off_w1, off_w2, off_c2, off_bias, off_s1, off_s2, total;
+    int64_t off_c1, off_w1, off_w2, off_c2, off_bias, off_s1, off_s2, off_f1, off_f2, total;
 };
 
 WLayout w_layout(const Plan &p)
@@ -255,6 +261,8 @@ WLayout w_layout(const Plan &p)
     L.off_bias = take(4 * p.N);
     L.off_s1 = take(p.fp8 ? 4 * p.N * p.m : 0);
     L.off_s2 = take(p.fp8 ? 4 * p.N * p.l : 0);
+    L.off_f1 = take(es * align_up(p.n_x, 32) * p.d);
+    L.off_f2 = take(es * align_up(p.d, 32) * p.ld_zh);
     L.total = o;
     return L;
 }
@@ -263,9 +271,22 @@ template <typename E>
 void launch_transpose(const void *src, int64_t R, int64_t C, int64_t batch, int64_t src_bstride, void *dst,
                       int64_t dst_ld, int64_t dst_bstride, hipStream_t s)
 {
-    dim3 grid((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32), (unsigned)batch);
-    transpose_kernel<E><<<grid, dim3(256), 0, s>>>(static_cast<const E *>(src), R, C, src_bstride,
-                                                   static_cast<E *>(dst), dst_ld, dst_bstride);
+    constexpr int64_t kMaxZ = 32768;  // grid z stays below the 65535 limit
+    for (int64_t b0 = 0; b0 < batch; b0 += kMaxZ) {
+        dim3 grid((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32), (unsigned)std::min(kMaxZ, batch - b0));
+        transpose_kernel<E><<<grid, dim3(256), 0, s>>>(static_cast<const E *>(src) + b0 * src_bstride, R, C,
+                                                       src_bstride, static_cast<E *>(dst) + b0 * dst_bstride,
+                                                       dst_ld, dst_bstride);
+        hip_check(hipGetLastError());
+    }
+}
+
+void launch_fragmajor(const void *src, int64_t N, int64_t row_bytes, void *dst, hipStream_t s)
+{
+    const int64_t units = ((N + 31) / 32) * 32 * (row_bytes / 32) * 2;
+    const int64_t blocks = std::min<int64_t>((units + 255) / 256, 65536);
+    fragmajor_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(static_cast<const char *>(src), N, row_bytes,
+                                                                  static_cast<char *>(dst));
     hip_check(hipGetLastError());
 }
 
@@ -285,23 +306,30 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
     launch_transpose<E>(w->w_down, p.d, p.l, 1, 0, c1 + p.N * p.d, p.d, 0, s);
     if (p.S > 0)
         launch_transpose<E>(w->w1_shared, p.d, p.ms, p.S, p.d * p.ms, c1 + (p.N + p.l) * p.d, p.d, p.ms * p.d, s);
-    // W1 [N', l, m] -> [N', m, l];  W2 [N', m, l] -> [N', l, m]  (E4M3 banks:
-    // the same transposes of bytes; their scales are copied as they are)
+    // W1 [N', l, m] -> [N', l / bk, m, bk];  W2 [N', m, l] -> [N', m / bk, l, bk]:
+    // per expert, k-tile t of output column n sits at (t * cols + n) * bk, so
+    // that the B tile of one k-step is one contiguous run (E4M3 banks: the
+    // same moves of bytes; their scales are copied as they are)
+    const int64_t bk = p.bk_b;
     if (p.fp8) {
-        launch_transpose<uint8_t>(w->w1, p.l, p.m, p.N, p.l * p.m, w1, p.l, p.m * p.l, s);
-        launch_transpose<uint8_t>(w->w2, p.m, p.l, p.N, p.m * p.l, w2, p.m, p.l * p.m, s);
+        launch_transpose<uint8_t>(w->w1, bk, p.m, p.N * (p.l / bk), bk * p.m, w1, bk, bk * p.m, s);
+        launch_transpose<uint8_t>(w->w2, bk, p.l, p.N * (p.m / bk), bk * p.l, w2, bk, bk * p.l, s);
         h->s1 = reinterpret_cast<float *>(base + L.off_s1);
         h->s2 = reinterpret_cast<float *>(base + L.off_s2);
         hip_check(hipMemcpyAsync(h->s1, w->w1_scale, 4 * p.N * p.m, hipMemcpyDeviceToDevice, s));
         hip_check(hipMemcpyAsync(h->s2, w->w2_scale, 4 * p.N * p.l, hipMemcpyDeviceToDevice, s));
     } else {
-        launch_transpose<E>(w->w1, p.l, p.m, p.N, p.l * p.m, w1, p.l, p.m * p.l, s);
-        launch_transpose<E>(w->w2, p.m, p.l, p.N, p.m * p.l, w2, p.m, p.l * p.m, s);
+        launch_transpose<E>(w->w1, bk, p.m, p.N * (p.l / bk), bk * p.m, w1, bk, bk * p.m, s);
+        launch_transpose<E>(w->w2, bk, p.l, p.N * (p.m / bk), bk * p.l, w2, bk, bk * p.l, s);
     }
     // [W_up ; W2_s] -> [d, l + S m_s]: row i holds W_up[:, i] then W2_s[j][:, i]
     launch_transpose<E>(w->w_up, p.l, p.d, 1, 0, c2, p.ld_zh, 0, s);
     if (p.S > 0)
         launch_transpose<E>(w->w2_shared, p.ms, p.d, p.S, p.ms * p.d, c2 + p.l, p.ld_zh, p.ms, s);
+    h->frag1 = base + L.off_f1;
+    h->frag2 = base + L.off_f2;
+    launch_fragmajor(c1, p.n_x, (int64_t)sizeof(E) * p.d, h->frag1, s);
+    launch_fragmajor(c2, p.d, (int64_t)sizeof(E) * p.ld_zh, h->frag2, s);
     h->wcat1T = c1;
     h->w1T = w1;
     h->w2T = w2;
@@ -337,15 +365,32 @@ void launch_grouped(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
 template <typename E, int TAG>
 void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_t s);
 
+template <typename E, int MT, int NW, int COLS, int TAG>
+void launch_skinny(const GemmParams &gp, hipStream_t s)
+{
+    const int64_t grid = (gp.N + COLS - 1) / COLS;
+    skinny_gemm_kernel<E, MT, NW, COLS, TAG><<<dim3((unsigned)grid), dim3(64 * NW), 0, s>>>(gp);
+    hip_check(hipGetLastError());
+}
+
 // Dense GEMMs: 256x256 tiles (8 waves) when they come close to filling the
-// 256 CUs once, 128x128 (4 waves, two workgroups per CU) when those do; for
-// few rows (decode) 64x128 tiles with K split so that ~512 workgroups stream
-// the weights, followed by a fixed-order reduce that applies the epilogue.
+// 256 CUs once, 128x128 (4 waves, two workgroups per CU) when those do; up to
+// 64 rows (decode) the few-row kernel (K split over the waves of a
+// workgroup); otherwise up to kSplitKMaxRows rows 64x128 tiles with K split
+// so that ~512 workgroups stream the weights, followed by a fixed-order
+// reduce that applies the epilogue.
 template <typename E, int TAG>
 void dense_gemm(const GemmParams &gp, float *partial, int64_t cap_floats, hipStream_t s)
 {
     const int64_t big = ((gp.M + 255) / 256) * ((gp.N + 255) / 256);
     const int64_t mid = ((gp.M + 127) / 128) * ((gp.N + 127) / 128);
+    if (gp.M <= 64 && mid < 256) {
+        if (gp.M <= 32)
+            launch_skinny<E, 1, 8, 16, TAG>(gp, s);
+        else
+            launch_skinny<E, 2, 8, 16, TAG>(gp, s);
+        return;
+    }
     if (big >= 192)
         launch_dense<E, 256, 256, 4, 2, 2, TAG>(gp, s);
     else if (mid >= 256 || gp.M > kSplitKMaxRows)
@@ -382,14 +427,16 @@ void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_
 
 // Grouped GEMMs: 128x128 tiles; when experts average few rows (decode),
 // 32x128 tiles with four LDS stages so that more weight bytes are in flight.
-// fp8: the weights (B) are E4M3 bytes with column scales in gp.scaleB.
+// fp8: the weights (B) are E4M3 bytes with column scales in gp.scaleB; for few
+// rows, 32x64 tiles of two waves and two stages (small LDS footprint, many
+// workgroups per CU) stream the half-size weights fastest.
 template <typename E, int TAG>
 void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hipStream_t s)
 {
     if constexpr (sizeof(E) == 2) {
         if (fp8) {
             if (bm == kGroupBMSmall)
-                launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, true>(gp, max_mtiles, s);
+                launch_grouped<E, kGroupBMSmall, 64, 1, 2, 2, TAG, true>(gp, max_mtiles, s);
             else
                 launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG, true>(gp, max_mtiles, s);
             return;
@@ -475,6 +522,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g.lda = p.d;
     g.a_bytes = (int64_t)T * p.d * es;
     g.B = h->wcat1T;
+    g.Bfrag = h->frag1;
     g.ldb = p.d;
     g.C32 = h->logits;
     g.ldc32 = p.N;
@@ -532,7 +580,8 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g1.lda = p.ld_zh;
     g1.a_bytes = (int64_t)T * p.ld_zh * es;
     g1.B = h->w1T;
-    g1.ldb = p.l;
+    g1.ldb = p.bk_b;
+    g1.b_kstep = p.m * p.bk_b * p.wesize;
     g1.strideB = p.m * p.l;
     g1.C = h->H;
     g1.ldc = p.m;
@@ -555,7 +604,8 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g2.lda = p.m;
     g2.a_bytes = P * p.m * es;
     g2.B = h->w2T;
-    g2.ldb = p.m;
+    g2.ldb = p.bk_b;
+    g2.b_kstep = p.l * p.bk_b * p.wesize;
     g2.strideB = p.l * p.m;
     g2.C = h->Yp;
     g2.ldc = p.l;
@@ -581,6 +631,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g3.lda = p.ld_zh;
     g3.a_bytes = (int64_t)T * p.ld_zh * es;
     g3.B = h->wcat2T;
+    g3.Bfrag = h->frag2;
     g3.ldb = p.ld_zh;
     g3.C = y;
     g3.ldc = p.d;

@@ -32,4 +32,23 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ sr
     }
 }
 
+// Fragment-major copy of K-contiguous rows for the few-row GEMM kernel: the
+// 32 bytes of k-step j of rows 32 b .. 32 b + 31 form one 1 KiB block,
+//   dst[((n / 32) * S + j) * 1024 + (n % 32) * 32 + t] = src[n * row_bytes + 32 j + t],
+// S = row_bytes / 32 steps per row; rows n >= N of the last block are zeros.
+// One thread per 16-byte unit, in source order.
+__global__ __launch_bounds__(256) void fragmajor_kernel(const char *__restrict__ src, int64_t N, int64_t row_bytes,
+                                                        char *__restrict__ dst)
+{
+    const int64_t S = row_bytes / 32;
+    const int64_t units = ((N + 31) / 32) * 32 * S * 2;
+    for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+        const int64_t n = u / (S * 2), rem = u - n * S * 2, j = rem >> 1, t = (rem & 1) * 16;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (n < N)
+            v = *reinterpret_cast<const uint4 *>(src + n * row_bytes + 32 * j + t);
+        *reinterpret_cast<uint4 *>(dst + ((n / 32) * S + j) * 1024 + (n % 32) * 32 + t) = v;
+    }
+}
+
 }  // namespace lmoe

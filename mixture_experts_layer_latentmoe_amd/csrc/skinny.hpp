@@ -1,0 +1,151 @@
+// Dense GEMMs with few rows (decode batches): C = epilogue(A B) for
+// M <= 32 * MT rows.  Such a product is bound by streaming B (the weights)
+// from HBM once; the split of K over workgroups that the tiled kernel needs
+// to occupy the chip writes partial sums as large as the weights and needs a
+// second pass.  Here one workgroup owns COLS output columns and all of K:
+// its NW waves each take a contiguous range of k-tiles, and the NW partial
+// tiles are summed in LDS in wave order, which keeps the result independent
+// of timing.  The epilogue is the tiled kernel's (store_out4).
+//
+// Operands of a wave, per k-tile (128 bytes of K: four k-steps of 32 bytes):
+//  - A (activations, every row of M): copied by LDS DMA into the wave's own
+//    two-stage LDS area, in the tiled kernel's swizzled layout (full 128-byte
+//    lines per load), then read as MFMA fragments.  No other wave touches the
+//    area, so a wave only waits for its own loads (no barrier in the loop).
+//  - B (weights): straight into registers from the fragment-major copy
+//    (fragmajor_kernel), where the 32 rows x 32 bytes of one k-step are one
+//    1 KiB run; every B byte is used once, so LDS would buy nothing.
+// A fragment is 16 bytes of row l % 32 at byte 16 (l / 32) of the k-step, the
+// operand layout of the 32x32 MFMA (Mfma32).  B is passed as the MFMA's first
+// operand, so lane l accumulates output row l % 32 and output columns
+// 8 g + 4 (l / 32) + {0..3} of register group g.  COLS = 16 leaves B rows
+// 16..31 out of range (zeros): half the bytes per workgroup, twice the
+// workgroups.  STAGE only names the layer stage (one symbol per stage).
+#pragma once
+
+#include "gemm.hpp"
+
+namespace lmoe {
+
+// One pipeline step of a wave: k-tile tn of A by LDS DMA into the stage wr
+// (lane l of DMA instruction i writes unit 64 i + l) and its four B
+// fragments into bn (no valid tile: every load is out of range and reads
+// nothing; the loads stay unconditional, so that the compiler's count of
+// loads in flight stays exact); then, if MULT, the k-tile held in the stage
+// rd times the fragments bc.  wr and rd are different LDS arrays.
+template <typename E, int MT, int NIA, bool MULT>
+__device__ __forceinline__ void skinny_step(uint4 *__restrict__ wr, const uint4 *__restrict__ rd, bool valid, int tn,
+                                            __amdgpu_buffer_rsrc_t ra, const unsigned (&a_off)[NIA],
+                                            __amdgpu_buffer_rsrc_t rb, unsigned b_off, uint4 (&bn)[4],
+                                            const uint4 (&bc)[4], f32x16 (&acc)[MT], int r, int h)
+{
+#pragma unroll
+    for (int i = 0; i < NIA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LMOE_LDS(wr + i * 64), 16,
+                                                 valid ? a_off[i] + (unsigned)tn * 128u : kOOB, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        bn[u] = buf_load16(rb, valid ? b_off + (unsigned)(4 * tn + u) * 1024u : kOOB);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the multiplies wait
+    if constexpr (MULT) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = 2 * u + h;
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int rr = i * 32 + r;
+                acc[i] = Mfma32<E>::run(bc[u], rd[rr * 8 + (c ^ ((rr >> 1) & 7))], acc[i]);
+            }
+        }
+    }
+}
+
+template <typename E, int MT, int NW, int COLS, int STAGE = 0>
+__global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(const GemmParams p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    static_assert(MT >= 1 && NW >= 1 && (COLS == 16 || COLS == 32), "skinny shape");
+    constexpr int AU = MT * 32 * 8;  // 16-byte units of one A k-tile (MT * 32 rows x 128 bytes)
+    constexpr int NIA = AU / 64;     // LDS-DMA instructions per A k-tile
+    constexpr int ES = (int)sizeof(E);
+    // two stages in two arrays, so that the compiler sees that reads of one
+    // stage do not depend on the DMA in flight into the other
+    __shared__ uint4 sA0[NW * AU], sA1[NW * AU];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n0 = blockIdx.x * COLS;
+
+    // this wave's k-tiles [t0, t1)
+    const int nkt = p.K * ES / 128, nsteps = nkt * 4;
+    const int per = (nkt + NW - 1) / NW;
+    const int t0 = min(nkt, wave * per), t1 = min(nkt, t0 + per);
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.A, p.a_bytes);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.Bfrag, (int64_t)((p.N + 31) / 32) * nsteps * 1024);
+    unsigned a_off[NIA];
+#pragma unroll
+    for (int i = 0; i < NIA; ++i) {
+        const int P = i * 64 + lane, r = P >> 3, c = (P & 7) ^ ((r >> 1) & 7);
+        a_off[i] = r < p.M ? (unsigned)((int64_t)r * p.lda * ES) + c * 16 : kOOB;
+    }
+    const int r = lane & 31, h = lane >> 5, nb = n0 + r;
+    const unsigned b_off =
+        (r < COLS && nb < p.N) ? (unsigned)(((int64_t)(nb >> 5) * nsteps) * 1024 + (nb & 31) * 32) + 16u * h : kOOB;
+
+    f32x16 acc[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            acc[i][q] = 0.f;
+
+    // two k-tiles in flight: while one stage is multiplied the other loads.
+    // The compiler orders each stage's LDS reads after the DMA that filled it
+    // (skinny_step's restrict-qualified stages tell it that the DMA in flight
+    // into the other stage does not matter); the explicit LDS wait before a
+    // step keeps a refill from overtaking the reads of the step before.
+    uint4 b0[4], b1[4];
+    uint4 *const w0 = sA0 + wave * AU, *const w1 = sA1 + wave * AU;
+    skinny_step<E, MT, NIA, false>(w0, w1, t0 < t1, t0, ra, a_off, rb, b_off, b0, b1, acc, r, h);
+    int t = t0;
+    for (; t + 1 < t1; t += 2) {
+        wait_vm_lgkm0<63>();
+        skinny_step<E, MT, NIA, true>(w1, w0, true, t + 1, ra, a_off, rb, b_off, b1, b0, acc, r, h);
+        wait_vm_lgkm0<63>();
+        skinny_step<E, MT, NIA, true>(w0, w1, t + 2 < t1, t + 2, ra, a_off, rb, b_off, b0, b1, acc, r, h);
+    }
+    if (t < t1) {
+        wait_vm_lgkm0<63>();
+        skinny_step<E, MT, NIA, true>(w1, w0, false, 0, ra, a_off, rb, b_off, b1, b0, acc, r, h);
+    }
+
+    // partial tiles, lane-contiguous, each wave over its own stage-0 area
+    // (which only it has used), then fixed-order sums over the waves
+    static_assert(sizeof(sA0) >= (size_t)NW * MT * 16 * 64 * 4, "reduction area");
+    float *red = reinterpret_cast<float *>(sA0);  // [NW][MT][16][64]
+    wait_vm_lgkm0<0>();
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            red[((wave * MT + i) * 16 + q) * 64 + lane] = acc[i][q];
+    __syncthreads();
+
+    // output groups of four columns: (m-tile i, register group g, lane ln)
+    for (int t = tid; t < MT * 4 * 64; t += 64 * NW) {
+        const int i = t >> 8, g = (t >> 6) & 3, ln = t & 63;
+        const int row = i * 32 + (ln & 31), col = n0 + 8 * g + 4 * (ln >> 5);
+        if (row >= p.M || col >= p.N || col - n0 >= COLS)
+            continue;
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                v[c] += red[((w * MT + i) * 16 + 4 * g + c) * 64 + ln];
+        store_out4<E>(p, row, col, v);
+    }
+#endif
+}
+
+}  // namespace lmoe
