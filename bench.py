@@ -116,6 +116,14 @@ def cpu_baseline(wl, target_s=12.0):
             "sample": f"{n2} of {T} tokens (seeded), full layer per token in fp64, {dt:.1f} s wall"}
 
 
+def weight_bytes(sh) -> int:
+    """Bytes of one repacked copy of the layer's weights."""
+    es = 4 if sh.dtype == "f32" else 2
+    eb = 1 if sh.expert_dtype == "fp8" else es
+    dense = sh.d * (sh.n_experts + sh.l) + sh.l * sh.d + 2 * sh.n_shared * sh.d * sh.m_shared
+    return 2 * dense * es + 2 * sh.n_experts * sh.l * sh.m * eb  # the dense part twice: tiled + fragment-major
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +132,10 @@ def main():
     ap.add_argument("--config", default="readme_acc")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--weight-copies", type=int, default=0,
+                    help="independently repacked weight copies that consecutive steps rotate through "
+                         "(0: enough for 2 GB of weights, at least 2, at most 8), so that no step finds "
+                         "its weights in the 256 MB last-level cache from the step before")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (3 launches) so that profiler "
                          "byte counters can be scaled by a kernel of known traffic")
@@ -142,14 +154,28 @@ def main():
     print(f"[bench] generating {sh.name} (seeded)", file=sys.stderr, flush=True)
     wl = make_workload(sh)
     dev = "cuda:0"
-    layer = LatentMoE.from_workload(wl, device=dev)
+    R = args.weight_copies or min(8, max(2, -(-2_000_000_000 // weight_bytes(sh))))
+    layers = [LatentMoE.from_workload(wl, device=dev) for _ in range(R)]
+    layer = layers[0]
     x = to_device(wl.tensors["x"], sh.dtype, dev)
     y = torch.empty_like(x)
     T = sh.T
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        layer.forward(x, y)
+    print(f"[bench] {R} weight copies; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(max(args.warmup, R)):
+        layers[i % R].forward(x, y)
     torch.cuda.synchronize()
+
+    def profile_begin(n, mask=_abi.ALL_STAGES):
+        for L in layers:
+            _abi.latentmoe_profile_begin(L.handle, n, mask)
+
+    def profile_end():
+        tot = {}
+        for L in layers:
+            for k, (ms, n) in _abi.latentmoe_profile_end(L.handle).items():
+                a, b = tot.get(k, (0.0, 0))
+                tot[k] = (a + ms, b + n)
+        return tot
 
     timing = not args.no_stage_timing
     counts = layer.forward_debug(x, want=("counts",))["counts"].cpu().numpy()
@@ -181,17 +207,17 @@ def main():
     stage_out, dom = {}, None
     if timing:
         nb = min(args.steps, 10)
-        _abi.latentmoe_profile_begin(layer.handle, nb)
-        for _ in range(nb):
-            layer.forward(x, y)
-        stage_out = stage_table(_abi.latentmoe_profile_end(layer.handle))
+        profile_begin(nb)
+        for i in range(nb):
+            layers[i % R].forward(x, y)
+        stage_out = stage_table(profile_end())
         dom = max((k for k in stage_out if "frac" in stage_out[k]), key=lambda k: stage_out[k]["avg_us"])
         # the timed region records events around the dominant stage only
-        _abi.latentmoe_profile_begin(layer.handle, args.steps, 1 << names[dom])
+        profile_begin(args.steps, 1 << names[dom])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        layer.forward(x, y)
+    for i in range(args.steps):
+        layers[i % R].forward(x, y)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     print(f"[bench] timed {args.steps} steps in {dt:.3f} s", file=sys.stderr, flush=True)
@@ -199,13 +225,14 @@ def main():
     value = T * args.steps / dt
     roof = None
     if timing:
-        timed = stage_table(_abi.latentmoe_profile_end(layer.handle))[dom]
+        timed = stage_table(profile_end())[dom]
         flop, nbytes = work[dom]
         roof = {"kernel": dom, **roofline_of(flop, nbytes, timed["avg_us"] * 1e-6, sh.dtype),
                 "avg_us": timed["avg_us"], "launches": timed["launches"],
                 "traffic": profiled_traffic(sh.name, dom)}
     total_flop = sum(f for f, _ in work.values() if f)
-    layer.close()
+    for L in layers:
+        L.close()
     if args.copy_calibration:
         # reads 256 MiB and writes 256 MiB per launch
         a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -224,7 +251,7 @@ def main():
                                f"N'={sh.n_experts} K'={sh.top_k} S={sh.n_shared}x{sh.m_shared} "
                                f"{sh.variant} {sh.dtype}"
                                + (" (routed experts E4M3 + per-column scales)" if sh.expert_dtype == "fp8" else ""),
-                   "tokens": T, "experts_with_tokens": n_active},
+                   "tokens": T, "experts_with_tokens": n_active, "weight_copies": R},
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
         "roofline": roof, "cpu_baseline": cpu, "stages": stage_out,
         "stages_note": "per-stage HIP-event times from an untimed pass of min(steps, 10) forwards; "
