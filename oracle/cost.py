@@ -17,7 +17,10 @@ Symbols: d model width, l = d/alpha latent width, m expert hidden width,
 N' routed experts (N = N'/alpha in the baseline), K' active (K = K'/alpha for
 variant acc, K = K' for eff), S shared experts of hidden width m_s.
 b_w bytes per expert weight; b_out / b_back bytes per element sent to /
-returned from an expert.  FLOPs count 2 per multiply-add.
+returned from an expert.  FLOPs count 2 per multiply-add.  Gated experts
+(the explainer's feed-forward section: with a gated activation such as
+SwiGLU a third matrix stands beside W1 and everything else carries over)
+hold and touch three expert matrices in place of two: ``matrices=3``.
 """
 
 from dataclasses import dataclass
@@ -60,13 +63,14 @@ class LayerCost:
 
 
 def layer_cost(d: int, l: int, m: int, n_experts: int, top_k: int, alpha: int,
-               variant: str, n_shared: int, m_shared: int) -> LayerCost:
+               variant: str, n_shared: int, m_shared: int, matrices: int = 2) -> LayerCost:
     N, K = n_experts // alpha, (top_k // alpha if variant == "acc" else top_k)
-    latent_expert = 2 * l * m
-    shared = n_shared * 2 * d * m_shared
+    mm = matrices
+    latent_expert = mm * l * m
+    shared = n_shared * mm * d * m_shared
     proj = 2 * d * l
     pool = n_experts * latent_expert
-    base_expert = 2 * d * m
+    base_expert = mm * d * m
     c = LayerCost(
         latent_expert_params=latent_expert,
         routed_pool_params=pool,
@@ -74,7 +78,7 @@ def layer_cost(d: int, l: int, m: int, n_experts: int, top_k: int, alpha: int,
         router_params=d * n_experts,
         layer_params_excl_router=pool + shared + proj,
         active_params_per_token=top_k * latent_expert + shared + proj,
-        flops_per_token=2 * (d * n_experts + 2 * d * l + top_k * 2 * l * m + n_shared * 2 * d * m_shared),
+        flops_per_token=2 * (d * n_experts + 2 * d * l + top_k * mm * l * m + n_shared * mm * d * m_shared),
         log10_combinations=log10_comb(n_experts, top_k),
         baseline_n_experts=N,
         baseline_top_k=K,

@@ -12,7 +12,10 @@ Page: "LatentMoE: NVIDIA's Latent Mixture of Experts Explained Through
 Equations, Architecture, Code and ..." -- Figure 3 (router, softmax, top-K),
 Figure 6 (down/up projections), Figure 8 (the three paths of the layer),
 Figure 9 (latent expert = two matrices around a squared ReLU), and the MoE
-code block (renormalisation of the K selected weights).
+code block (renormalisation of the K selected weights).  Gated experts (the
+explainer's feed-forward section: a third matrix beside W1) use torch's
+``silu`` as the activation of the gate branch, so this file and the C
+oracle do not share the activation either.
 """
 
 import numpy as np
@@ -49,11 +52,23 @@ def sq_relu(a: np.ndarray) -> np.ndarray:
     return np.square(np.maximum(a, 0.0))
 
 
-def layer_dense(x, w_router, b_router, w_down, w1, w2, w_up, w1_s, w2_s, K):
-    """All arguments float64 numpy arrays in the [in, out] layout.
+def silu_torch(a: np.ndarray) -> np.ndarray:
+    import torch
+    return torch.nn.functional.silu(torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))).numpy()
+
+
+def layer_dense(x, w_router, b_router, w_down, w1, w2, w_up, w1_s, w2_s, K, w1g=None, w1g_s=None):
+    """All arguments float64 numpy arrays in the [in, out] layout.  With gate
+    banks w1g [N', l, m] and w1g_s [S, d, m_s] the experts are gated:
+    silu(a W_g) * (a W1) in place of relu(a W1)^2.
 
     Returns dict with logits s, dense gates G, z, u, y.
     """
+    def act(a_in, w_val, w_gate):
+        if w_gate is None:
+            return sq_relu(a_in @ w_val)
+        return silu_torch(a_in @ w_gate) * (a_in @ w_val)
+
     s = x @ w_router
     if b_router is not None:
         s = s + b_router[None, :]
@@ -61,15 +76,15 @@ def layer_dense(x, w_router, b_router, w_down, w1, w2, w_up, w1_s, w2_s, K):
     z = x @ w_down
     u = np.zeros((x.shape[0], w_down.shape[1]))
     for e in range(w1.shape[0]):
-        u += G[:, e:e + 1] * (sq_relu(z @ w1[e]) @ w2[e])
+        u += G[:, e:e + 1] * (act(z, w1[e], None if w1g is None else w1g[e]) @ w2[e])
     y = u @ w_up
     for j in range(w1_s.shape[0]):
-        y = y + sq_relu(x @ w1_s[j]) @ w2_s[j]
+        y = y + act(x, w1_s[j], None if w1g_s is None else w1g_s[j]) @ w2_s[j]
     return {"logits": s, "G": G, "z": z, "u": u, "y": y}
 
 
 def expert_bank_f64(wl, name):
-    """W1 or W2 of a workload in float64.  FP8 (E4M3) banks are decoded with
+    """W1, W2 or W_g of a workload in float64.  FP8 (E4M3) banks are decoded with
     torch's float8_e4m3fn type -- a decoder independent of the C oracle's --
     and scaled per expert and output column: W[e, i, j] = decode(q) * s[e, j]
     (exact in float64)."""
@@ -90,8 +105,11 @@ def layer_dense_from_workload(wl, tokens=None):
     S = wl.shape.n_shared
     w1s = f("w1_s") if S > 0 else np.zeros((0, wl.shape.d, 1))
     w2s = f("w2_s") if S > 0 else np.zeros((0, 1, wl.shape.d))
+    gated = wl.shape.expert_act == "swiglu"
+    w1g = expert_bank_f64(wl, "w1g") if gated else None
+    w1gs = (f("w1g_s") if S > 0 else np.zeros((0, wl.shape.d, 1))) if gated else None
     return layer_dense(x, f("w_router"), b, f("w_down"), expert_bank_f64(wl, "w1"),
-                       expert_bank_f64(wl, "w2"), f("w_up"), w1s, w2s, wl.shape.top_k)
+                       expert_bank_f64(wl, "w2"), f("w_up"), w1s, w2s, wl.shape.top_k, w1g, w1gs)
 
 
 def dispatch_argsort(idx: np.ndarray, N: int):

@@ -44,6 +44,15 @@
  * largest finite value is 448) with one float32 scale per expert and output
  * column: W_e[i][j] = decode(q_e[i][j]) * scale_e[j], formed exactly in
  * double.
+ *
+ * Gated experts: the explainer notes (its feed-forward section) that with a
+ * gated activation such as SwiGLU a third matrix stands beside W1 and all
+ * else carries over; the shaping paper's rank tables name an expert's three
+ * matrices W_g, W_u, W_o.  The reading taken: a gated expert computes
+ *   h = silu(W_g a) * (W1 a),  silu(v) = v / (1 + exp(-v)),  out = W2 h,
+ * with W_g of W1's shape (W1 playing W_u, W2 playing W_o), for the routed
+ * experts (input z, width l) and the shared experts (input x, width d) alike.
+ * An FP8 bank holds W_g like W1, with its own per-column scales.
  */
 #include <math.h>
 #include <stdint.h>
@@ -58,6 +67,7 @@ typedef struct {
     int32_t bf16;       /* 1: tensors hold bf16 bit patterns, 0: float32 */
     int32_t has_bias;   /* 1: b_router is used */
     int32_t expert_fp8; /* 1: w1 and w2 hold E4M3 bytes with per-column scales */
+    int32_t gated;      /* 1: gated (SwiGLU) experts, gate matrices w1g and w1g_s */
 } orc_shape;
 
 typedef struct {
@@ -72,6 +82,9 @@ typedef struct {
     const void *w2_s;     /* [S, m_s, d] */
     const float *w1_scale;/* [N', m]  (FP8 expert banks only) */
     const float *w2_scale;/* [N', l]  (FP8 expert banks only) */
+    const void *w1g;      /* [N', l, m]  gate matrices (gated experts) */
+    const void *w1g_s;    /* [S, d, m_s] shared gate matrices (gated experts) */
+    const float *w1g_scale;/* [N', m] (gated FP8 expert banks only) */
 } orc_tensors;
 
 /* Optional per-token outputs; any pointer may be NULL.  Row r of each array
@@ -81,10 +94,10 @@ typedef struct {
     int32_t *idx;    /* [n, K'] */
     double *gate;    /* [n, K'] */
     double *z;       /* [n, l] */
-    double *h;       /* [n, K', m]  relu(W1_e z)^2 per slot */
+    double *h;       /* [n, K', m]  relu(W1_e z)^2 (gated: silu(W_g z) * W1_e z) per slot */
     double *o;       /* [n, K', l]  W2_e h per slot (before the gate) */
     double *u;       /* [n, l] */
-    double *hs;      /* [n, S*m_s]  relu(W1_s x)^2 */
+    double *hs;      /* [n, S*m_s]  relu(W1_s x)^2 (gated: silu(W_g,s x) * W1_s x) */
     double *y;       /* [n, d] */
 } orc_outputs;
 
@@ -153,6 +166,10 @@ static void matvec(const double *in, const void *W, int64_t off, int64_t rows,
 
 static double sq_relu(double a) { return a > 0.0 ? a * a : 0.0; }
 
+/* silu(v) = v * sigmoid(v) = v / (1 + e^-v); for v -> -inf the quotient
+ * tends to -0, which the IEEE division gives once e^-v overflows. */
+static double silu(double v) { return v / (1.0 + exp(-v)); }
+
 /* The K' indices with the largest s, ordered by (s descending, index
  * ascending).  Plain repeated selection. */
 static int select_topk(const double *s, int64_t n, int64_t k, int32_t *idx,
@@ -215,6 +232,8 @@ int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
         return -1;
     if (c->expert_fp8 && (!w->w1_scale || !w->w2_scale))
         return -1;
+    if (c->gated && (!w->w1g || (c->n_shared > 0 && !w->w1g_s) || (c->expert_fp8 && !w->w1g_scale)))
+        return -1;
     for (int64_t r = 0; r < n_tok; ++r)
         if (tokens[r] < 0 || tokens[r] >= T)
             return -2;
@@ -238,11 +257,12 @@ int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
         unsigned char *taken = malloc((size_t)N);
         double *z = malloc(sizeof(double) * (size_t)l);
         double *a = malloc(sizeof(double) * (size_t)(m > ms ? m : ms));
+        double *gv = malloc(sizeof(double) * (size_t)(m > ms ? m : ms));
         double *o = malloc(sizeof(double) * (size_t)(l > d ? l : d));
         double *u = malloc(sizeof(double) * (size_t)l);
         double *y = malloc(sizeof(double) * (size_t)d);
         double *tmp = malloc(sizeof(double) * (size_t)d);
-        if (!x || !s || !sel || !g || !taken || !z || !a || !o || !u || !y || !tmp)
+        if (!x || !s || !sel || !g || !taken || !z || !a || !gv || !o || !u || !y || !tmp)
             err |= 1;
 
 #pragma omp for schedule(dynamic, 1)
@@ -298,8 +318,17 @@ int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
                     matvec_fp8(z, (const uint8_t *)w->w1, e * l * m, l, m, w->w1_scale + e * m, a);
                 else
                     matvec(z, w->w1, e * l * m, l, m, bf, a);
-                for (int64_t j = 0; j < m; ++j)
-                    a[j] = sq_relu(a[j]);
+                if (c->gated) {
+                    if (c->expert_fp8)
+                        matvec_fp8(z, (const uint8_t *)w->w1g, e * l * m, l, m, w->w1g_scale + e * m, gv);
+                    else
+                        matvec(z, w->w1g, e * l * m, l, m, bf, gv);
+                    for (int64_t j = 0; j < m; ++j)
+                        a[j] = silu(gv[j]) * a[j];
+                } else {
+                    for (int64_t j = 0; j < m; ++j)
+                        a[j] = sq_relu(a[j]);
+                }
                 if (out->h)
                     memcpy(out->h + (r * K + k) * m, a, sizeof(double) * (size_t)m);
                 if (c->expert_fp8)
@@ -318,8 +347,14 @@ int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
             matvec(u, w->w_up, 0, l, d, bf, y);
             for (int64_t sh = 0; sh < S; ++sh) {
                 matvec(x, w->w1_s, sh * d * ms, d, ms, bf, a);
-                for (int64_t j = 0; j < ms; ++j)
-                    a[j] = sq_relu(a[j]);
+                if (c->gated) {
+                    matvec(x, w->w1g_s, sh * d * ms, d, ms, bf, gv);
+                    for (int64_t j = 0; j < ms; ++j)
+                        a[j] = silu(gv[j]) * a[j];
+                } else {
+                    for (int64_t j = 0; j < ms; ++j)
+                        a[j] = sq_relu(a[j]);
+                }
                 if (out->hs)
                     memcpy(out->hs + r * S * ms + sh * ms, a, sizeof(double) * (size_t)ms);
                 matvec(a, w->w2_s, sh * ms * d, ms, d, bf, tmp);
@@ -330,7 +365,7 @@ int orc_forward(const orc_shape *c, const orc_tensors *w, int64_t T,
                 memcpy(out->y + r * d, y, sizeof(double) * (size_t)d);
         }
         free(x); free(s); free(sel); free(g); free(taken); free(z);
-        free(a); free(o); free(u); free(y); free(tmp);
+        free(a); free(gv); free(o); free(u); free(y); free(tmp);
     }
     return err ? -3 : 0;
 }

@@ -27,12 +27,13 @@ _vp = C.c_void_p
 class _Shape(C.Structure):
     _fields_ = [("d", _i64), ("l", _i64), ("m", _i64), ("m_s", _i64),
                 ("n_shared", _i64), ("n_experts", _i64), ("top_k", _i64),
-                ("bf16", _i32), ("has_bias", _i32), ("expert_fp8", _i32)]
+                ("bf16", _i32), ("has_bias", _i32), ("expert_fp8", _i32), ("gated", _i32)]
 
 
 class _Tensors(C.Structure):
     _fields_ = [(n, _vp) for n in ("x", "w_router", "b_router", "w_down", "w1",
-                                   "w2", "w_up", "w1_s", "w2_s", "w1_scale", "w2_scale")]
+                                   "w2", "w_up", "w1_s", "w2_s", "w1_scale", "w2_scale",
+                                   "w1g", "w1g_s", "w1g_scale")]
 
 
 class _Outputs(C.Structure):
@@ -101,6 +102,7 @@ def forward(wl, tokens: Optional[Sequence[int]] = None, want=("y",),
     sh = wl.shape
     bf16 = sh.dtype == "bf16"
     fp8 = sh.expert_dtype == "fp8"
+    gated = sh.expert_act == "swiglu"
     T = sh.T
     tok = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, dtype=np.int64)
     n = tok.shape[0]
@@ -108,11 +110,12 @@ def forward(wl, tokens: Optional[Sequence[int]] = None, want=("y",),
     S, ms = sh.n_shared, sh.m_shared
     t = {k: (None if wl.tensors.get(k) is None else _storage(wl.tensors[k], bf16))
          for k in ("x", "w_router", "w_down", "w_up", "w1_s", "w2_s")}
-    for k in ("w1", "w2"):
+    t["w1g_s"] = _storage(wl.tensors["w1g_s"], bf16) if (gated and S > 0) else None
+    for k in (("w1", "w2", "w1g") if gated else ("w1", "w2")):
         if fp8:
             t[k] = np.ascontiguousarray(wl.tensors[k], dtype=np.uint8)
             sc = np.ascontiguousarray(wl.tensors[k + "_scale"], dtype=np.float32)
-            assert sc.shape == (N, m if k == "w1" else l)
+            assert sc.shape == (N, l if k == "w2" else m)
             t[k + "_scale"] = sc
         else:
             t[k] = _storage(wl.tensors[k], bf16)
@@ -129,11 +132,12 @@ def forward(wl, tokens: Optional[Sequence[int]] = None, want=("y",),
         setattr(res, name, arr)
         setattr(outs, name, arr.ctypes.data)
     cs = _Shape(d, l, m, ms if S > 0 else 0, S, N, K, 1 if bf16 else 0,
-                1 if (sh.has_bias and b is not None) else 0, 1 if fp8 else 0)
+                1 if (sh.has_bias and b is not None) else 0, 1 if fp8 else 0, 1 if gated else 0)
     ct = _Tensors(_ptr(t["x"]), _ptr(t["w_router"]), _ptr(b), _ptr(t["w_down"]),
                   _ptr(t["w1"]), _ptr(t["w2"]), _ptr(t["w_up"]),
                   _ptr(t["w1_s"]) if S > 0 else None, _ptr(t["w2_s"]) if S > 0 else None,
-                  _ptr(t["w1_scale"]), _ptr(t["w2_scale"]))
+                  _ptr(t["w1_scale"]), _ptr(t["w2_scale"]),
+                  _ptr(t.get("w1g")), _ptr(t["w1g_s"]), _ptr(t.get("w1g_scale")))
     forced = None
     if idx_in is not None:
         forced = np.ascontiguousarray(idx_in, dtype=np.int32)

@@ -46,6 +46,7 @@ class LayerShape:
     x_seed: Optional[int] = None   # seed of x if it differs from ``seed``
     zipf_s: Optional[float] = None  # router bias exponent (None: no bias)
     expert_dtype: Optional[str] = None  # "fp8": W1/W2 as E4M3 bytes + per-column scales
+    expert_act: str = "relu2"  # "swiglu": gated experts silu(W_g a) * (W1 a), routed and shared
 
     @property
     def P(self) -> int:
@@ -86,6 +87,13 @@ CONFIGS = {
                                  n_experts=256, top_k=6, n_shared=2, m_shared=1408,
                                  alpha=4, variant="eff", dtype="bf16", seed=1,
                                  x_seed=2, expert_dtype="fp8"),
+    # gated (SwiGLU) experts at the shaping paper's 8B "deeper" expert widths
+    # (its Table 1: l = 640, m = 512, K'/N' = 16/512, shared width 1024),
+    # synthetic d = 2560, uniform routing
+    "shape_swiglu": LayerShape("shape_swiglu", T=8192, d=2560, l=640, m=512,
+                               n_experts=512, top_k=16, n_shared=1, m_shared=1024,
+                               alpha=4, variant="acc", dtype="bf16", seed=5,
+                               expert_act="swiglu"),
 }
 
 CONFIG_ORDER = ["tiny_f32", "readme_acc", "decode_eff", "wide_prefill", "zipf_skew"]

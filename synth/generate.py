@@ -1,7 +1,8 @@
 """Seeded generation of LatentMoE layer inputs.
 
-Recipe (one numpy ``SeedSequence(seed).spawn(9)`` child per tensor, in the
-fixed order x, W_r, b, W_down, W1, W2, W_up, W1_s, W2_s):
+Recipe (one numpy ``SeedSequence(seed).spawn(11)`` child per tensor, in the
+fixed order x, W_r, b, W_down, W1, W2, W_up, W1_s, W2_s, W_g, W_g_s; the
+first nine children do not depend on how many are spawned):
 
   * x ~ N(0, 1), shape [T, d]
   * every weight ~ N(0, 1/fan_in) with fan_in its input width:
@@ -9,6 +10,7 @@ fixed order x, W_r, b, W_down, W1, W2, W_up, W1_s, W2_s):
       W1  [N', l, m], W_up [l, d]                    -> fan_in l
       W2  [N', m, l]                                 -> fan_in m
       W2_s [S, m_s, d]                               -> fan_in m_s
+      gated experts only: W_g [N', l, m] -> fan_in l, W_g_s [S, d, m_s] -> fan_in d
     Weights are stored [in, out] row-major, so row i of a matrix holds the
     weights leaving input coordinate i.
   * optional router bias b_e = 2 ln( (e+1)^-s / H_{N', s} )  (Zipf law of
@@ -23,7 +25,8 @@ FP8 expert banks (``expert_dtype="fp8"``): each expert's W1 and W2 float32
 draw is quantized per output column j: scale_j = max_i |W[i, j]| / 448 (the
 largest finite E4M3 value) and q[i, j] = E4M3(W[i, j] / scale_j), rounded to
 nearest even by torch's float8_e4m3fn conversion.  The bytes q and the
-float32 scales are the canonical inputs; the other tensors stay bf16.
+float32 scales are the canonical inputs; the other tensors stay bf16.  A
+gated bank's W_g is quantized the same way.
 """
 
 from dataclasses import dataclass, field
@@ -34,7 +37,7 @@ import numpy as np
 
 from .configs import LayerShape
 
-_ORDER = ("x", "w_router", "b_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s")
+_ORDER = ("x", "w_router", "b_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s", "w1g", "w1g_s")
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -146,7 +149,7 @@ def _children(seed: int):
 
 @lru_cache(maxsize=4)
 def _weights(shape_key: tuple) -> Dict[str, np.ndarray]:
-    (d, l, m, n_e, S, m_s, dtype, seed, zipf_s, expert_dtype) = shape_key
+    (d, l, m, n_e, S, m_s, dtype, seed, zipf_s, expert_dtype, expert_act) = shape_key
     ch = _children(seed)
     g = {name: np.random.default_rng(c) for name, c in zip(_ORDER, ch)}
     w = {}
@@ -162,6 +165,12 @@ def _weights(shape_key: tuple) -> Dict[str, np.ndarray]:
     w["w_up"] = _store(_normal(g["w_up"], (l, d), l), dtype)
     w["w1_s"] = _bank(g["w1_s"], S, (d, m_s), d, dtype)
     w["w2_s"] = _bank(g["w2_s"], S, (m_s, d), m_s, dtype)
+    if expert_act == "swiglu":
+        if expert_dtype == "fp8":
+            w["w1g"], w["w1g_scale"] = _bank_fp8(g["w1g"], n_e, (l, m), l)
+        else:
+            w["w1g"] = _bank(g["w1g"], n_e, (l, m), l, dtype)
+        w["w1g_s"] = _bank(g["w1g_s"], S, (d, m_s), d, dtype)
     for a in w.values():
         if a is not None:
             a.setflags(write=False)
@@ -179,7 +188,7 @@ def make_workload(shape: LayerShape, T: Optional[int] = None,
                   x_seed: Optional[int] = None) -> Workload:
     """Weights from ``shape.seed``; x from ``x_seed`` (default: the shape's)."""
     key = (shape.d, shape.l, shape.m, shape.n_experts, shape.n_shared,
-           shape.m_shared, shape.dtype, shape.seed, shape.zipf_s, shape.expert_dtype)
+           shape.m_shared, shape.dtype, shape.seed, shape.zipf_s, shape.expert_dtype, shape.expert_act)
     w = _weights(key)
     x = make_x(shape, T, x_seed)
     t = dict(w)

@@ -7,18 +7,22 @@ from synth.generate import f32_to_bf16_bits
 
 
 def shape(name="custom", T=8, d=8, l=4, m=6, n_experts=4, top_k=2, n_shared=1,
-          m_shared=5, alpha=2, variant="acc", dtype="f32", seed=0, zipf_s=None, expert_dtype=None):
+          m_shared=5, alpha=2, variant="acc", dtype="f32", seed=0, zipf_s=None, expert_dtype=None,
+          expert_act="relu2"):
     return LayerShape(name, T=T, d=d, l=l, m=m, n_experts=n_experts, top_k=top_k,
                       n_shared=n_shared, m_shared=m_shared, alpha=alpha,
                       variant=variant, dtype=dtype, seed=seed, zipf_s=zipf_s,
-                      expert_dtype=expert_dtype)
+                      expert_dtype=expert_dtype, expert_act=expert_act)
 
 
 def workload_from_arrays(sh: LayerShape, arrays: dict) -> Workload:
     """Build a workload from float arrays (exactly representable in the
     shape's dtype).  Missing shared banks become empty."""
     t = {}
-    for k in ("x", "w_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s"):
+    names = ["x", "w_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s"]
+    if sh.expert_act == "swiglu":
+        names += ["w1g", "w1g_s"]
+    for k in names:
         a = np.asarray(arrays[k], dtype=np.float32)
         if sh.dtype == "bf16":
             bits = f32_to_bf16_bits(a)
@@ -48,6 +52,9 @@ def random_arrays(sh: LayerShape, rng, scale=1.0):
     }
     if sh.has_bias:
         a["b_router"] = rng.standard_normal(sh.n_experts).astype(np.float32)
+    if sh.expert_act == "swiglu":  # drawn last: the other arrays do not depend on it
+        a["w1g"] = nrm((sh.n_experts, sh.l, sh.m), sh.l)
+        a["w1g_s"] = nrm((S, sh.d, sh.m_shared), sh.d)
     if sh.dtype == "bf16":
         from synth import round_to_bf16
         a = {k: (round_to_bf16(v) if k != "b_router" else v) for k, v in a.items()}
@@ -76,7 +83,7 @@ def random_fp8_workload(sh: LayerShape, seed=0, pow2_scales=False) -> Workload:
     rng = np.random.default_rng(seed)
     arrays = random_arrays(sh, rng)
     t = dict(workload_from_arrays(sh, arrays).tensors)
-    for k in ("w1", "w2"):
+    for k in (("w1", "w2", "w1g") if sh.expert_act == "swiglu" else ("w1", "w2")):
         w = arrays[k]
         q = np.empty(w.shape, dtype=np.uint8)
         sc = np.empty((w.shape[0], w.shape[2]), dtype=np.float32)
