@@ -40,12 +40,14 @@ def stage_work(sh, T, n_active):
     ms = sh.n_shared * sh.m_shared
     ldzh = sh.l + ms
     N, d, l, m = sh.n_experts, sh.d, sh.l, sh.m
+    g = 2 if sh.expert_act == "swiglu" else 1  # gated: a gate matrix beside each W1
+    nx = N + l + g * ms                         # B columns of the pass over x
     return {
         # one pass over x: router scores (fp32 out), z and the shared-expert hidden layer
-        "gemm_x_router_down_shared1": (2.0 * T * d * (N + ldzh),
-                                       es * (T * d + d * (N + ldzh) + T * ldzh) + 4.0 * T * N),
+        "gemm_x_router_down_shared1": (2.0 * T * d * nx,
+                                       es * (T * d + d * nx + T * ldzh) + 4.0 * T * N),
         # expert weights (+ their fp32 column scales for E4M3 banks), rows in and out
-        "grouped_gemm1_relu2": (2.0 * P * l * m, ew * n_active * l * m + (4.0 * n_active * m if fp8 else 0.0)
+        "grouped_gemm1_relu2": (2.0 * P * l * m * g, g * (ew * n_active * l * m + (4.0 * n_active * m if fp8 else 0.0))
                                 + es * (P * l + P * m) + 4.0 * P),
         "grouped_gemm2": (2.0 * P * m * l, ew * n_active * m * l + (4.0 * n_active * l if fp8 else 0.0)
                           + es * (P * m + P * l)),
@@ -120,8 +122,9 @@ def weight_bytes(sh) -> int:
     """Bytes of one repacked copy of the layer's weights."""
     es = 4 if sh.dtype == "f32" else 2
     eb = 1 if sh.expert_dtype == "fp8" else es
-    dense = sh.d * (sh.n_experts + sh.l) + sh.l * sh.d + 2 * sh.n_shared * sh.d * sh.m_shared
-    return 2 * dense * es + 2 * sh.n_experts * sh.l * sh.m * eb  # the dense part twice: tiled + fragment-major
+    mats = 3 if sh.expert_act == "swiglu" else 2
+    dense = sh.d * (sh.n_experts + sh.l) + sh.l * sh.d + mats * sh.n_shared * sh.d * sh.m_shared
+    return 2 * dense * es + mats * sh.n_experts * sh.l * sh.m * eb  # the dense part twice: tiled + fragment-major
 
 
 def main():
@@ -250,7 +253,8 @@ def main():
         "config": {"workload": f"{sh.name}: LatentMoE layer forward, T={T} d={sh.d} l={sh.l} m={sh.m} "
                                f"N'={sh.n_experts} K'={sh.top_k} S={sh.n_shared}x{sh.m_shared} "
                                f"{sh.variant} {sh.dtype}"
-                               + (" (routed experts E4M3 + per-column scales)" if sh.expert_dtype == "fp8" else ""),
+                               + (" (routed experts E4M3 + per-column scales)" if sh.expert_dtype == "fp8" else "")
+                               + (" SwiGLU experts" if sh.expert_act == "swiglu" else ""),
                    "tokens": T, "experts_with_tokens": n_active, "weight_copies": R},
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
         "roofline": roof, "cpu_baseline": cpu, "stages": stage_out,

@@ -63,6 +63,14 @@ typedef enum latentmoe_expert_format {
     LATENTMOE_EXPERT_FP8_E4M3 = 1
 } latentmoe_expert_format;
 
+/* Expert activation.  RELU2: out = W2 relu(W1 a)^2 (the explainer's Expert
+ * class and Figure 9).  SWIGLU: the gated form the explainer's feed-forward
+ * section allows ("a third matrix beside W1"; the shaping paper's W_g, W_u,
+ * W_o): out = W2 (silu(W_g a) * (W1 a)), silu(v) = v / (1 + e^-v), for the
+ * routed experts (a = z) and the shared experts (a = x) alike; the gate
+ * matrices come in w1_gate and w1_shared_gate. */
+typedef enum latentmoe_expert_act { LATENTMOE_ACT_RELU2 = 0, LATENTMOE_ACT_SWIGLU = 1 } latentmoe_expert_act;
+
 typedef struct latentmoe_config {
     int64_t d;          /* model width */
     int64_t l;          /* latent width; l * alpha == d */
@@ -77,6 +85,7 @@ typedef struct latentmoe_config {
     int64_t max_tokens; /* largest T a forward call may pass; sizes the workspace */
     int32_t has_router_bias; /* 1: b_router is added to the scores before softmax */
     int32_t expert_format;   /* latentmoe_expert_format */
+    int32_t expert_act;      /* latentmoe_expert_act */
 } latentmoe_config;
 
 /* Device pointers, in the config's dtype except b_router and the scales
@@ -94,6 +103,9 @@ typedef struct latentmoe_weights {
     const void *w2_shared;  /* [S, m_shared, d] (NULL when S == 0) */
     const float *w1_scale;  /* [N', m] FP8 expert banks only, else NULL */
     const float *w2_scale;  /* [N', l] FP8 expert banks only, else NULL */
+    const void *w1_gate;         /* [N', l, m] SWIGLU only (E4M3 bytes in an FP8 bank), else NULL */
+    const void *w1_shared_gate;  /* [S, d, m_shared] SWIGLU with S > 0 only, else NULL */
+    const float *w1_gate_scale;  /* [N', m] SWIGLU FP8 expert banks only, else NULL */
 } latentmoe_weights;
 
 /* Optional device buffers that a forward call fills with its intermediate
@@ -116,7 +128,9 @@ typedef struct latentmoe_debug {
 /* Closed-form cost counts (README "Inspect the asymptotic cost quantities
  * from Table 1" section; every worked count of the explainer reproduces).
  * The baseline is the standard MoE with N = N'/alpha experts of width d and
- * K = K'/alpha (acc) or K' (eff).  FLOPs count 2 per multiply-add. */
+ * K = K'/alpha (acc) or K' (eff).  FLOPs count 2 per multiply-add.  The
+ * "2" of each expert term below is the number of expert matrices: 3 for
+ * LATENTMOE_ACT_SWIGLU (routed, shared and baseline experts alike). */
 typedef struct latentmoe_cost_out {
     double latent_expert_params;        /* 2 l m */
     double routed_pool_params;          /* N' 2 l m */
@@ -144,7 +158,9 @@ typedef struct latentmoe_handle latentmoe_handle;
 /* Validate cfg and w, allocate the workspace for cfg->max_tokens, and copy
  * the weights into the kernels' layout on `hip_stream` (a hipStream_t, or
  * NULL for the default stream).  Returns when the copies are complete.
- * On success *out owns the handle; on failure *out is NULL. */
+ * On success *out owns the handle; on failure *out is NULL.  A weight that
+ * the config needs and w leaves NULL (the scales of an FP8 bank, the gate
+ * matrices of a SWIGLU layer) is LATENTMOE_ERR_INVALID_ARGUMENT. */
 int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w,
                      void *hip_stream, latentmoe_handle **out);
 

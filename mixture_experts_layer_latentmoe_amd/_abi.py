@@ -18,6 +18,7 @@ LATENTMOE_ERR_HIP = 4
 LATENTMOE_VARIANT_ACC, LATENTMOE_VARIANT_EFF = 0, 1
 LATENTMOE_DTYPE_F32, LATENTMOE_DTYPE_BF16 = 0, 1
 LATENTMOE_EXPERT_AS_DTYPE, LATENTMOE_EXPERT_FP8_E4M3 = 0, 1
+LATENTMOE_ACT_RELU2, LATENTMOE_ACT_SWIGLU = 0, 1
 LATENTMOE_MAX_STAGES = 16
 
 EXPORTED = ("latentmoe_create", "latentmoe_forward", "latentmoe_destroy", "latentmoe_validate_config",
@@ -29,12 +30,14 @@ EXPORTED = ("latentmoe_create", "latentmoe_forward", "latentmoe_destroy", "laten
 class latentmoe_config(C.Structure):
     _fields_ = [("d", _i64), ("l", _i64), ("m", _i64), ("m_shared", _i64), ("n_shared", _i64),
                 ("n_experts", _i64), ("top_k", _i64), ("alpha", _i64), ("variant", _i32),
-                ("dtype", _i32), ("max_tokens", _i64), ("has_router_bias", _i32), ("expert_format", _i32)]
+                ("dtype", _i32), ("max_tokens", _i64), ("has_router_bias", _i32), ("expert_format", _i32),
+                ("expert_act", _i32)]
 
 
 class latentmoe_weights(C.Structure):
     _fields_ = [(n, _vp) for n in ("w_router", "b_router", "w_down", "w1", "w2", "w_up",
-                                   "w1_shared", "w2_shared", "w1_scale", "w2_scale")]
+                                   "w1_shared", "w2_shared", "w1_scale", "w2_scale",
+                                   "w1_gate", "w1_shared_gate", "w1_gate_scale")]
 
 
 class latentmoe_debug(C.Structure):
@@ -111,12 +114,14 @@ def _check(fn, st):
 
 
 def make_config(d, l, m, n_experts, top_k, alpha, n_shared=0, m_shared=0, variant="acc",
-                dtype="bf16", max_tokens=1, has_router_bias=False, expert_dtype=None) -> latentmoe_config:
+                dtype="bf16", max_tokens=1, has_router_bias=False, expert_dtype=None,
+                expert_act="relu2") -> latentmoe_config:
     return latentmoe_config(d, l, m, m_shared, n_shared, n_experts, top_k, alpha,
                             LATENTMOE_VARIANT_ACC if variant == "acc" else LATENTMOE_VARIANT_EFF,
                             LATENTMOE_DTYPE_BF16 if dtype == "bf16" else LATENTMOE_DTYPE_F32,
                             max_tokens, 1 if has_router_bias else 0,
-                            LATENTMOE_EXPERT_FP8_E4M3 if expert_dtype == "fp8" else LATENTMOE_EXPERT_AS_DTYPE)
+                            LATENTMOE_EXPERT_FP8_E4M3 if expert_dtype == "fp8" else LATENTMOE_EXPERT_AS_DTYPE,
+                            LATENTMOE_ACT_SWIGLU if expert_act == "swiglu" else LATENTMOE_ACT_RELU2)
 
 
 def latentmoe_validate_config(cfg: latentmoe_config) -> int:

@@ -54,7 +54,11 @@ struct GemmParams {
     const float *bias32;  // nullable
     int c_split;        // multiple of 4; 0: no fp32 part
     int M, N, K;        // M: dense rows (unused in grouped mode)
-    int relu2_from;     // first column of C (after the split) that gets relu^2
+    int relu2_from = 1 << 30;  // first column of C (after the split) that gets relu^2
+    int glu_from = 1 << 30;    // first B column of gated pairs: from it on, in blocks of 16 B columns,
+                        // 8 gate columns then the 8 value columns of the same outputs; each
+                        // block gives 8 C columns silu(gate) * value (>= N: none).  A multiple
+                        // of 16, at or after c_split.
     int group_m;        // dense: tiles of this many M-tiles are walked together
     int splitk;         // dense: > 1 splits K into this many contiguous k-tile ranges;
                         // raw fp32 sums go to partial[split][M][N] and a reduce
@@ -237,6 +241,18 @@ __device__ __forceinline__ void store_out4(const GemmParams &p, int64_t row, int
 
 // Epilogue straight from the accumulators: each lane stores runs of four
 // output columns (times the column scales cs, if any).
+// silu(g) * v for a gated pair; silu(g) = g / (1 + e^-g) (for g -> -inf
+// the quotient tends to -0: e^-g overflows to +inf first).
+__device__ __forceinline__ float glu_value(float g, float v) { return g / (1.f + expf(-g)) * v; }
+
+// C column of the output that the gate group starting at B column `col`
+// (col >= glu_from, (col - glu_from) % 16 < 8) feeds.
+__device__ __forceinline__ int glu_out_col(const GemmParams &p, int col)
+{
+    const int rel = col - p.glu_from;
+    return p.glu_from - p.c_split + (rel >> 4) * 8 + (rel & 15);
+}
+
 template <typename E, int TM, int TN, int WTM, int WTN>
 __device__ __forceinline__ void store_tile_direct(const GemmParams &p, const f32x16 (&acc)[TM][TN], int64_t row_base,
                                                   int rows_valid, int n0, int wm, int wn, int lane,
@@ -260,6 +276,20 @@ __device__ __forceinline__ void store_tile_direct(const GemmParams &p, const f32
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
                         v[r] *= cs[col + r];
+                }
+                if (col >= p.glu_from) {
+                    // tiles start at multiples of 32 and glu_from is a multiple
+                    // of 16, so the gate groups are the even g and their value
+                    // groups (8 columns on) the next register group
+                    if (g & 1)
+                        continue;
+                    float u[4] = {acc[i][jn][4 * g + 4], acc[i][jn][4 * g + 5], acc[i][jn][4 * g + 6],
+                                  acc[i][jn][4 * g + 7]};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = glu_value(v[r], cs ? u[r] * cs[col + 8 + r] : u[r]);
+                    store4(static_cast<E *>(p.C) + row * p.ldc + glu_out_col(p, col), v[0], v[1], v[2], v[3]);
+                    continue;
                 }
                 store_out4<E>(p, row, col, v);
             }
@@ -311,6 +341,70 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
                         const float t = fmaxf(v[r], 0.f);
                         v[r] = t * t;
                     }
+                const int byte = cc * ES, ch = byte / 16;
+                store4(reinterpret_cast<E *>(sb + (lr * CPR + (ch ^ (lr & (CPR - 1)))) * 16 + byte % 16), v[0], v[1],
+                       v[2], v[3]);
+            }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r0 = 0; r0 < 32; r0 += RPI) {
+            const int rl = r0 + lane / CPR;
+            const uint4 v = stg[rl * CPR + (cw ^ (rl & (CPR - 1)))];
+            if (col_ok && i * 32 + rl < rows_here)
+                *reinterpret_cast<uint4 *>(C + (row_base + wm * WTM + i * 32 + rl) * p.ldc + cbase + cw * (16 / ES)) = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// The staged epilogue of a wave block whose B columns are all gated pairs
+// (bcol0 = n0 + wn WTN >= glu_from): the wave stages 32 rows x WTN / 2
+// outputs silu(gate) * value, then writes whole 16-byte chunks of output
+// rows.  bcol0 - glu_from is a multiple of 16, so the gate groups are the even
+// register groups g, their values sit in group g + 1, and the outputs of gate
+// group g of MFMA tile jn are staged columns 16 jn + 4 g + 4 (lane / 32).
+template <typename E, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_tile_staged_glu(const GemmParams &p, const f32x16 (&acc)[TM][TN],
+                                                      int64_t row_base, int rows_valid, int n0, int wm, int wn,
+                                                      int lane, uint4 *stg, const float *cs = nullptr)
+{
+    constexpr int ES = (int)sizeof(E);
+    constexpr int CPR = (WTN / 2) * ES / 16;  // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPR;             // staged rows per store instruction
+    static_assert(CPR >= 1 && CPR <= 64 && (CPR & (CPR - 1)) == 0, "staged row");
+    const int lr = lane & 31, lc = lane >> 5;
+    const int bcol0 = n0 + wn * WTN;
+    const int cbase = glu_out_col(p, bcol0);  // C column of the wave's first output
+    const int rows_here = rows_valid - wm * WTM;
+    const int cw = lane % CPR;
+    const bool col_ok = bcol0 + cw * 2 * (16 / ES) < p.N;  // a chunk's outputs come from 2 x its width of B
+    E *C = static_cast<E *>(p.C);
+    char *sb = reinterpret_cast<char *>(stg);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        if (i * 32 >= rows_here)  // uniform: nothing left to store
+            break;
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+            for (int g = 0; g < 4; g += 2) {
+                float v[4] = {acc[i][jn][4 * g], acc[i][jn][4 * g + 1], acc[i][jn][4 * g + 2], acc[i][jn][4 * g + 3]};
+                float u[4] = {acc[i][jn][4 * g + 4], acc[i][jn][4 * g + 5], acc[i][jn][4 * g + 6],
+                              acc[i][jn][4 * g + 7]};
+                if (cs) {
+                    const int col = bcol0 + jn * 32 + 8 * g + 4 * lc;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        v[r] *= (col + r < p.N) ? cs[col + r] : 0.f;
+                        u[r] *= (col + 8 + r < p.N) ? cs[col + 8 + r] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = glu_value(v[r], u[r]);
+                const int cc = jn * 16 + 4 * g + 4 * lc;  // output column inside the wave block
                 const int byte = cc * ES, ch = byte / 16;
                 store4(reinterpret_cast<E *>(sb + (lr * CPR + (ch ^ (lr & (CPR - 1)))) * 16 + byte % 16), v[0], v[1],
                        v[2], v[3]);
@@ -519,7 +613,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     }
 
     const float *cs = (BQ8 && p.scaleB) ? p.scaleB + (int64_t)expert * p.N : nullptr;  // column scales
-    if (sizeof(E) != 2 || n0 < p.c_split) {  // fp32 outputs: straight from the registers
+    // fp32 outputs, and tiles that hold router columns or straddle the start
+    // of the gated pairs: straight from the registers
+    if (sizeof(E) != 2 || n0 < p.c_split || (n0 < p.glu_from && n0 + BN > p.glu_from)) {
         store_tile_direct<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, cs);
         return;
     }
@@ -534,7 +630,10 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
         uint4 *stg = (IN_A ? (wave < PER_ARR ? sA0 : sA1) : (wave < PER_ARR ? sB0 : sB1)) + (wave % PER_ARR) * WAVE_U;
-        store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg, cs);
+        if (n0 >= p.glu_from)
+            store_tile_staged_glu<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg, cs);
+        else
+            store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg, cs);
     }
 #endif
 }
@@ -550,13 +649,32 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p)
         return;
     const int64_t row = q / groups;
     const int col = (int)(q - row * groups) * 4;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    // gated pairs: the thread of a gate group also sums its value group
+    // (8 columns on); the thread of a value group has nothing to do
+    const bool glu = col >= p.glu_from;
+    if (glu && ((col - p.glu_from) & 15) >= 8)
+        return;
+    float v[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < p.splitk; ++s) {
-        const float4 x = *reinterpret_cast<const float4 *>(p.partial + ((int64_t)s * p.M + row) * p.N + col);
+        const float *src = p.partial + ((int64_t)s * p.M + row) * p.N + col;
+        const float4 x = *reinterpret_cast<const float4 *>(src);
         v[0] += x.x;
         v[1] += x.y;
         v[2] += x.z;
         v[3] += x.w;
+        if (glu) {
+            const float4 w = *reinterpret_cast<const float4 *>(src + 8);
+            u[0] += w.x;
+            u[1] += w.y;
+            u[2] += w.z;
+            u[3] += w.w;
+        }
+    }
+    if (glu) {
+        for (int r = 0; r < 4; ++r)
+            v[r] = glu_value(v[r], u[r]);
+        store4(static_cast<E *>(p.C) + row * p.ldc + glu_out_col(p, col), v[0], v[1], v[2], v[3]);
+        return;
     }
     store_out4<E>(p, row, col, v);
 }

@@ -80,8 +80,10 @@ struct Plan {
     bool fp8;       // routed-expert banks W1/W2 as E4M3 bytes + per-column scales
     int wesize;     // bytes per W1/W2 element
     int bk_b;       // elements per k-tile of the W1/W2 B tiles (128 bytes, 64 for E4M3)
+    bool glu;       // gated (SwiGLU) experts: gate and value columns interleaved in the B operands
+    int64_t nb1;    // B columns of grouped GEMM 1: m, or 2m when gated
     int64_t ld_zh;  // l + S*ms: row of [z|u , h_s]
-    int64_t n_x;    // N' + l + S*ms: output columns of the pass over x
+    int64_t n_x;    // N' + l + S*ms (gated: N' + l + 2 S*ms): B columns of the pass over x
     int64_t nchunks_max;
     int64_t ld_chunks;  // row length of the expert-major chunk arrays (multiple of 4)
     int64_t P_max;
@@ -89,6 +91,7 @@ struct Plan {
 };
 
 constexpr int kGroupBM = 128, kGroupBMSmall = 32, kMinGroupBM = 32;
+constexpr int kNoColumn = 1 << 30;  // relu2_from / glu_from: no such columns
 constexpr int kSplitKMaxRows = 256, kSplitKMax = 16;
 
 int64_t max_mtiles_for(int64_t P, int64_t N, int bm) { return (P + bm - 1) / bm + std::min<int64_t>(N, P); }
@@ -147,6 +150,8 @@ int validate(const latentmoe_config *c)
         return LATENTMOE_ERR_INVALID_ARGUMENT;
     if (c->expert_format != LATENTMOE_EXPERT_AS_DTYPE && c->expert_format != LATENTMOE_EXPERT_FP8_E4M3)
         return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (c->expert_act != LATENTMOE_ACT_RELU2 && c->expert_act != LATENTMOE_ACT_SWIGLU)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
     // kernel support
     if (c->expert_format == LATENTMOE_EXPERT_FP8_E4M3 && c->dtype != LATENTMOE_DTYPE_BF16)
         return LATENTMOE_ERR_UNSUPPORTED;
@@ -163,11 +168,13 @@ int validate(const latentmoe_config *c)
     // offsets: each must stay below 2 GiB
     const int64_t es = c->dtype == LATENTMOE_DTYPE_BF16 ? 2 : 4;
     const int64_t ld_zh = c->l + c->n_shared * ms;
+    const int64_t gm = c->expert_act == LATENTMOE_ACT_SWIGLU ? 2 : 1;  // gated: gate beside W1
+    const int64_t n_x = c->n_experts + c->l + gm * c->n_shared * ms;
     const int64_t lim = (int64_t(1) << 31) - 1;
     if (c->max_tokens * c->d * es > lim || c->max_tokens * ld_zh * es > lim || P * c->m * es > lim ||
-        (c->n_experts + ld_zh) * c->d * es > lim || c->d * ld_zh * es > lim || c->max_tokens * c->n_experts * 4 > lim ||
-        c->l * c->m * es > lim ||  // one expert's W1 or W2
-        (c->n_experts + ld_zh + 31) * c->d * es > lim)  // fragment-major copy (rows padded to 32)
+        (n_x + 31) * c->d * es > lim || c->d * ld_zh * es > lim || c->max_tokens * c->n_experts * 4 > lim ||
+        gm * c->l * c->m * es > lim)  // one expert's GEMM 1 bank ([W_g | W1] when gated) or W2;
+                                       // x-pass rows padded to 32 in the fragment-major copy
         return LATENTMOE_ERR_UNSUPPORTED;
     return LATENTMOE_OK;
 }
@@ -189,8 +196,10 @@ Plan make_plan(const latentmoe_config *c)
     p.fp8 = c->expert_format == LATENTMOE_EXPERT_FP8_E4M3;
     p.wesize = p.fp8 ? 1 : p.esize;
     p.bk_b = p.fp8 ? 64 : 128 / p.esize;
+    p.glu = c->expert_act == LATENTMOE_ACT_SWIGLU;
+    p.nb1 = p.glu ? 2 * p.m : p.m;
     p.ld_zh = p.l + p.S * p.ms;
-    p.n_x = p.N + p.ld_zh;
+    p.n_x = p.N + p.l + p.S * p.ms * (p.glu ? 2 : 1);
     p.nchunks_max = (p.Tmax + kRouterTokens - 1) / kRouterTokens;
     p.ld_chunks = align_up(p.nchunks_max, 4);
     p.P_max = p.Tmax * p.K;
@@ -255,11 +264,11 @@ WLayout w_layout(const Plan &p)
     };
     const int64_t es = p.esize;
     L.off_c1 = take(es * p.n_x * p.d);
-    L.off_w1 = take(p.wesize * p.N * p.m * p.l);
+    L.off_w1 = take(p.wesize * p.N * p.nb1 * p.l);
     L.off_w2 = take(p.wesize * p.N * p.l * p.m);
     L.off_c2 = take(es * p.d * p.ld_zh);
     L.off_bias = take(4 * p.N);
-    L.off_s1 = take(p.fp8 ? 4 * p.N * p.m : 0);
+    L.off_s1 = take(p.fp8 ? 4 * p.N * p.nb1 : 0);
     L.off_s2 = take(p.fp8 ? 4 * p.N * p.l : 0);
     L.off_f1 = take(es * align_up(p.n_x, 32) * p.d);
     L.off_f2 = take(es * align_up(p.d, 32) * p.ld_zh);
@@ -269,14 +278,14 @@ WLayout w_layout(const Plan &p)
 
 template <typename E>
 void launch_transpose(const void *src, int64_t R, int64_t C, int64_t batch, int64_t src_bstride, void *dst,
-                      int64_t dst_ld, int64_t dst_bstride, hipStream_t s)
+                      int64_t dst_ld, int64_t dst_bstride, hipStream_t s, int glu_off = -1)
 {
     constexpr int64_t kMaxZ = 32768;  // grid z stays below the 65535 limit
     for (int64_t b0 = 0; b0 < batch; b0 += kMaxZ) {
         dim3 grid((unsigned)((C + 31) / 32), (unsigned)((R + 31) / 32), (unsigned)std::min(kMaxZ, batch - b0));
         transpose_kernel<E><<<grid, dim3(256), 0, s>>>(static_cast<const E *>(src) + b0 * src_bstride, R, C,
                                                        src_bstride, static_cast<E *>(dst) + b0 * dst_bstride,
-                                                       dst_ld, dst_bstride);
+                                                       dst_ld, dst_bstride, glu_off);
         hip_check(hipGetLastError());
     }
 }
@@ -301,25 +310,48 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
     char *w2 = base + L.off_w2;
     E *c2 = reinterpret_cast<E *>(base + L.off_c2);
     // [W_r | W_down | W1_s] [d, N' + l + S m_s] -> K-contiguous rows:
-    // W_r^T (N' rows), W_down^T (l rows), then W1_s[j]^T (m_s rows each)
+    // W_r^T (N' rows), W_down^T (l rows), then W1_s[j]^T (m_s rows each;
+    // gated: 2 m_s rows each, 8 gate rows then 8 value rows per 8 outputs)
     launch_transpose<E>(w->w_router, p.d, p.N, 1, 0, c1, p.d, 0, s);
     launch_transpose<E>(w->w_down, p.d, p.l, 1, 0, c1 + p.N * p.d, p.d, 0, s);
-    if (p.S > 0)
+    if (p.S > 0 && p.glu) {
+        E *sh = c1 + (p.N + p.l) * p.d;
+        launch_transpose<E>(w->w1_shared_gate, p.d, p.ms, p.S, p.d * p.ms, sh, p.d, 2 * p.ms * p.d, s, 0);
+        launch_transpose<E>(w->w1_shared, p.d, p.ms, p.S, p.d * p.ms, sh, p.d, 2 * p.ms * p.d, s, 8);
+    } else if (p.S > 0) {
         launch_transpose<E>(w->w1_shared, p.d, p.ms, p.S, p.d * p.ms, c1 + (p.N + p.l) * p.d, p.d, p.ms * p.d, s);
-    // W1 [N', l, m] -> [N', l / bk, m, bk];  W2 [N', m, l] -> [N', m / bk, l, bk]:
-    // per expert, k-tile t of output column n sits at (t * cols + n) * bk, so
-    // that the B tile of one k-step is one contiguous run (E4M3 banks: the
-    // same moves of bytes; their scales are copied as they are)
-    const int64_t bk = p.bk_b;
+    }
+    // W1 [N', l, m] -> [N', l / bk, nb1, bk];  W2 [N', m, l] -> [N', m / bk, l, bk]:
+    // per expert, k-tile t of B column n sits at (t * cols + n) * bk, so that
+    // the B tile of one k-step is one contiguous run.  Gated: nb1 = 2m, the
+    // gate matrix and W1 interleaved by 8 columns (transpose_kernel's row
+    // map).  E4M3 banks: the same moves of bytes; the scales follow their
+    // columns (gated: 8 gate scales, then 8 value scales).
+    const int64_t bk = p.bk_b, nb1 = p.nb1;
+    auto bank1 = [&](auto tag, const void *src, int glu_off) {
+        using T = decltype(tag);
+        launch_transpose<T>(src, bk, p.m, p.N * (p.l / bk), bk * p.m, w1, bk, bk * nb1, s, glu_off);
+    };
     if (p.fp8) {
-        launch_transpose<uint8_t>(w->w1, bk, p.m, p.N * (p.l / bk), bk * p.m, w1, bk, bk * p.m, s);
+        bank1(uint8_t{}, w->w1, p.glu ? 8 : -1);
+        if (p.glu)
+            bank1(uint8_t{}, w->w1_gate, 0);
         launch_transpose<uint8_t>(w->w2, bk, p.l, p.N * (p.m / bk), bk * p.l, w2, bk, bk * p.l, s);
         h->s1 = reinterpret_cast<float *>(base + L.off_s1);
         h->s2 = reinterpret_cast<float *>(base + L.off_s2);
-        hip_check(hipMemcpyAsync(h->s1, w->w1_scale, 4 * p.N * p.m, hipMemcpyDeviceToDevice, s));
+        if (p.glu) {
+            // rows of 8 scales: gate rows to the even 32-byte slots, value rows to the odd ones
+            hip_check(hipMemcpy2DAsync(h->s1, 64, w->w1_gate_scale, 32, 32, p.N * p.m / 8, hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpy2DAsync(reinterpret_cast<char *>(h->s1) + 32, 64, w->w1_scale, 32, 32, p.N * p.m / 8,
+                                       hipMemcpyDeviceToDevice, s));
+        } else {
+            hip_check(hipMemcpyAsync(h->s1, w->w1_scale, 4 * p.N * p.m, hipMemcpyDeviceToDevice, s));
+        }
         hip_check(hipMemcpyAsync(h->s2, w->w2_scale, 4 * p.N * p.l, hipMemcpyDeviceToDevice, s));
     } else {
-        launch_transpose<E>(w->w1, bk, p.m, p.N * (p.l / bk), bk * p.m, w1, bk, bk * p.m, s);
+        bank1(E{}, w->w1, p.glu ? 8 : -1);
+        if (p.glu)
+            bank1(E{}, w->w1_gate, 0);
         launch_transpose<E>(w->w2, bk, p.l, p.N * (p.m / bk), bk * p.l, w2, bk, bk * p.l, s);
     }
     // [W_up ; W2_s] -> [d, l + S m_s]: row i holds W_up[:, i] then W2_s[j][:, i]
@@ -533,7 +565,8 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g.M = T;
     g.N = (int)p.n_x;
     g.K = (int)p.d;
-    g.relu2_from = (int)p.l;
+    g.relu2_from = p.glu ? kNoColumn : (int)p.l;
+    g.glu_from = p.glu ? (int)(p.N + p.l) : kNoColumn;
     g.group_m = 8;
     tm.begin(ST_GEMM_X);
     dense_gemm<E, kTagX>(g, h->partial, h->partial_cap, s);
@@ -581,13 +614,14 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g1.a_bytes = (int64_t)T * p.ld_zh * es;
     g1.B = h->w1T;
     g1.ldb = p.bk_b;
-    g1.b_kstep = p.m * p.bk_b * p.wesize;
-    g1.strideB = p.m * p.l;
+    g1.b_kstep = p.nb1 * p.bk_b * p.wesize;
+    g1.strideB = p.nb1 * p.l;
     g1.C = h->H;
     g1.ldc = p.m;
-    g1.N = (int)p.m;
+    g1.N = (int)p.nb1;
     g1.K = (int)p.l;
-    g1.relu2_from = 0;
+    g1.relu2_from = p.glu ? kNoColumn : 0;
+    g1.glu_from = p.glu ? 0 : kNoColumn;
     g1.gather = h->perm;
     g1.tile_expert = h->tile_expert;
     g1.tile_row0 = h->tile_row0;
@@ -611,7 +645,8 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g2.ldc = p.l;
     g2.N = (int)p.l;
     g2.K = (int)p.m;
-    g2.relu2_from = 1 << 30;
+    g2.relu2_from = kNoColumn;
+    g2.glu_from = kNoColumn;
     g2.gather = nullptr;
     g2.scaleB = h->s2;
     tm.begin(ST_GEMM2);
@@ -638,7 +673,8 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g3.M = T;
     g3.N = (int)p.d;
     g3.K = (int)p.ld_zh;
-    g3.relu2_from = 1 << 30;
+    g3.relu2_from = kNoColumn;
+    g3.glu_from = kNoColumn;
     g3.group_m = 8;
     tm.begin(ST_GEMM_UP);
     dense_gemm<E, kTagUp>(g3, h->partial, h->partial_cap, s);
@@ -724,25 +760,27 @@ int latentmoe_cost(const latentmoe_config *c, latentmoe_cost_out *o)
     const double d = (double)c->d, l = (double)c->l, m = (double)c->m, N = (double)c->n_experts,
                  K = (double)c->top_k, a = (double)c->alpha, S = (double)c->n_shared,
                  ms = c->n_shared > 0 ? (double)c->m_shared : 0.0;
+    // expert matrices: two, or three for gated experts (a gate beside W1)
+    const double em = c->expert_act == LATENTMOE_ACT_SWIGLU ? 3.0 : 2.0;
     std::memset(o, 0, sizeof *o);
-    o->latent_expert_params = 2 * l * m;
-    o->routed_pool_params = N * 2 * l * m;
+    o->latent_expert_params = em * l * m;
+    o->routed_pool_params = N * em * l * m;
     o->projection_params = 2 * d * l;
     o->router_params = d * N;
-    o->shared_params = S * 2 * d * ms;
+    o->shared_params = S * em * d * ms;
     o->layer_params_excl_router = o->routed_pool_params + o->shared_params + o->projection_params;
-    o->active_params_per_token = K * 2 * l * m + o->shared_params + o->projection_params;
-    o->expert_bytes_per_token_fp8 = K * 2 * l * m;
-    o->expert_bytes_per_token_bf16 = K * 2 * l * m * 2;
+    o->active_params_per_token = K * em * l * m + o->shared_params + o->projection_params;
+    o->expert_bytes_per_token_fp8 = K * em * l * m;
+    o->expert_bytes_per_token_bf16 = K * em * l * m * 2;
     o->a2a_bytes_per_token = K * l * (0.5 + 2.0);
-    o->flops_per_token = 2 * (d * N + 2 * d * l + 2 * K * l * m + 2 * S * d * ms);
+    o->flops_per_token = 2 * (d * N + 2 * d * l + em * K * l * m + em * S * d * ms);
     o->log10_combinations = log10_comb(N, K);
     const double Nb = N / a, Kb = c->variant == LATENTMOE_VARIANT_ACC ? K / a : K;
     o->baseline_n_experts = Nb;
     o->baseline_top_k = Kb;
-    o->baseline_expert_params = 2 * d * m;
-    o->baseline_layer_params_excl_router = Nb * 2 * d * m + o->shared_params;
-    o->baseline_active_params_per_token = Kb * 2 * d * m + o->shared_params;
+    o->baseline_expert_params = em * d * m;
+    o->baseline_layer_params_excl_router = Nb * em * d * m + o->shared_params;
+    o->baseline_active_params_per_token = Kb * em * d * m + o->shared_params;
     o->baseline_a2a_bytes_per_token = Kb * d * (0.5 + 2.0);
     o->baseline_log10_combinations = log10_comb(Nb, Kb);
     o->log10_combination_bound = a * o->baseline_log10_combinations;
@@ -765,6 +803,10 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
     if (cfg->has_router_bias && !w->b_router)
         return LATENTMOE_ERR_INVALID_ARGUMENT;
     if (cfg->expert_format == LATENTMOE_EXPERT_FP8_E4M3 && (!w->w1_scale || !w->w2_scale))
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (cfg->expert_act == LATENTMOE_ACT_SWIGLU &&
+        (!w->w1_gate || (cfg->n_shared > 0 && !w->w1_shared_gate) ||
+         (cfg->expert_format == LATENTMOE_EXPERT_FP8_E4M3 && !w->w1_gate_scale)))
         return LATENTMOE_ERR_INVALID_ARGUMENT;
     latentmoe_handle *h = new (std::nothrow) latentmoe_handle();
     if (!h)

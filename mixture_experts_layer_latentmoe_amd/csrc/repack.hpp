@@ -1,7 +1,11 @@
 // Weight repacking at create time: [in, out] row-major -> [out, in] (K
 // contiguous), written into a destination with its own row stride so that
 // several matrices can share one K-contiguous array:
-//   dst[c * dst_ld + r] = src[r * C + c]   for every batch b
+//   dst[row(c) * dst_ld + r] = src[r * C + c]   for every batch b
+// with row(c) = c, or for the two halves of a gated expert's first GEMM
+// (glu_off 0: the gate matrix, 8: the value matrix) row(c) =
+// 16 (c / 8) + c % 8 + glu_off: blocks of 8 gate rows alternate with the 8
+// value rows of the same outputs.
 #pragma once
 
 #include "common.hpp"
@@ -11,7 +15,7 @@ namespace lmoe {
 template <typename E>
 __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ src, int64_t R, int64_t C,
                                                         int64_t src_bstride, E *__restrict__ dst,
-                                                        int64_t dst_ld, int64_t dst_bstride)
+                                                        int64_t dst_ld, int64_t dst_bstride, int glu_off)
 {
     __shared__ E tile[32][33];
     const int64_t b = blockIdx.z;
@@ -27,8 +31,9 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E *__restrict__ sr
     __syncthreads();
     for (int i = ty; i < 32; i += 8) {
         const int64_t c = c0 + i, r = r0 + tx;
+        const int64_t row = glu_off < 0 ? c : 16 * (c >> 3) + (c & 7) + glu_off;
         if (r < R && c < C)
-            d[c * dst_ld + r] = tile[tx][i];
+            d[row * dst_ld + r] = tile[tx][i];
     }
 }
 

@@ -138,11 +138,26 @@ __global__ __launch_bounds__(64 * NW) void skinny_gemm_kernel(const GemmParams p
         const int row = i * 32 + (ln & 31), col = n0 + 8 * g + 4 * (ln >> 5);
         if (row >= p.M || col >= p.N || col - n0 >= COLS)
             continue;
-        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        // gated pairs: n0 and glu_from are multiples of 16, so gate groups
+        // are the even g and their values the next register group
+        const bool glu = col >= p.glu_from;
+        if (glu && (g & 1))
+            continue;
+        float v[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
         for (int w = 0; w < NW; ++w)
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
+            for (int c = 0; c < 4; ++c) {
                 v[c] += red[((w * MT + i) * 16 + 4 * g + c) * 64 + ln];
+                if (glu)
+                    u[c] += red[((w * MT + i) * 16 + 4 * g + 4 + c) * 64 + ln];
+            }
+        if (glu) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                v[c] = glu_value(v[c], u[c]);
+            store4(static_cast<E *>(p.C) + row * p.ldc + glu_out_col(p, col), v[0], v[1], v[2], v[3]);
+            continue;
+        }
         store_out4<E>(p, row, col, v);
     }
 #endif

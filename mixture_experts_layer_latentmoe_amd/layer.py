@@ -44,6 +44,7 @@ class Shape:
     dtype: str
     has_bias: bool
     expert_dtype: Optional[str] = None  # "fp8": W1/W2 are E4M3 bytes with column scales
+    expert_act: str = "relu2"           # "swiglu": gated experts, gate banks w1g / w1g_s
 
 
 class LatentMoE:
@@ -53,7 +54,9 @@ class LatentMoE:
     None), w_down [d,l], w1 [N',l,m], w2 [N',m,l], w_up [l,d],
     w1_s [S,d,m_s], w2_s [S,m_s,d] as float32 or bf16-bit uint16 arrays;
     with ``expert_dtype == "fp8"`` w1/w2 are uint8 E4M3 bytes and
-    w1_scale [N',m], w2_scale [N',l] their float32 column scales.
+    w1_scale [N',m], w2_scale [N',l] their float32 column scales.  With
+    ``expert_act == "swiglu"`` the gate banks w1g [N',l,m] (like w1, with
+    w1g_scale in an FP8 bank) and w1g_s [S,d,m_s] come too.
     """
 
     def __init__(self, shape: Shape, arrays: Dict[str, np.ndarray], max_tokens: int, device="cuda:0"):
@@ -63,20 +66,22 @@ class LatentMoE:
         self.tdtype = _TORCH[shape.dtype]
         self.cfg = _abi.make_config(shape.d, shape.l, shape.m, shape.n_experts, shape.top_k, shape.alpha,
                                     shape.n_shared, shape.m_shared, shape.variant, shape.dtype,
-                                    self.max_tokens, shape.has_bias, shape.expert_dtype)
+                                    self.max_tokens, shape.has_bias, shape.expert_dtype, shape.expert_act)
         fp8 = shape.expert_dtype == "fp8"
-        dev = {}
-        for k in ("w_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s"):
-            if k in ("w1_s", "w2_s") and shape.n_shared == 0:
+        gated = shape.expert_act == "swiglu"
+        dev = {"w1g": None, "w1g_s": None}
+        names = ["w_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s"] + (["w1g", "w1g_s"] if gated else [])
+        for k in names:
+            if k in ("w1_s", "w2_s", "w1g_s") and shape.n_shared == 0:
                 dev[k] = None
                 continue
-            if fp8 and k in ("w1", "w2"):
+            if fp8 and k in ("w1", "w2", "w1g"):
                 dev[k] = torch.from_numpy(np.ascontiguousarray(arrays[k], dtype=np.uint8).copy()).to(self.device)
                 continue
             dev[k] = to_device(arrays[k], shape.dtype, self.device)
-        for k in ("w1_scale", "w2_scale"):
+        for k in ("w1_scale", "w2_scale", "w1g_scale"):
             dev[k] = (torch.from_numpy(np.ascontiguousarray(arrays[k], dtype=np.float32).copy()).to(self.device)
-                      if fp8 else None)
+                      if fp8 and (gated or k != "w1g_scale") else None)
         b = arrays.get("b_router")
         dev["b_router"] = (torch.from_numpy(np.asarray(b, np.float32)).to(self.device)
                            if (shape.has_bias and b is not None) else None)
@@ -86,7 +91,8 @@ class LatentMoE:
 
         w = _abi.latentmoe_weights(ptr(dev["w_router"]), ptr(dev["b_router"]), ptr(dev["w_down"]),
                                    ptr(dev["w1"]), ptr(dev["w2"]), ptr(dev["w_up"]), ptr(dev["w1_s"]),
-                                   ptr(dev["w2_s"]), ptr(dev["w1_scale"]), ptr(dev["w2_scale"]))
+                                   ptr(dev["w2_s"]), ptr(dev["w1_scale"]), ptr(dev["w2_scale"]),
+                                   ptr(dev["w1g"]), ptr(dev["w1g_s"]), ptr(dev["w1g_scale"]))
         with torch.cuda.device(self.device):
             self.handle = _abi.latentmoe_create(self.cfg, w, _stream_ptr(self.device))
         del dev  # create copied the weights
@@ -95,7 +101,7 @@ class LatentMoE:
     def from_workload(cls, wl, max_tokens: Optional[int] = None, device="cuda:0") -> "LatentMoE":
         sh = wl.shape
         s = Shape(sh.d, sh.l, sh.m, sh.n_experts, sh.top_k, sh.alpha, sh.n_shared, sh.m_shared,
-                  sh.variant, sh.dtype, sh.has_bias, sh.expert_dtype)
+                  sh.variant, sh.dtype, sh.has_bias, sh.expert_dtype, sh.expert_act)
         return cls(s, wl.tensors, max_tokens or sh.T, device)
 
     def close(self):

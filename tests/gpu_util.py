@@ -35,6 +35,16 @@ TOL = {"bf16": 2e-2, "f32": 1e-4}   # y: max |err| <= TOL * RMS(reference)
 TOL_NARROW_BF16 = 4e-2
 
 
+# Gated experts, stage H only: h = silu(g) v multiplies two sums that both
+# carry the bf16 rounding of z, so H has heavier relative error than relu^2's
+# h on the |d| / (|ref| + RMS) scale.  The exact emulation of the bf16
+# rounding points (z, H rounded once; sums exact), with no kernel, reaches
+# 2.53e-2 at the shaping-paper widths (l 640, m 512; 300 tokens), where
+# relu^2 experts reach 0.78e-2; the HIP path matches that emulation.  Twice
+# the layer's bar covers it.  y keeps the layer's bar.
+GATED_H_FACTOR = 2.0
+
+
 def tol_for(sh):
     if sh.dtype == "bf16" and sh.name == "custom" and sh.d <= 256:
         return TOL_NARROW_BF16
@@ -177,7 +187,8 @@ def check_stages(out, wl, ref, tokens, decided):
     errs = {k: elem_err(a, b) for k, (a, b) in pairs.items()}
     say("[gpu]   stage errors, max |d| / (|ref| + RMS): " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
-        assert v <= tol, (k, v, tol)
+        t = tol * GATED_H_FACTOR if (k == "h" and sh.expert_act == "swiglu" and sh.dtype == "bf16") else tol
+        assert v <= t, (k, v, t)
     return errs
 
 

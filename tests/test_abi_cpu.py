@@ -33,7 +33,8 @@ def test_library_exports_every_declared_function():
 def _cfg(sh, **over):
     kw = dict(d=sh.d, l=sh.l, m=sh.m, n_experts=sh.n_experts, top_k=sh.top_k, alpha=sh.alpha,
               n_shared=sh.n_shared, m_shared=sh.m_shared, variant=sh.variant, dtype=sh.dtype,
-              max_tokens=sh.T, has_router_bias=sh.has_bias, expert_dtype=sh.expert_dtype)
+              max_tokens=sh.T, has_router_bias=sh.has_bias, expert_dtype=sh.expert_dtype,
+              expert_act=sh.expert_act)
     kw.update(over)
     return _abi.make_config(**kw)
 
@@ -84,6 +85,55 @@ def test_fp8_create_needs_scales_before_any_gpu_call():
     assert h.value is None
 
 
+def test_expert_act_checks():
+    c = _cfg(CONFIGS["readme_acc"])
+    c.expert_act = 2
+    assert _abi.latentmoe_validate_config(c) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
+    assert _abi.latentmoe_validate_config(_cfg(CONFIGS["readme_acc"], expert_act="swiglu")) == _abi.LATENTMOE_OK
+    assert _abi.latentmoe_validate_config(_cfg(CONFIGS["decode_eff_fp8"], expert_act="swiglu")) == _abi.LATENTMOE_OK
+    # the gated bank of one expert ([W_g | W1], 2 l m elements) must stay under 2 GiB
+    big = _cfg(CONFIGS["readme_acc"], d=32768, l=8192, m=65536, n_experts=16, top_k=4, n_shared=0, max_tokens=8)
+    assert _abi.latentmoe_validate_config(big) == _abi.LATENTMOE_OK
+    big.expert_act = _abi.LATENTMOE_ACT_SWIGLU
+    assert _abi.latentmoe_validate_config(big) == _abi.LATENTMOE_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("fp8,shared", [(False, True), (False, False), (True, True)])
+def test_gated_create_needs_gate_banks_before_any_gpu_call(fp8, shared):
+    L = _abi.lib()
+    sh = CONFIGS["decode_eff_fp8" if fp8 else "readme_acc"]
+    cfg = _cfg(sh, expert_act="swiglu", **({} if shared else dict(n_shared=0)))
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: the checks come first
+    sc = fake if fp8 else None
+    full = dict(w_router=fake, w_down=fake, w1=fake, w2=fake, w_up=fake, w1_shared=fake if shared else None,
+                w2_shared=fake if shared else None, w1_scale=sc, w2_scale=sc, w1_gate=fake,
+                w1_shared_gate=fake if shared else None, w1_gate_scale=sc)
+    missing = ["w1_gate"] + (["w1_shared_gate"] if shared else []) + (["w1_gate_scale"] if fp8 else [])
+    for k in missing:
+        kw = dict(full)
+        kw[k] = None
+        w = _abi.latentmoe_weights(**kw)
+        h = ctypes.c_void_p(0)
+        assert L.latentmoe_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(h)) == \
+            _abi.LATENTMOE_ERR_INVALID_ARGUMENT, k
+        assert h.value is None
+
+
+def test_gated_cost_counts_three_matrices():
+    # "three matrices in place of two": every expert term scales by 3/2, the
+    # projections and the router do not
+    sh = CONFIGS["readme_acc"]
+    a = _abi.latentmoe_cost(_cfg(sh))
+    b = _abi.latentmoe_cost(_cfg(sh, expert_act="swiglu"))
+    for k in ("latent_expert_params", "routed_pool_params", "shared_params", "baseline_expert_params",
+              "expert_bytes_per_token_fp8"):
+        assert b[k] == pytest.approx(1.5 * a[k], rel=1e-15), k
+    for k in ("projection_params", "router_params", "a2a_bytes_per_token", "log10_combinations"):
+        assert b[k] == a[k], k
+    assert b["active_params_per_token"] - a["active_params_per_token"] == pytest.approx(
+        0.5 * (a["active_params_per_token"] - a["projection_params"]), rel=1e-15)
+
+
 def test_eff_variant_allows_any_topk():
     assert _abi.latentmoe_validate_config(_cfg(CONFIGS["readme_acc"], top_k=22, variant="eff")) == 0
 
@@ -127,7 +177,7 @@ def test_host_cost_matches_oracle_closed_forms(name):
     sh = CONFIGS[name]
     got = _abi.latentmoe_cost(_cfg(sh))
     ref = ocost.layer_cost(sh.d, sh.l, sh.m, sh.n_experts, sh.top_k, sh.alpha, sh.variant,
-                           sh.n_shared, sh.m_shared)
+                           sh.n_shared, sh.m_shared, matrices=3 if sh.expert_act == "swiglu" else 2)
     pairs = [("latent_expert_params", ref.latent_expert_params),
              ("routed_pool_params", ref.routed_pool_params),
              ("projection_params", ref.projection_params),

@@ -233,3 +233,43 @@ def test_fp8_shape_edge_cases(cfg):
     from tests.helpers import random_fp8_workload
     sh = shape(dtype="bf16", expert_dtype="fp8", **cfg)
     _full_check(random_fp8_workload(sh, seed=cfg["T"]))
+
+
+# --------------------------------------------------------------------------
+# gated (SwiGLU) experts: gate and value columns interleaved by 8 in the B
+# operands, silu(gate) * value in every epilogue
+# --------------------------------------------------------------------------
+def test_swiglu_full_size():
+    _full_check(make_workload(get_config("shape_swiglu")), n_sample=32)
+
+
+@pytest.mark.parametrize("T", [300, 130, 64, 7])
+def test_swiglu_token_counts(T):
+    # 300: 128x128 tiles (staged gated epilogue); 130: split-K x-pass (its
+    # reduce pairs the gate and value groups); 64 and 7: the few-row kernel
+    # with 64 and 32 rows, and the 32-row grouped tiles
+    _full_check(make_workload(get_config("shape_swiglu"), T=T))
+
+
+@pytest.mark.parametrize("cfg", [
+    # x-pass gated columns from 144: the 128-column tile [128, 256) holds
+    # both plain z columns and gated pairs (direct epilogue)
+    dict(T=300, d=256, l=128, m=128, n_experts=16, top_k=4, n_shared=1, m_shared=192, alpha=2),
+    dict(T=70, d=256, l=128, m=128, n_experts=16, top_k=4, n_shared=1, m_shared=192, alpha=2),
+    dict(T=40, d=256, l=128, m=128, n_experts=16, top_k=4, n_shared=1, m_shared=192, alpha=2),
+    dict(T=9, d=128, l=64, m=64, n_experts=32, top_k=8, n_shared=0, m_shared=0, alpha=2),
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_swiglu_shape_edge_cases(cfg, dtype):
+    sh = shape(dtype=dtype, expert_act="swiglu", **cfg)
+    _full_check(random_workload(sh, seed=cfg["T"] + 1))
+
+
+@pytest.mark.parametrize("cfg", [
+    dict(T=96, d=128, l=64, m=192, n_experts=16, top_k=4, n_shared=1, m_shared=64, alpha=2),
+    dict(T=33, d=256, l=128, m=64, n_experts=32, top_k=8, n_shared=0, m_shared=0, alpha=2),
+])
+def test_swiglu_fp8_banks(cfg):
+    from tests.helpers import random_fp8_workload
+    sh = shape(dtype="bf16", expert_dtype="fp8", expert_act="swiglu", **cfg)
+    _full_check(random_fp8_workload(sh, seed=cfg["T"] + 2))
