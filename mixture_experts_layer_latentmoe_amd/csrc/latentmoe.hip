@@ -406,7 +406,8 @@ void launch_skinny(const GemmParams &gp, hipStream_t s)
 }
 
 // Dense GEMMs: 256x256 tiles (8 waves) when they come close to filling the
-// 256 CUs once, 128x128 (4 waves, two workgroups per CU) when those do; up to
+// 256 CUs once, else 128x256 (8 waves, three LDS stages) when those fill it,
+// else 128x128 (4 waves, two workgroups per CU) when those do; up to
 // 64 rows (decode) the few-row kernel (K split over the waves of a
 // workgroup); otherwise up to kSplitKMaxRows rows 64x128 tiles with K split
 // so that ~512 workgroups stream the weights, followed by a fixed-order
@@ -423,8 +424,11 @@ void dense_gemm(const GemmParams &gp, float *partial, int64_t cap_floats, hipStr
             launch_skinny<E, 2, 8, 16, TAG>(gp, s);
         return;
     }
+    const int64_t wide = ((gp.M + 127) / 128) * ((gp.N + 255) / 256);
     if (big >= 192)
         launch_dense<E, 256, 256, 4, 2, 2, TAG>(gp, s);
+    else if (sizeof(E) == 2 && wide >= 256)
+        launch_dense<E, 128, 256, 2, 4, 3, TAG>(gp, s);
     else if (mid >= 256 || gp.M > kSplitKMaxRows)
         launch_dense<E, 128, 128, 2, 2, 2, TAG>(gp, s);
     else
@@ -457,8 +461,10 @@ void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_
     hip_check(hipGetLastError());
 }
 
-// Grouped GEMMs: 128x128 tiles; when experts average few rows (decode),
-// 32x128 tiles with four LDS stages so that more weight bytes are in flight.
+// Grouped GEMMs: 128x256 tiles (8 waves, three LDS stages, one workgroup per
+// CU) when N is a multiple of 256, else 128x128 (two workgroups per CU); when
+// experts average few rows (decode), 32x128 tiles with four LDS stages so
+// that more weight bytes are in flight.
 // fp8: the weights (B) are E4M3 bytes with column scales in gp.scaleB; for few
 // rows, 32x64 tiles of two waves and two stages (small LDS footprint, many
 // workgroups per CU) stream the half-size weights fastest.
@@ -476,6 +482,8 @@ void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hi
     }
     if (bm == kGroupBMSmall)
         launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, false>(gp, max_mtiles, s);
+    else if (sizeof(E) == 2 && gp.N % 256 == 0)
+        launch_grouped<E, kGroupBM, 256, 2, 4, 3, TAG, false>(gp, max_mtiles, s);
     else
         launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG, false>(gp, max_mtiles, s);
 }
