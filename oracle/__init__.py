@@ -23,6 +23,9 @@ permutation equivariance, expert relabelling invariance); every worked
 number of the explainer page for ``cost.py``; and for FP8 (E4M3) expert banks
 the format's defining values, all 256 byte values against torch's
 float8_e4m3fn, equality with the bf16 path at power-of-two scales, and the
-dense brute force with arbitrary per-column scales.  No function here is left
-parity-unpinned.
+dense brute force with arbitrary per-column scales; for gated experts the
+dense brute force with torch's silu and the exact odd/even identities of silu
+under a sign flip of the gate banks; for the backward pass (orc_backward)
+torch autograd on a dense formulation and central finite differences.  No
+function here is left parity-unpinned.
 """

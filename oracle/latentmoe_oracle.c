@@ -447,3 +447,338 @@ int orc_max_threads(void)
     return 1;
 #endif
 }
+
+/* ------------------------------------------------------------------------
+ * Backward pass (the gradient of a scalar loss L through the layer, given
+ * dy = dL/dy).  The routing is piecewise constant in the scores, so no
+ * gradient flows through the top-K' choice; it flows through the gates,
+ * g_k = exp(s_k) / sum_{j in sel} exp(s_j) (the renormalised softmax of
+ * steps 2 and 4), whose Jacobian on the selected experts is
+ * dg_k / ds_j = g_k (delta_kj - g_j) and zero elsewhere:
+ *   ds_j = g_j (dg_j - sum_k g_k dg_k) for j in sel, 0 otherwise.
+ * Every other step is a matrix product or an elementwise map:
+ *   relu(a)^2 has derivative 2 relu(a);
+ *   silu(g) v has partials silu'(g) v and silu(g), with
+ *   silu'(g) = sigma(g) (1 + g (1 - sigma(g))), sigma(g) = 1 / (1 + e^-g).
+ * Products and sums in double in plain index order; expert-bank gradients
+ * are computed for a listed set of experts (their full size would not fit a
+ * test's memory at the named widths).  FP8 banks are not differentiated.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    double *dx;        /* [T, d] */
+    double *dw_router; /* [d, N'] */
+    double *db_router; /* [N'] */
+    double *dw_down;   /* [d, l] */
+    double *dw1;       /* [n_ex, l, m] for the listed experts */
+    double *dw2;       /* [n_ex, m, l] */
+    double *dw1g;      /* [n_ex, l, m] gated only */
+    double *dw_up;     /* [l, d] */
+    double *dw1_s;     /* [S, d, m_s] */
+    double *dw2_s;     /* [S, m_s, d] */
+    double *dw1g_s;    /* [S, d, m_s] gated only */
+} orc_grads;
+
+/* out[i] = sum_j W[off + i*cols + j] v[j]  (the product with W transposed) */
+static void matvec_t(const double *v, const void *W, int64_t off, int64_t rows, int64_t cols, int bf16,
+                     double *out)
+{
+    for (int64_t i = 0; i < rows; ++i) {
+        double acc = 0.0;
+        const int64_t row = off + i * cols;
+        for (int64_t j = 0; j < cols; ++j)
+            acc += ld_elem(W, row + j, bf16) * v[j];
+        out[i] = acc;
+    }
+}
+
+static double sigm(double v) { return 1.0 / (1.0 + exp(-v)); }
+
+/* The expert's hidden layer and its input gradient for one input vector.
+ * relu^2: pre holds a = in W1; gated: pre holds a_g = in W_g and a_v = in W1.
+ * Given dh (gradient of the hidden layer), writes da (gradient of a, or of
+ * a_g and a_v). */
+static void act_forward(int gated, const double *a, const double *ag, int64_t n, double *h)
+{
+    for (int64_t j = 0; j < n; ++j)
+        h[j] = gated ? silu(ag[j]) * a[j] : sq_relu(a[j]);
+}
+
+static void act_backward(int gated, const double *a, const double *ag, const double *dh, int64_t n, double *da,
+                         double *dag)
+{
+    for (int64_t j = 0; j < n; ++j) {
+        if (gated) {
+            const double sg = sigm(ag[j]);
+            da[j] = dh[j] * silu(ag[j]);
+            dag[j] = dh[j] * a[j] * sg * (1.0 + ag[j] * (1.0 - sg));
+        } else {
+            da[j] = a[j] > 0.0 ? dh[j] * 2.0 * a[j] : 0.0;
+        }
+    }
+}
+
+int orc_backward(const orc_shape *c, const orc_tensors *w, int64_t T, const double *dy, const int32_t *experts,
+                 int64_t n_ex, const orc_grads *out, int n_threads)
+{
+    if (check_shape(c) || !w || !dy || !out || T <= 0 || c->expert_fp8 || (n_ex > 0 && !experts))
+        return -1;
+    if (c->gated && (!w->w1g || (c->n_shared > 0 && !w->w1g_s)))
+        return -1;
+    const int64_t d = c->d, l = c->l, m = c->m, ms = c->m_s, S = c->n_shared;
+    const int64_t N = c->n_experts, K = c->top_k;
+    const int bf = c->bf16, gated = c->gated;
+    for (int64_t r = 0; r < n_ex; ++r)
+        if (experts[r] < 0 || experts[r] >= N)
+            return -2;
+#ifdef _OPENMP
+    if (n_threads > 0)
+        omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+    /* per-token quantities kept for the weight gradients */
+    double *X = malloc(sizeof(double) * (size_t)(T * d));
+    double *Z = malloc(sizeof(double) * (size_t)(T * l));
+    double *U = malloc(sizeof(double) * (size_t)(T * l));
+    double *DU = malloc(sizeof(double) * (size_t)(T * l));
+    double *DS = malloc(sizeof(double) * (size_t)(T * N));
+    double *DZ = malloc(sizeof(double) * (size_t)(T * l));
+    double *HS = malloc(sizeof(double) * (size_t)(T * (S * ms + 1)));
+    double *DAS = malloc(sizeof(double) * (size_t)(T * (S * ms + 1)));
+    double *DAGS = malloc(sizeof(double) * (size_t)(T * (S * ms + 1)));
+    int32_t *SEL = malloc(sizeof(int32_t) * (size_t)(T * K));
+    double *G = malloc(sizeof(double) * (size_t)(T * K));
+    int err = (!X || !Z || !U || !DU || !DS || !DZ || !HS || !DAS || !DAGS || !SEL || !G);
+
+    /* phase 1: per token */
+#pragma omp parallel reduction(| : err)
+    {
+        const int64_t wmax = m > ms ? m : ms;
+        double *s = malloc(sizeof(double) * (size_t)N);
+        unsigned char *taken = malloc((size_t)N);
+        double *a = malloc(sizeof(double) * (size_t)wmax);
+        double *ag = malloc(sizeof(double) * (size_t)wmax);
+        double *h = malloc(sizeof(double) * (size_t)wmax);
+        double *dh = malloc(sizeof(double) * (size_t)wmax);
+        double *da = malloc(sizeof(double) * (size_t)wmax);
+        double *dag = malloc(sizeof(double) * (size_t)wmax);
+        double *o = malloc(sizeof(double) * (size_t)(K * l));
+        double *dg = malloc(sizeof(double) * (size_t)K);
+        double *tmp = malloc(sizeof(double) * (size_t)(d > l ? d : l));
+        if (!s || !taken || !a || !ag || !h || !dh || !da || !dag || !o || !dg || !tmp)
+            err |= 1;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t) {
+            if (err)
+                continue;
+            double *x = X + t * d, *z = Z + t * l, *u = U + t * l, *du = DU + t * l, *dz = DZ + t * l;
+            const double *dyt = dy + t * d;
+            int32_t *sel = SEL + t * K;
+            double *g = G + t * K;
+            for (int64_t i = 0; i < d; ++i)
+                x[i] = ld_elem(w->x, t * d + i, bf);
+            matvec(x, w->w_router, 0, d, N, bf, s);
+            if (c->has_bias && w->b_router)
+                for (int64_t e = 0; e < N; ++e)
+                    s[e] += (double)w->b_router[e];
+            if (select_topk(s, N, K, sel, taken)) {
+                err |= 4;
+                continue;
+            }
+            gates(s, N, sel, K, g);
+            matvec(x, w->w_down, 0, d, l, bf, z);
+            /* forward of the routed experts, keeping each slot's output */
+            for (int64_t j = 0; j < l; ++j)
+                u[j] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t e = sel[k];
+                matvec(z, w->w1, e * l * m, l, m, bf, a);
+                if (gated)
+                    matvec(z, w->w1g, e * l * m, l, m, bf, ag);
+                act_forward(gated, a, ag, m, h);
+                matvec(h, w->w2, e * m * l, m, l, bf, o + k * l);
+                for (int64_t j = 0; j < l; ++j)
+                    u[j] += g[k] * o[k * l + j];
+            }
+            /* y = u W_up + shared: du = dy W_up^T */
+            matvec_t(dyt, w->w_up, 0, l, d, bf, du);
+            /* gates and scores */
+            double gdg = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < l; ++j)
+                    acc += du[j] * o[k * l + j];
+                dg[k] = acc;
+                gdg += g[k] * acc;
+            }
+            double *ds = DS + t * N;
+            for (int64_t e = 0; e < N; ++e)
+                ds[e] = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                ds[sel[k]] = g[k] * (dg[k] - gdg);
+            /* back through the routed experts into z */
+            for (int64_t j = 0; j < l; ++j)
+                dz[j] = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t e = sel[k];
+                matvec(z, w->w1, e * l * m, l, m, bf, a);
+                if (gated)
+                    matvec(z, w->w1g, e * l * m, l, m, bf, ag);
+                for (int64_t j = 0; j < l; ++j)
+                    tmp[j] = g[k] * du[j]; /* gradient of slot k's output */
+                matvec_t(tmp, w->w2, e * m * l, m, l, bf, dh);
+                act_backward(gated, a, ag, dh, m, da, dag);
+                matvec_t(da, w->w1, e * l * m, l, m, bf, tmp);
+                for (int64_t j = 0; j < l; ++j)
+                    dz[j] += tmp[j];
+                if (gated) {
+                    matvec_t(dag, w->w1g, e * l * m, l, m, bf, tmp);
+                    for (int64_t j = 0; j < l; ++j)
+                        dz[j] += tmp[j];
+                }
+            }
+            /* dx = ds W_r^T + dz W_down^T + shared */
+            double *dx = out->dx ? out->dx + t * d : NULL;
+            if (dx) {
+                matvec_t(ds, w->w_router, 0, d, N, bf, dx);
+                matvec_t(dz, w->w_down, 0, d, l, bf, tmp);
+                for (int64_t i = 0; i < d; ++i)
+                    dx[i] += tmp[i];
+            }
+            for (int64_t sh = 0; sh < S; ++sh) {
+                double *hs = HS + t * S * ms + sh * ms, *das = DAS + t * S * ms + sh * ms;
+                double *dags = DAGS + t * S * ms + sh * ms;
+                matvec(x, w->w1_s, sh * d * ms, d, ms, bf, a);
+                if (gated)
+                    matvec(x, w->w1g_s, sh * d * ms, d, ms, bf, ag);
+                act_forward(gated, a, ag, ms, hs);
+                matvec_t(dyt, w->w2_s, sh * ms * d, ms, d, bf, dh);
+                act_backward(gated, a, ag, dh, ms, das, dags);
+                if (dx) {
+                    matvec_t(das, w->w1_s, sh * d * ms, d, ms, bf, tmp);
+                    for (int64_t i = 0; i < d; ++i)
+                        dx[i] += tmp[i];
+                    if (gated) {
+                        matvec_t(dags, w->w1g_s, sh * d * ms, d, ms, bf, tmp);
+                        for (int64_t i = 0; i < d; ++i)
+                            dx[i] += tmp[i];
+                    }
+                }
+            }
+        }
+        free(s); free(taken); free(a); free(ag); free(h); free(dh); free(da); free(dag); free(o); free(dg);
+        free(tmp);
+    }
+
+    /* phase 2: dense weight gradients, sums over tokens in token order */
+    if (!err) {
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t i = 0; i < d; ++i) {
+            for (int64_t e = 0; e < N && out->dw_router; ++e) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    acc += X[t * d + i] * DS[t * N + e];
+                out->dw_router[i * N + e] = acc;
+            }
+            for (int64_t j = 0; j < l && out->dw_down; ++j) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    acc += X[t * d + i] * DZ[t * l + j];
+                out->dw_down[i * l + j] = acc;
+            }
+            for (int64_t sh = 0; sh < S; ++sh)
+                for (int64_t j = 0; j < ms; ++j) {
+                    double acc = 0.0, accg = 0.0;
+                    for (int64_t t = 0; t < T; ++t) {
+                        acc += X[t * d + i] * DAS[t * S * ms + sh * ms + j];
+                        accg += X[t * d + i] * DAGS[t * S * ms + sh * ms + j];
+                    }
+                    if (out->dw1_s)
+                        out->dw1_s[(sh * d + i) * ms + j] = acc;
+                    if (gated && out->dw1g_s)
+                        out->dw1g_s[(sh * d + i) * ms + j] = accg;
+                }
+        }
+        if (out->db_router)
+            for (int64_t e = 0; e < N; ++e) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    acc += DS[t * N + e];
+                out->db_router[e] = acc;
+            }
+#pragma omp parallel for schedule(dynamic, 4)
+        for (int64_t i = 0; i < l; ++i)
+            for (int64_t j = 0; j < d && out->dw_up; ++j) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < T; ++t)
+                    acc += U[t * l + i] * dy[t * d + j];
+                out->dw_up[i * d + j] = acc;
+            }
+        if (out->dw2_s) {
+#pragma omp parallel for schedule(dynamic, 4)
+            for (int64_t r = 0; r < S * ms; ++r) {
+                const int64_t sh = r / ms, j = r % ms;
+                for (int64_t i = 0; i < d; ++i) {
+                    double acc = 0.0;
+                    for (int64_t t = 0; t < T; ++t)
+                        acc += HS[t * S * ms + sh * ms + j] * dy[t * d + i];
+                    out->dw2_s[(sh * ms + j) * d + i] = acc;
+                }
+            }
+        }
+    }
+
+    /* phase 3: expert-bank gradients of the listed experts, tokens in order */
+    if (!err && n_ex > 0 && (out->dw1 || out->dw2 || (gated && out->dw1g))) {
+#pragma omp parallel reduction(| : err)
+        {
+            double *a = malloc(sizeof(double) * (size_t)m), *ag = malloc(sizeof(double) * (size_t)m);
+            double *h = malloc(sizeof(double) * (size_t)m), *dh = malloc(sizeof(double) * (size_t)m);
+            double *da = malloc(sizeof(double) * (size_t)m), *dag = malloc(sizeof(double) * (size_t)m);
+            double *go = malloc(sizeof(double) * (size_t)l);
+            if (!a || !ag || !h || !dh || !da || !dag || !go)
+                err |= 1;
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n_ex; ++r) {
+                if (err)
+                    continue;
+                const int64_t e = experts[r];
+                double *w1g_out = (gated && out->dw1g) ? out->dw1g + r * l * m : NULL;
+                if (out->dw1)
+                    memset(out->dw1 + r * l * m, 0, sizeof(double) * (size_t)(l * m));
+                if (out->dw2)
+                    memset(out->dw2 + r * m * l, 0, sizeof(double) * (size_t)(m * l));
+                if (w1g_out)
+                    memset(w1g_out, 0, sizeof(double) * (size_t)(l * m));
+                for (int64_t t = 0; t < T; ++t)
+                    for (int64_t k = 0; k < K; ++k) {
+                        if (SEL[t * K + k] != e)
+                            continue;
+                        const double *z = Z + t * l;
+                        matvec(z, w->w1, e * l * m, l, m, bf, a);
+                        if (gated)
+                            matvec(z, w->w1g, e * l * m, l, m, bf, ag);
+                        act_forward(gated, a, ag, m, h);
+                        for (int64_t j = 0; j < l; ++j)
+                            go[j] = G[t * K + k] * DU[t * l + j];
+                        if (out->dw2)
+                            for (int64_t i = 0; i < m; ++i)
+                                for (int64_t j = 0; j < l; ++j)
+                                    out->dw2[(r * m + i) * l + j] += h[i] * go[j];
+                        matvec_t(go, w->w2, e * m * l, m, l, bf, dh);
+                        act_backward(gated, a, ag, dh, m, da, dag);
+                        for (int64_t i = 0; i < l; ++i)
+                            for (int64_t j = 0; j < m; ++j) {
+                                if (out->dw1)
+                                    out->dw1[(r * l + i) * m + j] += z[i] * da[j];
+                                if (w1g_out)
+                                    w1g_out[i * m + j] += z[i] * dag[j];
+                            }
+                    }
+            }
+            free(a); free(ag); free(h); free(dh); free(da); free(dag); free(go);
+        }
+    }
+    free(X); free(Z); free(U); free(DU); free(DS); free(DZ); free(HS); free(DAS); free(DAGS); free(SEL); free(G);
+    return err ? -3 : 0;
+}

@@ -207,3 +207,54 @@ def fp8_decode(q: np.ndarray) -> np.ndarray:
     if rc != 0:
         raise RuntimeError("orc_fp8_decode failed")
     return out
+
+
+class _Grads(C.Structure):
+    _fields_ = [(n, _vp) for n in ("dx", "dw_router", "db_router", "dw_down", "dw1", "dw2", "dw1g",
+                                   "dw_up", "dw1_s", "dw2_s", "dw1g_s")]
+
+
+def backward(wl, dy: np.ndarray, experts: Optional[Sequence[int]] = None, n_threads: int = 0) -> dict:
+    """Gradients of a loss L through the layer of workload ``wl`` given
+    dy = dL/dy [T, d] (float64), over all T tokens.  Returns dx and every
+    weight gradient in float64, in the weights' [in, out] layouts; the
+    expert banks' gradients (dw1, dw2, and dw1g when gated) only for
+    ``experts`` (default: all), stacked in that order."""
+    sh = wl.shape
+    if sh.expert_dtype == "fp8":
+        raise ValueError("FP8 expert banks are not differentiated")
+    bf16 = sh.dtype == "bf16"
+    gated = sh.expert_act == "swiglu"
+    T, N, K, l, m, d = sh.T, sh.n_experts, sh.top_k, sh.l, sh.m, sh.d
+    S, ms = sh.n_shared, sh.m_shared
+    ex = np.arange(N, dtype=np.int32) if experts is None else np.asarray(experts, dtype=np.int32)
+    t = {k: (None if wl.tensors.get(k) is None else _storage(wl.tensors[k], bf16))
+         for k in ("x", "w_router", "w_down", "w1", "w2", "w_up", "w1_s", "w2_s")}
+    t["w1g"] = _storage(wl.tensors["w1g"], bf16) if gated else None
+    t["w1g_s"] = _storage(wl.tensors["w1g_s"], bf16) if (gated and S > 0) else None
+    b = wl.tensors.get("b_router")
+    if b is not None:
+        b = np.ascontiguousarray(b, dtype=np.float32)
+    dyd = np.ascontiguousarray(dy, dtype=np.float64)
+    assert dyd.shape == (T, d)
+    shapes = {"dx": (T, d), "dw_router": (d, N), "db_router": (N,), "dw_down": (d, l),
+              "dw1": (len(ex), l, m), "dw2": (len(ex), m, l), "dw_up": (l, d),
+              "dw1_s": (S, d, ms), "dw2_s": (S, ms, d)}
+    if gated:
+        shapes.update({"dw1g": (len(ex), l, m), "dw1g_s": (S, d, ms)})
+    res = {k: np.zeros(v) for k, v in shapes.items()}
+    g = _Grads(*[res[k].ctypes.data if k in res else None for k, _ in _Grads._fields_])
+    cs = _Shape(d, l, m, ms if S > 0 else 0, S, N, K, 1 if bf16 else 0,
+                1 if (sh.has_bias and b is not None) else 0, 0, 1 if gated else 0)
+    ct = _Tensors(_ptr(t["x"]), _ptr(t["w_router"]), _ptr(b), _ptr(t["w_down"]), _ptr(t["w1"]), _ptr(t["w2"]),
+                  _ptr(t["w_up"]), _ptr(t["w1_s"]) if S > 0 else None, _ptr(t["w2_s"]) if S > 0 else None,
+                  None, None, _ptr(t["w1g"]), _ptr(t["w1g_s"]), None)
+    L = lib()
+    L.orc_backward.argtypes = [C.POINTER(_Shape), C.POINTER(_Tensors), _i64, _vp, _vp, _i64,
+                               C.POINTER(_Grads), C.c_int]
+    L.orc_backward.restype = C.c_int
+    rc = L.orc_backward(C.byref(cs), C.byref(ct), T, dyd.ctypes.data, ex.ctypes.data, len(ex), C.byref(g),
+                        int(n_threads))
+    if rc != 0:
+        raise RuntimeError(f"orc_backward failed with {rc}")
+    return res
