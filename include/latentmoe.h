@@ -172,6 +172,39 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w,
 int latentmoe_forward(latentmoe_handle *h, const void *x, void *y, int64_t T,
                       void *hip_stream, const latentmoe_debug *dbg);
 
+/* Gradients of a scalar loss L through the layer (device pointers; NULL
+ * skips that gradient).  Weight gradients are fp32 in the weights' own
+ * [in, out] layouts and are written, not accumulated; dx has the config
+ * dtype.  P = T * K'. */
+typedef struct latentmoe_grads {
+    void *dx;               /* [T, d] E */
+    float *dw_router;       /* [d, N'] */
+    float *db_router;       /* [N'] (layers with a router bias) */
+    float *dw_down;         /* [d, l] */
+    float *dw1;             /* [N', l, m] */
+    float *dw2;             /* [N', m, l] */
+    float *dw_up;           /* [l, d] */
+    float *dw1_shared;      /* [S, d, m_shared] */
+    float *dw2_shared;      /* [S, m_shared, d] */
+    float *dw1_gate;        /* [N', l, m] SWIGLU only */
+    float *dw1_shared_gate; /* [S, d, m_shared] SWIGLU only */
+} latentmoe_grads;
+
+/* The layer's backward pass at input x[T, d] for dy = dL/dy [T, d] (both
+ * device buffers of the config dtype): dx and the weight gradients.  The
+ * top-K' choice is piecewise constant in the scores and passes no gradient;
+ * it flows through the gates, the softmax renormalised over the selected
+ * experts (explainer, MoE code block), and through every matrix product and
+ * activation of the forward.  The forward is recomputed inside the call.
+ * Asynchronous on hip_stream like latentmoe_forward, and deterministic.  The
+ * first call on a handle allocates its backward workspace and the weight
+ * layouts the backward products read (about one more copy of the weights).
+ * Errors: LATENTMOE_ERR_UNSUPPORTED for FP8 expert banks;
+ * LATENTMOE_ERR_INVALID_ARGUMENT for null handle/x/dy/g, T out of range, or
+ * a router-bias gradient asked of a layer without one. */
+int latentmoe_backward(latentmoe_handle *h, const void *x, const void *dy, int64_t T, void *hip_stream,
+                       const latentmoe_grads *g);
+
 /* Free the handle and everything it owns (NULL is a no-op).  The caller
  * must ensure no forward is still running on it. */
 int latentmoe_destroy(latentmoe_handle *h);

@@ -21,7 +21,8 @@ LATENTMOE_EXPERT_AS_DTYPE, LATENTMOE_EXPERT_FP8_E4M3 = 0, 1
 LATENTMOE_ACT_RELU2, LATENTMOE_ACT_SWIGLU = 0, 1
 LATENTMOE_MAX_STAGES = 16
 
-EXPORTED = ("latentmoe_create", "latentmoe_forward", "latentmoe_destroy", "latentmoe_validate_config",
+EXPORTED = ("latentmoe_create", "latentmoe_forward", "latentmoe_backward", "latentmoe_destroy",
+            "latentmoe_validate_config",
             "latentmoe_workspace_bytes", "latentmoe_cost", "latentmoe_status_string",
             "latentmoe_last_hip_error", "latentmoe_profile_begin", "latentmoe_profile_end",
             "latentmoe_stage_name")
@@ -43,6 +44,11 @@ class latentmoe_weights(C.Structure):
 class latentmoe_debug(C.Structure):
     _fields_ = [(n, _vp) for n in ("logits", "idx", "gate", "counts", "offsets", "perm_token",
                                    "pos", "z", "h_shared", "h", "y_perm", "u")]
+
+
+class latentmoe_grads(C.Structure):
+    _fields_ = [(n, _vp) for n in ("dx", "dw_router", "db_router", "dw_down", "dw1", "dw2", "dw_up",
+                                   "dw1_shared", "dw2_shared", "dw1_gate", "dw1_shared_gate")]
 
 
 _COST_FIELDS = ("latent_expert_params", "routed_pool_params", "projection_params", "router_params",
@@ -86,6 +92,7 @@ def lib():
         P = C.POINTER
         L.latentmoe_create.argtypes = [P(latentmoe_config), P(latentmoe_weights), _vp, P(_vp)]
         L.latentmoe_forward.argtypes = [_vp, _vp, _vp, _i64, _vp, P(latentmoe_debug)]
+        L.latentmoe_backward.argtypes = [_vp, _vp, _vp, _i64, _vp, P(latentmoe_grads)]
         L.latentmoe_destroy.argtypes = [_vp]
         L.latentmoe_validate_config.argtypes = [P(latentmoe_config)]
         L.latentmoe_workspace_bytes.argtypes = [P(latentmoe_config), P(_i64)]
@@ -150,6 +157,11 @@ def latentmoe_forward(handle: int, x_ptr: int, y_ptr: int, T: int, stream: int,
                       dbg: latentmoe_debug = None) -> None:
     _check("latentmoe_forward", lib().latentmoe_forward(_vp(handle), _vp(x_ptr), _vp(y_ptr), int(T),
                                                         _vp(stream), C.byref(dbg) if dbg is not None else None))
+
+
+def latentmoe_backward(handle: int, x_ptr: int, dy_ptr: int, T: int, stream: int, grads: latentmoe_grads) -> None:
+    _check("latentmoe_backward", lib().latentmoe_backward(_vp(handle), _vp(x_ptr), _vp(dy_ptr), int(T),
+                                                          _vp(stream), C.byref(grads)))
 
 
 def latentmoe_destroy(handle: int) -> None:

@@ -73,6 +73,12 @@ struct GemmParams {
     const float *scaleB;     // grouped, E4M3 B: [N'][N] scale of each expert's output column
     // dense, few rows: B again in fragment-major 1 KiB blocks (fragmajor_kernel)
     const void *Bfrag;
+    // dense, batched K (weight gradients of the experts): n_batches products
+    // share A and B and differ in their K range: batch e sums over
+    // [k_offsets[e], k_offsets[e + 1]) (elements, multiples of the k-tile;
+    // an empty range gives zeros) and writes output rows e M .. e M + M - 1
+    const int *k_offsets;
+    int n_batches;
 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -107,6 +113,7 @@ template <int N> __device__ __forceinline__ void wait_vm_lgkm0()
 struct TileInfo {
     int n0, rows_valid, expert, split;
     int64_t row_base;
+    int64_t c_row0;  // added to the output rows (batched K: e M)
 };
 
 // Logical tile t (no split-K) -> output tile.  Grouped: t walks the device
@@ -118,6 +125,7 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int t, int ntn,
     int tm, tn;
     ti.expert = 0;
     ti.split = 0;
+    ti.c_row0 = 0;
     if constexpr (GROUPED) {
         tm = t / ntn;
         tn = t - tm * ntn;
@@ -153,6 +161,15 @@ __device__ __forceinline__ bool locate_tile(const GemmParams &p, TileInfo &ti)
         if (t < 0)
             return false;
         tile_coords<BM, BN, true>(p, t, ntn, ti);
+    } else if (p.k_offsets) {
+        const int ntm = (p.M + BM - 1) / BM, per = ntm * ntn;
+        const int t = xcd_logical_tile(blockIdx.x, p.n_batches * per);
+        if (t < 0)
+            return false;
+        const int e = t / per;
+        tile_coords<BM, BN, false>(p, t - e * per, ntn, ti);
+        ti.expert = e;
+        ti.c_row0 = (int64_t)e * p.M;
     } else {
         const int ntm = (p.M + BM - 1) / BM;
         const int S = p.splitk > 1 ? p.splitk : 1;
@@ -545,7 +562,12 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         kt0 = split * per;
         nkl = min(per, nkl - kt0);
     }
-    tile_dma<NIA, NIB, NW>(sA0, sB0, true, kt0, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
+    if (!GROUPED && p.k_offsets) {
+        kt0 = p.k_offsets[expert] / BK;
+        nkl = p.k_offsets[expert + 1] / BK - kt0;
+    }
+    const int64_t c_row_base = row_base + ti.c_row0;  // first output row of the tile
+    tile_dma<NIA, NIB, NW>(sA0, sB0, nkl > 0, kt0, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
     if constexpr (NS > 2)
         tile_dma<NIA, NIB, NW>(sA1, sB1, nkl > 1, kt0 + 1, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
     if constexpr (NS > 3)
@@ -569,7 +591,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     }
 
     int j = 0;
-    if constexpr (NS == 2) {
+    if (nkl <= 0) {
+        // an empty K range: the products are zero
+    } else if constexpr (NS == 2) {
         for (;;) {
             LMOE_KSTEP(sA0, sB0, sA1, sB1)
             LMOE_KSTEP(sA1, sB1, sA0, sB0)
@@ -616,7 +640,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     // fp32 outputs, and tiles that hold router columns or straddle the start
     // of the gated pairs: straight from the registers
     if (sizeof(E) != 2 || n0 < p.c_split || (n0 < p.glu_from && n0 + BN > p.glu_from)) {
-        store_tile_direct<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, cs);
+        store_tile_direct<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, cs);
         return;
     }
     if constexpr (sizeof(E) == 2) {
@@ -631,9 +655,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         __builtin_amdgcn_s_barrier();
         uint4 *stg = (IN_A ? (wave < PER_ARR ? sA0 : sA1) : (wave < PER_ARR ? sB0 : sB1)) + (wave % PER_ARR) * WAVE_U;
         if (n0 >= p.glu_from)
-            store_tile_staged_glu<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg, cs);
+            store_tile_staged_glu<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg, cs);
         else
-            store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, row_base, rows_valid, n0, wm, wn, lane, stg, cs);
+            store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg, cs);
     }
 #endif
 }

@@ -38,6 +38,7 @@
 #include "repack.hpp"
 #include "router.hpp"
 #include "skinny.hpp"
+#include "backward.hpp"
 
 using namespace lmoe;
 
@@ -123,6 +124,20 @@ struct latentmoe_handle {
     uint32_t prof_mask = 0;  // stages timed
     std::vector<hipEvent_t> ev;  // [prof_cap][ST_COUNT][2]
     std::vector<int> ev_used;    // [prof_cap][ST_COUNT]
+    // backward pass (allocated by its first call)
+    void *bwbuf = nullptr;  // weight layouts of the backward products
+    void *bws = nullptr;    // backward workspace
+    void *wx_o = nullptr, *wx_of = nullptr;  // [d, n_x] = Wx (rows K = n_x contiguous) + fragment-major copy
+    void *wu_o = nullptr, *wu_of = nullptr;  // [l + S m_s, d] = [W_up ; W2_s] + fragment-major copy
+    void *w1b = nullptr, *w2b = nullptr;     // per expert [nb1 / bk][l][bk], [l / bk][m][bk]
+    void *XA = nullptr;   // [Tmax, l + g S m_s] raw x-pass output (z, shared pre-activations)
+    float *Apre = nullptr;  // [Pmax, nb1] routed pre-activations
+    void *dUH = nullptr, *dYp = nullptr, *dH = nullptr, *dA = nullptr, *dzp = nullptr, *dX = nullptr;
+    void *xT = nullptr, *dXT = nullptr, *zhT = nullptr, *dyT = nullptr;
+    void *HT = nullptr, *dYpT = nullptr, *zpT = nullptr, *dAT = nullptr;
+    int *koff = nullptr;
+    float *dWx = nullptr, *dWu = nullptr, *dW1g = nullptr;
+    int64_t Tpad = 0, Ppad = 0;
 };
 
 namespace {
@@ -374,7 +389,7 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
 // ---- kernel launch helpers -------------------------------------------------
 
 // GEMM stage tags (one kernel symbol per layer stage)
-constexpr int kTagX = 0, kTagG1 = 1, kTagG2 = 2, kTagUp = 3;
+constexpr int kTagX = 0, kTagG1 = 1, kTagG2 = 2, kTagUp = 3, kTagBwd = 4;
 
 template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG>
 void launch_dense(const GemmParams &gp, hipStream_t s)
@@ -542,8 +557,13 @@ void copy2d(void *dst, int64_t dst_pitch, const void *src, int64_t src_pitch, in
     hip_check(hipMemcpy2DAsync(dst, dst_pitch, src, src_pitch, width, rows, hipMemcpyDeviceToDevice, s));
 }
 
+// train: the forward the backward pass recomputes.  The x-pass writes its
+// raw output (z and the shared pre-activations) to XA and grouped GEMM 1 its
+// pre-activations in fp32 to Apre; small kernels then form h_s and H.  u
+// ends in zh beside h_s; y is not formed.
 template <typename E>
-void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_t s, const latentmoe_debug *dbg)
+void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_t s, const latentmoe_debug *dbg,
+                  bool train = false)
 {
     const Plan &p = h->plan;
     const int N = (int)p.N, K = (int)p.K;
@@ -576,8 +596,22 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g.relu2_from = p.glu ? kNoColumn : (int)p.l;
     g.glu_from = p.glu ? (int)(p.N + p.l) : kNoColumn;
     g.group_m = 8;
+    const int64_t ld_xa = p.n_x - p.N;  // l + g S m_s
+    if (train) {
+        g.C = h->XA;
+        g.ldc = ld_xa;
+        g.relu2_from = kNoColumn;
+        g.glu_from = kNoColumn;
+    }
     tm.begin(ST_GEMM_X);
     dense_gemm<E, kTagX>(g, h->partial, h->partial_cap, s);
+    if (train) {
+        const int64_t n = (int64_t)T * p.ld_zh;
+        xpass_act_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+            static_cast<const E *>(h->XA), ld_xa, T, (int)p.l, (int)(p.S * p.ms), p.glu ? 1 : 0,
+            static_cast<E *>(h->zh), p.ld_zh);
+        hip_check(hipGetLastError());
+    }
     tm.end(ST_GEMM_X);
     if (dbg && dbg->logits)
         hip_check(hipMemcpyAsync(dbg->logits, h->logits, 4 * (size_t)T * N, hipMemcpyDeviceToDevice, s));
@@ -636,8 +670,20 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g1.n_mtiles = h->n_mtiles;
     g1.offsets = h->offsets;
     g1.scaleB = h->s1;
+    if (train) {  // raw pre-activations, fp32
+        g1.C32 = h->Apre;
+        g1.ldc32 = p.nb1;
+        g1.c_split = (int)p.nb1;
+        g1.relu2_from = kNoColumn;
+        g1.glu_from = kNoColumn;
+    }
     tm.begin(ST_GEMM1);
     grouped_gemm<E, kTagG1>(g1, max_mt, gbm, p.fp8, s);
+    if (train) {
+        expert_act_kernel<E><<<dim3((unsigned)((P * p.m + 255) / 256)), dim3(256), 0, s>>>(
+            h->Apre, P, (int)p.m, (int)p.nb1, p.glu ? 1 : 0, static_cast<E *>(h->H));
+        hip_check(hipGetLastError());
+    }
     tm.end(ST_GEMM1);
 
     // 6: Y = H W2_e
@@ -657,6 +703,8 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g2.glu_from = kNoColumn;
     g2.gather = nullptr;
     g2.scaleB = h->s2;
+    g2.C32 = nullptr;
+    g2.c_split = 0;
     tm.begin(ST_GEMM2);
     grouped_gemm<E, kTagG2>(g2, max_mt, gbm, p.fp8, s);
     tm.end(ST_GEMM2);
@@ -667,6 +715,8 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
         static_cast<const E *>(h->Yp), h->pos, h->gate, T, K, (int)p.l, static_cast<E *>(h->zh), p.ld_zh);
     hip_check(hipGetLastError());
     tm.end(ST_COMBINE);
+    if (train)
+        return;
 
     // 8: y = [u | h_s] [W_up ; W2_s]
     GemmParams g3{};
@@ -721,10 +771,360 @@ void free_handle(latentmoe_handle *h)
         (void)hipFree(h->wbuf);
     if (h->ws)
         (void)hipFree(h->ws);
+    if (h->bwbuf)
+        (void)hipFree(h->bwbuf);
+    if (h->bws)
+        (void)hipFree(h->bws);
     delete h;
 }
 
 double log10_comb(double n, double k) { return (std::lgamma(n + 1) - std::lgamma(k + 1) - std::lgamma(n - k + 1)) / std::log(10.0); }
+
+// ---- backward pass -----------------------------------------------------
+
+template <typename E, int TAG>
+void launch_batched_k(const GemmParams &gp, hipStream_t s)
+{
+    constexpr int BM = 128, BN = 128;
+    const int64_t tiles = (int64_t)gp.n_batches * ((gp.M + BM - 1) / BM) * ((gp.N + BN - 1) / BN);
+    gemm_kernel<E, BM, BN, 2, 2, 2, false, 1, TAG><<<dim3((unsigned)align_up(tiles, 8)), dim3(256), 0, s>>>(gp);
+    hip_check(hipGetLastError());
+}
+
+template <typename E>
+void launch_pad_transpose(const void *src, int64_t ld_src, int rows, int C, const int *gather, const int *offs,
+                          const int *koff, int nseg, void *dst, int64_t ld_dst, hipStream_t s)
+{
+    dim3 grid((unsigned)((C + 31) / 32), (unsigned)(ld_dst / 32));
+    pad_transpose_kernel<E><<<grid, dim3(256), 0, s>>>(static_cast<const E *>(src), ld_src, rows, C, gather, offs,
+                                                       koff, nseg, static_cast<E *>(dst), ld_dst);
+    hip_check(hipGetLastError());
+}
+
+int64_t n_x_padded(const Plan &p) { return align_up(p.n_x, 64); }
+
+// Bytes of the backward's weight layouts and workspace.
+struct BwdLayout {
+    int64_t off_wx, off_wxf, off_wu, off_wuf, off_w1b, off_w2b, wtotal;
+    int64_t off_xa, off_apre, off_duh, off_dyp, off_dh, off_da, off_dzp, off_dx, off_xt, off_dxt, off_zht, off_dyt,
+        off_ht, off_dypt, off_zpt, off_dat, off_koff, off_dwx, off_dwu, off_dw1g, total;
+    int64_t Tpad, Ppad;
+};
+
+BwdLayout bwd_layout(const Plan &p)
+{
+    BwdLayout L{};
+    const int64_t es = p.esize, nxp = n_x_padded(p), ldxa = p.n_x - p.N;
+    int64_t o = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = o;
+        o = align_up(o + bytes, 256);
+        return at;
+    };
+    L.off_wx = take(es * p.d * nxp);
+    L.off_wxf = take(es * align_up(p.d, 32) * nxp);
+    L.off_wu = take(es * p.ld_zh * p.d);
+    L.off_wuf = take(es * align_up(p.ld_zh, 32) * p.d);
+    L.off_w1b = take(es * p.N * p.l * p.nb1);
+    L.off_w2b = take(es * p.N * p.m * p.l);
+    L.wtotal = o;
+    o = 0;
+    L.Tpad = align_up(p.Tmax, 64);
+    L.Ppad = align_up(p.P_max + 64 * p.N, 64);  // >= sum over experts of their rows rounded up to 64
+    L.off_xa = take(es * p.Tmax * ldxa);
+    L.off_apre = take(4 * p.P_max * p.nb1);
+    L.off_duh = take(es * p.Tmax * p.ld_zh);
+    L.off_dyp = take(es * p.P_max * p.l);
+    L.off_dh = take(es * p.P_max * p.m);
+    L.off_da = take(es * p.P_max * p.nb1);
+    L.off_dzp = take(es * p.P_max * p.l);
+    L.off_dx = take(es * p.Tmax * nxp);
+    L.off_xt = take(es * p.d * L.Tpad);
+    L.off_dxt = take(es * nxp * L.Tpad);
+    L.off_zht = take(es * p.ld_zh * L.Tpad);
+    L.off_dyt = take(es * p.d * L.Tpad);
+    L.off_ht = take(es * p.m * L.Ppad);
+    L.off_dypt = take(es * p.l * L.Ppad);
+    L.off_zpt = take(es * p.l * L.Ppad);
+    L.off_dat = take(es * p.nb1 * L.Ppad);
+    L.off_koff = take(4 * (p.N + 1));
+    L.off_dwx = take(4 * p.d * p.n_x);
+    L.off_dwu = take(4 * p.ld_zh * p.d);
+    L.off_dw1g = take(p.glu ? 4 * p.N * p.l * p.nb1 : 0);
+    L.total = o;
+    return L;
+}
+
+// Every operand the backward reads through a buffer descriptor stays below
+// 2 GiB (32-bit offsets).
+bool bwd_fits(const Plan &p)
+{
+    const BwdLayout L = bwd_layout(p);
+    const int64_t es = p.esize, lim = (int64_t(1) << 31) - 1;
+    const int64_t sizes[] = {es * p.d * n_x_padded(p), es * p.ld_zh * p.d, es * p.l * p.nb1, es * p.m * p.l,
+                             4 * p.P_max * p.nb1, es * p.P_max * p.nb1, es * p.Tmax * n_x_padded(p),
+                             es * n_x_padded(p) * L.Tpad, es * p.d * L.Tpad, es * p.ld_zh * L.Tpad,
+                             es * p.m * L.Ppad, es * p.l * L.Ppad, es * p.nb1 * L.Ppad};
+    for (int64_t v : sizes)
+        if (v > lim)
+            return false;
+    return true;
+}
+
+// The first backward call on a handle: the weight layouts of the backward
+// products (from the handle's own repacked copies) and the workspace.
+template <typename E>
+void backward_setup(latentmoe_handle *h, hipStream_t s)
+{
+    const Plan &p = h->plan;
+    const BwdLayout L = bwd_layout(p);
+    const int64_t es = p.esize, nxp = n_x_padded(p);
+    if (hipMalloc(&h->bwbuf, L.wtotal) != hipSuccess)
+        throw HipError{hipErrorOutOfMemory};
+    if (hipMalloc(&h->bws, L.total) != hipSuccess)
+        throw HipError{hipErrorOutOfMemory};
+    char *w = static_cast<char *>(h->bwbuf);
+    char *b = static_cast<char *>(h->bws);
+    h->wx_o = w + L.off_wx;
+    h->wx_of = w + L.off_wxf;
+    h->wu_o = w + L.off_wu;
+    h->wu_of = w + L.off_wuf;
+    h->w1b = w + L.off_w1b;
+    h->w2b = w + L.off_w2b;
+    h->XA = b + L.off_xa;
+    h->Apre = reinterpret_cast<float *>(b + L.off_apre);
+    h->dUH = b + L.off_duh;
+    h->dYp = b + L.off_dyp;
+    h->dH = b + L.off_dh;
+    h->dA = b + L.off_da;
+    h->dzp = b + L.off_dzp;
+    h->dX = b + L.off_dx;
+    h->xT = b + L.off_xt;
+    h->dXT = b + L.off_dxt;
+    h->zhT = b + L.off_zht;
+    h->dyT = b + L.off_dyt;
+    h->HT = b + L.off_ht;
+    h->dYpT = b + L.off_dypt;
+    h->zpT = b + L.off_zpt;
+    h->dAT = b + L.off_dat;
+    h->koff = reinterpret_cast<int *>(b + L.off_koff);
+    h->dWx = reinterpret_cast<float *>(b + L.off_dwx);
+    h->dWu = reinterpret_cast<float *>(b + L.off_dwu);
+    h->dW1g = p.glu ? reinterpret_cast<float *>(b + L.off_dw1g) : nullptr;
+    h->Tpad = L.Tpad;
+    h->Ppad = L.Ppad;
+    // columns n_x .. n_xp of Wx and of dX stay zero (the dx product runs over
+    // the padded width, a multiple of the k-tile)
+    hip_check(hipMemsetAsync(h->wx_o, 0, es * p.d * nxp, s));
+    hip_check(hipMemsetAsync(h->dX, 0, es * p.Tmax * nxp, s));
+    // Wx [d, n_x]: the transpose of the x-pass's [n_x, d] rows (same column
+    // order, gated pairs included); [W_up ; W2_s] [l + S m_s, d] likewise
+    launch_transpose<E>(h->wcat1T, p.n_x, p.d, 1, 0, h->wx_o, nxp, 0, s);
+    launch_transpose<E>(h->wcat2T, p.d, p.ld_zh, 1, 0, h->wu_o, p.d, 0, s);
+    launch_fragmajor(h->wx_o, p.d, es * nxp, h->wx_of, s);
+    launch_fragmajor(h->wu_o, p.ld_zh, es * p.d, h->wu_of, s);
+    // expert banks with rows and K swapped: dH = dY W2^T reads W2 with rows
+    // m and K = l; dz = dA W1^T reads W1 with rows l and K = nb1
+    constexpr int BK = 128 / (int)sizeof(E);
+    retile_kernel<E, BK><<<dim3((unsigned)(p.nb1 / BK), (unsigned)(p.l / BK), (unsigned)p.N), dim3(256), 0, s>>>(
+        static_cast<const E *>(h->w1T), (int)p.l, (int)p.nb1, static_cast<E *>(h->w1b));
+    hip_check(hipGetLastError());
+    retile_kernel<E, BK><<<dim3((unsigned)(p.l / BK), (unsigned)(p.m / BK), (unsigned)p.N), dim3(256), 0, s>>>(
+        static_cast<const E *>(h->w2T), (int)p.m, (int)p.l, static_cast<E *>(h->w2b));
+    hip_check(hipGetLastError());
+}
+
+template <typename E>
+void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hipStream_t s,
+                   const latentmoe_grads *gr)
+{
+    const Plan &p = h->plan;
+    const int N = (int)p.N, K = (int)p.K;
+    const int64_t P = (int64_t)T * K, es = p.esize, nxp = n_x_padded(p), ldxa = p.n_x - p.N;
+    const int gbm = group_bm_for(P, N);
+    const int64_t max_mt = max_mtiles_for(P, N, gbm);
+    const int64_t Tp = align_up(T, 64);
+    const int gl = p.glu ? 1 : 0;
+    const int sms = (int)(p.S * p.ms);
+
+    forward_impl<E>(h, x, nullptr, T, s, nullptr, true);
+
+    // [du | dh_s] = dy [W_up ; W2_s]^T
+    GemmParams ga{};
+    ga.A = dy;
+    ga.lda = p.d;
+    ga.a_bytes = (int64_t)T * p.d * es;
+    ga.B = h->wu_o;
+    ga.Bfrag = h->wu_of;
+    ga.ldb = p.d;
+    ga.C = h->dUH;
+    ga.ldc = p.ld_zh;
+    ga.M = T;
+    ga.N = (int)p.ld_zh;
+    ga.K = (int)p.d;
+    ga.group_m = 8;
+    dense_gemm<E, kTagBwd>(ga, h->partial, h->partial_cap, s);
+    // shared experts: the gradient of their pre-activations -> dX[:, N' + l ..]
+    if (sms > 0) {
+        const int64_t n = (int64_t)T * sms;
+        shared_act_grad_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+            static_cast<const E *>(h->XA), ldxa, static_cast<const E *>(h->dUH), p.ld_zh, T, (int)p.l, sms, gl,
+            static_cast<E *>(h->dX), nxp, (int)(p.N + p.l));
+        hip_check(hipGetLastError());
+    }
+    // gates and combine: dY_perm, and ds -> dX[:, 0 .. N')
+    gate_combine_grad_kernel<E><<<dim3((unsigned)T), dim3(256), 0, s>>>(
+        static_cast<const E *>(h->dUH), p.ld_zh, static_cast<const E *>(h->Yp), h->pos, h->idx, h->gate, K,
+        (int)p.l, N, static_cast<E *>(h->dYp), static_cast<E *>(h->dX), nxp);
+    hip_check(hipGetLastError());
+    // dH = dY_perm W2_e^T, then the gradient of the routed pre-activations
+    GemmParams gb{};
+    gb.A = h->dYp;
+    gb.lda = p.l;
+    gb.a_bytes = P * p.l * es;
+    gb.B = h->w2b;
+    gb.ldb = p.bk_b;
+    gb.b_kstep = p.m * p.bk_b * es;
+    gb.strideB = p.m * p.l;
+    gb.C = h->dH;
+    gb.ldc = p.m;
+    gb.N = (int)p.m;
+    gb.K = (int)p.l;
+    gb.tile_expert = h->tile_expert;
+    gb.tile_row0 = h->tile_row0;
+    gb.n_mtiles = h->n_mtiles;
+    gb.offsets = h->offsets;
+    grouped_gemm<E, kTagBwd>(gb, max_mt, gbm, false, s);
+    expert_act_grad_kernel<E><<<dim3((unsigned)((P * p.m + 255) / 256)), dim3(256), 0, s>>>(
+        h->Apre, static_cast<const E *>(h->dH), P, (int)p.m, (int)p.nb1, gl, static_cast<E *>(h->dA));
+    hip_check(hipGetLastError());
+    // dz_perm = dA W1_e^T; dz[t] = sum over t's slots -> dX[:, N' .. N' + l)
+    GemmParams gc = gb;
+    gc.A = h->dA;
+    gc.lda = p.nb1;
+    gc.a_bytes = P * p.nb1 * es;
+    gc.B = h->w1b;
+    gc.b_kstep = p.l * p.bk_b * es;
+    gc.strideB = p.l * p.nb1;
+    gc.C = h->dzp;
+    gc.ldc = p.l;
+    gc.N = (int)p.l;
+    gc.K = (int)p.nb1;
+    grouped_gemm<E, kTagBwd>(gc, max_mt, gbm, false, s);
+    {
+        const int64_t n = (int64_t)T * p.l;
+        gather_sum_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+            static_cast<const E *>(h->dzp), h->pos, T, K, (int)p.l, static_cast<E *>(h->dX), nxp, N);
+        hip_check(hipGetLastError());
+    }
+    // dx = [ds | dz | d pre_s] Wx^T
+    if (gr->dx) {
+        GemmParams gd{};
+        gd.A = h->dX;
+        gd.lda = nxp;
+        gd.a_bytes = (int64_t)T * nxp * es;
+        gd.B = h->wx_o;
+        gd.Bfrag = h->wx_of;
+        gd.ldb = nxp;
+        gd.C = gr->dx;
+        gd.ldc = p.d;
+        gd.M = T;
+        gd.N = (int)p.d;
+        gd.K = (int)nxp;
+        gd.group_m = 8;
+        dense_gemm<E, kTagBwd>(gd, h->partial, h->partial_cap, s);
+    }
+
+    // ---- weight gradients (fp32), sums over tokens / an expert's rows ----
+    auto wgrad = [&](const void *A, int64_t M, const void *B, int64_t Nn, int64_t lda, float *C) {
+        GemmParams g{};
+        g.A = A;
+        g.lda = lda;
+        g.a_bytes = M * lda * es;
+        g.B = B;
+        g.ldb = lda;
+        g.C32 = C;
+        g.ldc32 = Nn;
+        g.c_split = (int)Nn;
+        g.M = (int)M;
+        g.N = (int)Nn;
+        g.K = (int)lda;
+        g.group_m = 8;
+        return g;
+    };
+    // tokens padded to 64 with zero columns
+    launch_pad_transpose<E>(x, p.d, T, (int)p.d, nullptr, nullptr, nullptr, 0, h->xT, Tp, s);
+    launch_pad_transpose<E>(h->dX, nxp, T, (int)p.n_x, nullptr, nullptr, nullptr, 0, h->dXT, Tp, s);
+    launch_pad_transpose<E>(h->zh, p.ld_zh, T, (int)p.ld_zh, nullptr, nullptr, nullptr, 0, h->zhT, Tp, s);
+    launch_pad_transpose<E>(dy, p.d, T, (int)p.d, nullptr, nullptr, nullptr, 0, h->dyT, Tp, s);
+    if (gr->dw_router || gr->dw_down || gr->dw1_shared || gr->dw1_shared_gate) {
+        GemmParams g = wgrad(h->xT, p.d, h->dXT, p.n_x, Tp, h->dWx);
+        launch_dense<E, 128, 128, 2, 2, 2, kTagBwd>(g, s);
+        auto split = [&](float *dst, int rows, int col0, int nb, int w, int sel) {
+            const int64_t n = (int64_t)nb * rows * w;
+            split_cols_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(h->dWx, p.n_x, rows, col0, nb,
+                                                                                    w, sel, dst);
+            hip_check(hipGetLastError());
+        };
+        if (gr->dw_router)
+            split(gr->dw_router, (int)p.d, 0, 1, N, -1);
+        if (gr->dw_down)
+            split(gr->dw_down, (int)p.d, N, 1, (int)p.l, -1);
+        if (p.S > 0 && gr->dw1_shared)
+            split(gr->dw1_shared, (int)p.d, (int)(p.N + p.l), (int)p.S, (int)p.ms, p.glu ? 1 : -1);
+        if (p.S > 0 && p.glu && gr->dw1_shared_gate)
+            split(gr->dw1_shared_gate, (int)p.d, (int)(p.N + p.l), (int)p.S, (int)p.ms, 0);
+    }
+    if (gr->dw_up || gr->dw2_shared) {
+        GemmParams g = wgrad(h->zhT, p.ld_zh, h->dyT, p.d, Tp, h->dWu);
+        launch_dense<E, 128, 128, 2, 2, 2, kTagBwd>(g, s);
+        if (gr->dw_up)
+            hip_check(hipMemcpyAsync(gr->dw_up, h->dWu, 4 * p.l * p.d, hipMemcpyDeviceToDevice, s));
+        if (p.S > 0 && gr->dw2_shared)
+            hip_check(hipMemcpyAsync(gr->dw2_shared, h->dWu + p.l * p.d, 4 * p.S * p.ms * p.d,
+                                     hipMemcpyDeviceToDevice, s));
+    }
+    if (h->cfg.has_router_bias && gr->db_router) {
+        col_sum_kernel<E><<<dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s>>>(static_cast<const E *>(h->dX), nxp,
+                                                                                  T, N, gr->db_router);
+        hip_check(hipGetLastError());
+    }
+    // expert banks: per expert a sum over its rows, padded to 64 per expert
+    const bool need1 = gr->dw1 || (p.glu && gr->dw1_gate);
+    if (gr->dw2 || need1) {
+        padded_offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(h->counts, N, 64, h->koff);
+        hip_check(hipGetLastError());
+    }
+    if (gr->dw2) {
+        launch_pad_transpose<E>(h->H, p.m, (int)P, (int)p.m, nullptr, h->offsets, h->koff, N, h->HT, h->Ppad, s);
+        launch_pad_transpose<E>(h->dYp, p.l, (int)P, (int)p.l, nullptr, h->offsets, h->koff, N, h->dYpT, h->Ppad, s);
+        GemmParams g = wgrad(h->HT, p.m, h->dYpT, p.l, h->Ppad, gr->dw2);
+        g.k_offsets = h->koff;
+        g.n_batches = N;
+        launch_batched_k<E, kTagBwd>(g, s);
+    }
+    if (need1) {
+        launch_pad_transpose<E>(h->XA, ldxa, (int)P, (int)p.l, h->perm, h->offsets, h->koff, N, h->zpT, h->Ppad, s);
+        launch_pad_transpose<E>(h->dA, p.nb1, (int)P, (int)p.nb1, nullptr, h->offsets, h->koff, N, h->dAT, h->Ppad,
+                                s);
+        float *dst = p.glu ? h->dW1g : gr->dw1;
+        GemmParams g = wgrad(h->zpT, p.l, h->dAT, p.nb1, h->Ppad, dst);
+        g.k_offsets = h->koff;
+        g.n_batches = N;
+        launch_batched_k<E, kTagBwd>(g, s);
+        if (p.glu) {  // [N' l, 2m] gated pairs -> W1 (value) and W_g (gate)
+            const int64_t n = p.N * p.l * p.m;
+            for (int sel = 0; sel < 2; ++sel) {
+                float *out = sel ? gr->dw1 : gr->dw1_gate;
+                if (!out)
+                    continue;
+                split_cols_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+                    h->dW1g, p.nb1, (int)(p.N * p.l), 0, 1, (int)p.m, sel, out);
+                hip_check(hipGetLastError());
+            }
+        }
+    }
+}
 
 }  // namespace
 
@@ -870,6 +1270,41 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
         return LATENTMOE_ERR_OUT_OF_MEMORY;
     }
     *out = h;
+    return LATENTMOE_OK;
+}
+
+int latentmoe_backward(latentmoe_handle *h, const void *x, const void *dy, int64_t T, void *hip_stream,
+                       const latentmoe_grads *g)
+{
+    if (!h || !x || !dy || !g || T < 1 || T > h->plan.Tmax)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (g->db_router && !h->cfg.has_router_bias)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (h->plan.fp8)
+        return LATENTMOE_ERR_UNSUPPORTED;
+    if (!bwd_fits(h->plan))
+        return LATENTMOE_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    try {
+        if (!h->bwbuf) {
+            if (h->plan.dtype == LATENTMOE_DTYPE_BF16)
+                backward_setup<bf16>(h, s);
+            else
+                backward_setup<float>(h, s);
+        }
+        if (h->plan.dtype == LATENTMOE_DTYPE_BF16)
+            backward_impl<bf16>(h, x, dy, (int)T, s, g);
+        else
+            backward_impl<float>(h, x, dy, (int)T, s, g);
+    } catch (const HipError &e) {
+        g_last_hip_error = (int)e.e;
+        if (e.e == hipErrorOutOfMemory && !h->bws) {
+            (void)hipFree(h->bwbuf);
+            h->bwbuf = nullptr;
+            return LATENTMOE_ERR_OUT_OF_MEMORY;
+        }
+        return LATENTMOE_ERR_HIP;
+    }
     return LATENTMOE_OK;
 }
 

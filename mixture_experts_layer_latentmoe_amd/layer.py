@@ -143,3 +143,29 @@ class LatentMoE:
                                      for k, _ in _abi.latentmoe_debug._fields_])
         out["y"] = self.forward(x, dbg=dbg)
         return out
+
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, want=None):
+        """dx and the weight gradients (fp32, the weights' [in, out] layouts)
+        for dy = dL/dy, as device tensors; ``want`` names a subset."""
+        s = self.shape
+        T = x.shape[0]
+        assert x.is_contiguous() and dy.is_contiguous() and dy.shape == x.shape
+        f32, E = torch.float32, self.tdtype
+        S, ms = s.n_shared, s.m_shared
+        shapes = {"dx": ((T, s.d), E), "dw_router": ((s.d, s.n_experts), f32), "dw_down": ((s.d, s.l), f32),
+                  "dw1": ((s.n_experts, s.l, s.m), f32), "dw2": ((s.n_experts, s.m, s.l), f32),
+                  "dw_up": ((s.l, s.d), f32)}
+        if S > 0:
+            shapes.update({"dw1_shared": ((S, s.d, ms), f32), "dw2_shared": ((S, ms, s.d), f32)})
+        if s.has_bias:
+            shapes["db_router"] = ((s.n_experts,), f32)
+        if s.expert_act == "swiglu":
+            shapes["dw1_gate"] = ((s.n_experts, s.l, s.m), f32)
+            if S > 0:
+                shapes["dw1_shared_gate"] = ((S, s.d, ms), f32)
+        keys = list(shapes) if want is None else [k for k in want if k in shapes]
+        out = {k: torch.empty(*shapes[k][0], dtype=shapes[k][1], device=self.device) for k in keys}
+        g = _abi.latentmoe_grads(*[(out[k].data_ptr() if k in out else None)
+                                   for k, _ in _abi.latentmoe_grads._fields_])
+        _abi.latentmoe_backward(self.handle, x.data_ptr(), dy.data_ptr(), T, _stream_ptr(self.device), g)
+        return out
