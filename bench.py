@@ -139,6 +139,9 @@ def main():
                     help="independently repacked weight copies that consecutive steps rotate through "
                          "(0: enough for 2 GB of weights, at least 2, at most 8), so that no step finds "
                          "its weights in the 256 MB last-level cache from the step before")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the layer's backward pass (its forward recompute included) over the same "
+                         "steps and report it under \"backward\"")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (3 launches) so that profiler "
                          "byte counters can be scaled by a kernel of known traffic")
@@ -234,6 +237,24 @@ def main():
                 "avg_us": timed["avg_us"], "launches": timed["launches"],
                 "traffic": profiled_traffic(sh.name, dom)}
     total_flop = sum(f for f, _ in work.values() if f)
+    bwd = None
+    if args.backward and sh.expert_dtype != "fp8":
+        # algorithmic work: the recomputed forward (no up-projection), the
+        # data gradients and the weight gradients of every GEMM: 3F - F_up
+        gemm_flop = total_flop - work["gemm_up_shared2"][0] + 2.0 * total_flop
+        dy = torch.randn_like(x)
+        for i in range(max(2, R)):
+            layers[i % R].backward(x, dy)
+        torch.cuda.synchronize()
+        tb0 = time.perf_counter()
+        for i in range(args.steps):
+            layers[i % R].backward(x, dy)
+        torch.cuda.synchronize()
+        tb = (time.perf_counter() - tb0) / args.steps
+        bwd = {"ms_per_step": round(tb * 1e3, 4), "tokens_per_s": round(T / tb, 1),
+               "algorithmic_tflops": round(gemm_flop / tb / 1e12, 1),
+               "note": "forward recompute + data and weight gradients (fp32), weight copies rotated as above"}
+        print(f"[bench] backward {args.steps} steps in {tb * args.steps:.3f} s", file=sys.stderr, flush=True)
     for L in layers:
         L.close()
     if args.copy_calibration:
@@ -258,6 +279,7 @@ def main():
                    "tokens": T, "experts_with_tokens": n_active, "weight_copies": R},
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
         "roofline": roof, "cpu_baseline": cpu, "stages": stage_out,
+        **({"backward": bwd} if bwd else {}),
         "stages_note": "per-stage HIP-event times from an untimed pass of min(steps, 10) forwards; "
                        "roofline.avg_us is the dominant kernel timed over the timed region",
     }

@@ -54,17 +54,122 @@ __global__ __launch_bounds__(256) void xpass_act_kernel(const E *__restrict__ XA
     zh[t * ld_zh + c] = from_f32<E>(v);
 }
 
-// H[p, j] = act(A[p, :]) for the routed experts (A fp32 [P, nb1]).
+// Eight consecutive values of E as one 16-byte (bf16) or two (fp32) moves.
+template <typename E> __device__ __forceinline__ void load8(const E *p, float (&v)[8])
+{
+    if constexpr (sizeof(E) == 2) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        const E *e = reinterpret_cast<const E *>(&u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = to_f32(e[i]);
+    } else {
+        const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+        v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    }
+}
+template <typename E> __device__ __forceinline__ void store8(E *p, const float (&v)[8])
+{
+    if constexpr (sizeof(E) == 2) {
+        E e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            e[i] = from_f32<E>(v[i]);
+        *reinterpret_cast<uint4 *>(p) = *reinterpret_cast<const uint4 *>(e);
+    } else {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+}
+
+// H[p, 8 g .. 8 g + 7] = act(A[p, :]) for one group of 8 outputs; with the
+// gated block layout the group's gate columns are 16 g .. 16 g + 7 and its
+// value columns the next 8.  m is a multiple of 8.
 template <typename E>
-__global__ __launch_bounds__(256) void expert_act_kernel(const float *__restrict__ A, int64_t P, int m, int nb1,
-                                                         int gated, E *__restrict__ H)
+__global__ __launch_bounds__(256) void expert_act8_kernel(const float *__restrict__ A, int64_t P, int m, int nb1,
+                                                          int gated, E *__restrict__ H)
 {
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= P * m)
+    const int gpr = m / 8;
+    if (q >= P * gpr)
         return;
-    const int64_t p = q / m;
-    const int j = (int)(q - p * m);
-    H[p * m + j] = from_f32<E>(act_of(A + p * nb1, j, gated != 0));
+    const int64_t p = q / gpr;
+    const int g = (int)(q - p * gpr);
+    float v[8];
+    if (!gated) {
+        load8(A + p * nb1 + 8 * g, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float a = fmaxf(v[i], 0.f);
+            v[i] = a * a;
+        }
+    } else {
+        float gt[8], va[8];
+        load8(A + p * nb1 + 16 * g, gt);
+        load8(A + p * nb1 + 16 * g + 8, va);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = bwd_silu(gt[i]) * va[i];
+    }
+    store8(H + p * m + 8 * g, v);
+}
+
+// dA for one group of 8 outputs of the routed experts (see act_grad).
+template <typename E>
+__global__ __launch_bounds__(256) void expert_act_grad8_kernel(const float *__restrict__ A, const E *__restrict__ dH,
+                                                               int64_t P, int m, int nb1, int gated,
+                                                               E *__restrict__ dA)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int gpr = m / 8;
+    if (q >= P * gpr)
+        return;
+    const int64_t p = q / gpr;
+    const int g = (int)(q - p * gpr);
+    float d[8];
+    load8(dH + p * m + 8 * g, d);
+    if (!gated) {
+        float a[8];
+        load8(A + p * nb1 + 8 * g, a);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            a[i] = a[i] > 0.f ? 2.f * a[i] * d[i] : 0.f;
+        store8(dA + p * nb1 + 8 * g, a);
+    } else {
+        float gt[8], va[8];
+        load8(A + p * nb1 + 16 * g, gt);
+        load8(A + p * nb1 + 16 * g + 8, va);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float sg = bwd_sigmoid(gt[i]);
+            const float dg = d[i] * va[i] * sg * (1.f + gt[i] * (1.f - sg));
+            va[i] = d[i] * gt[i] * sg;
+            gt[i] = dg;
+        }
+        store8(dA + p * nb1 + 16 * g, gt);
+        store8(dA + p * nb1 + 16 * g + 8, va);
+    }
+}
+
+// dz[t, 8 g ..] = sum_k dz_perm[pos[t, k], 8 g ..] (slot order) -> dX[t, col0 ..].
+template <typename E>
+__global__ __launch_bounds__(256) void gather_sum8_kernel(const E *__restrict__ dzp, const int *__restrict__ pos, int T,
+                                                          int K, int l, E *__restrict__ dX, int64_t ld_dx, int col0)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int gpr = l / 8;
+    if (q >= (int64_t)T * gpr)
+        return;
+    const int64_t t = q / gpr;
+    const int g = (int)(q - t * gpr);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, v[8];
+    for (int k = 0; k < K; ++k) {
+        load8(dzp + (int64_t)pos[t * K + k] * l + 8 * g, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] += v[i];
+    }
+    store8(dX + t * ld_dx + col0 + 8 * g, acc);
 }
 
 // Gradient through the activation: from dh (width m or m_s) and the
@@ -84,20 +189,6 @@ __device__ __forceinline__ void act_grad(const PRE *pre, const E *dh, int j, boo
     const float g = to_f32(pre[c]), v = to_f32(pre[c + 8]), sg = bwd_sigmoid(g);
     dpre[c] = from_f32<E>(d * v * sg * (1.f + g * (1.f - sg)));
     dpre[c + 8] = from_f32<E>(d * g * sg);
-}
-
-// Routed experts: dA[P, nb1] from dH[P, m] and A (fp32).
-template <typename E>
-__global__ __launch_bounds__(256) void expert_act_grad_kernel(const float *__restrict__ A, const E *__restrict__ dH,
-                                                              int64_t P, int m, int nb1, int gated,
-                                                              E *__restrict__ dA)
-{
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= P * m)
-        return;
-    const int64_t p = q / m;
-    const int j = (int)(q - p * m);
-    act_grad<E, float>(A + p * nb1, dH + p * m, j, gated != 0, dA + p * nb1);
 }
 
 // Shared experts: the shared part of dX_in [T, n_x] (columns from col0 on)
@@ -161,22 +252,6 @@ __global__ __launch_bounds__(256) void gate_combine_grad_kernel(const E *__restr
         const float g = gate[t * K + k];
         ds[idx[t * K + k]] = from_f32<E>(g * (s_dg[k] - gdg));
     }
-}
-
-// dz[t] = sum_k dz_perm[pos[t, k]] (slot order), written to dX[t, col0 ..].
-template <typename E>
-__global__ __launch_bounds__(256) void gather_sum_kernel(const E *__restrict__ dzp, const int *__restrict__ pos, int T,
-                                                         int K, int l, E *__restrict__ dX, int64_t ld_dx, int col0)
-{
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (q >= (int64_t)T * l)
-        return;
-    const int64_t t = q / l;
-    const int j = (int)(q - t * l);
-    float acc = 0.f;
-    for (int k = 0; k < K; ++k)
-        acc += to_f32(dzp[(int64_t)pos[t * K + k] * l + j]);
-    dX[t * ld_dx + col0 + j] = from_f32<E>(acc);
 }
 
 // Padded per-expert offsets: koff[0] = 0, koff[e + 1] = koff[e] +
@@ -255,6 +330,79 @@ __global__ __launch_bounds__(256) void pad_transpose_kernel(const E *__restrict_
         const int64_t q = q0 + tx;
         if (c < C && q < qend)
             dst[c * ld_dst + q] = from_f32<E>(tile[tx][i]);
+    }
+}
+
+// The same map as pad_transpose_kernel in 64 x 64 tiles with 16-byte loads
+// and stores.  Padded segments are multiples of 64 long, so a tile of 64
+// destination columns q0 .. q0 + 63 (q0 a multiple of 64) lies in one
+// segment: one lookup per tile.  Needs C, ld_src and the source base
+// 16-byte aligned in elements of E, and ld_dst a multiple of 64.
+template <typename E>
+__global__ __launch_bounds__(256) void pad_transpose64_kernel(const E *__restrict__ src, int64_t ld_src, int rows,
+                                                              int C, const int *__restrict__ gather,
+                                                              const int *__restrict__ offs,
+                                                              const int *__restrict__ koff, int nseg,
+                                                              E *__restrict__ dst, int64_t ld_dst)
+{
+    constexpr int VEC = 16 / (int)sizeof(E);  // elements per 16-byte access
+    constexpr int TPR = 64 / VEC;             // threads per 64-element row
+    constexpr int RPP = 256 / TPR;            // rows per pass
+    __shared__ E tile[64][64 + 2];            // [c][q]
+    __shared__ int64_t s_base;                // source row of q0 (-1: none)
+    __shared__ int s_valid;                   // valid rows from q0 on
+    const int64_t q0 = (int64_t)blockIdx.y * 64;
+    const int c0 = blockIdx.x * 64;
+    const int64_t qend = koff ? koff[nseg] : ld_dst;
+    if (q0 >= qend)
+        return;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        if (koff) {
+            int lo = 0, hi = nseg - 1;  // the segment e with koff[e] <= q0 < koff[e + 1]
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (koff[mid] <= q0)
+                    lo = mid;
+                else
+                    hi = mid - 1;
+            }
+            const int64_t r = q0 - koff[lo];
+            s_base = offs[lo] + r;
+            s_valid = (int)max((int64_t)0, (int64_t)(offs[lo + 1] - offs[lo]) - r);
+        } else {
+            s_base = q0;
+            s_valid = (int)max((int64_t)0, (int64_t)rows - q0);
+        }
+    }
+    __syncthreads();
+    const int64_t base = s_base;
+    const int valid = s_valid;
+    const int cl = (tid % TPR) * VEC;  // first column of this thread's 16 bytes
+    for (int rr = tid / TPR; rr < 64; rr += RPP) {
+        E v[VEC];
+        if (rr < valid && c0 + cl < C) {
+            const int64_t row = gather ? gather[base + rr] : base + rr;
+            *reinterpret_cast<uint4 *>(v) = *reinterpret_cast<const uint4 *>(src + row * ld_src + c0 + cl);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                v[i] = from_f32<E>(0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+            tile[cl + i][rr] = v[i];
+    }
+    __syncthreads();
+    const int ql = (tid % TPR) * VEC;
+    for (int cc = tid / TPR; cc < 64; cc += RPP) {
+        if (c0 + cc >= C || q0 + ql >= qend)
+            continue;
+        E v[VEC];
+#pragma unroll
+        for (int i = 0; i < VEC; ++i)
+            v[i] = tile[cc][ql + i];
+        *reinterpret_cast<uint4 *>(dst + (int64_t)(c0 + cc) * ld_dst + q0 + ql) = *reinterpret_cast<const uint4 *>(v);
     }
 }
 

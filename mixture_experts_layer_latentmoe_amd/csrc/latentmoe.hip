@@ -680,7 +680,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     tm.begin(ST_GEMM1);
     grouped_gemm<E, kTagG1>(g1, max_mt, gbm, p.fp8, s);
     if (train) {
-        expert_act_kernel<E><<<dim3((unsigned)((P * p.m + 255) / 256)), dim3(256), 0, s>>>(
+        expert_act8_kernel<E><<<dim3((unsigned)((P * p.m / 8 + 255) / 256)), dim3(256), 0, s>>>(
             h->Apre, P, (int)p.m, (int)p.nb1, p.glu ? 1 : 0, static_cast<E *>(h->H));
         hip_check(hipGetLastError());
     }
@@ -795,6 +795,14 @@ template <typename E>
 void launch_pad_transpose(const void *src, int64_t ld_src, int rows, int C, const int *gather, const int *offs,
                           const int *koff, int nseg, void *dst, int64_t ld_dst, hipStream_t s)
 {
+    constexpr int VEC = 16 / (int)sizeof(E);
+    if (reinterpret_cast<uintptr_t>(src) % 16 == 0 && ld_src % VEC == 0 && C % VEC == 0 && ld_dst % 64 == 0) {
+        dim3 grid((unsigned)((C + 63) / 64), (unsigned)(ld_dst / 64));
+        pad_transpose64_kernel<E><<<grid, dim3(256), 0, s>>>(static_cast<const E *>(src), ld_src, rows, C, gather,
+                                                             offs, koff, nseg, static_cast<E *>(dst), ld_dst);
+        hip_check(hipGetLastError());
+        return;
+    }
     dim3 grid((unsigned)((C + 31) / 32), (unsigned)(ld_dst / 32));
     pad_transpose_kernel<E><<<grid, dim3(256), 0, s>>>(static_cast<const E *>(src), ld_src, rows, C, gather, offs,
                                                        koff, nseg, static_cast<E *>(dst), ld_dst);
@@ -995,7 +1003,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     gb.n_mtiles = h->n_mtiles;
     gb.offsets = h->offsets;
     grouped_gemm<E, kTagBwd>(gb, max_mt, gbm, false, s);
-    expert_act_grad_kernel<E><<<dim3((unsigned)((P * p.m + 255) / 256)), dim3(256), 0, s>>>(
+    expert_act_grad8_kernel<E><<<dim3((unsigned)((P * p.m / 8 + 255) / 256)), dim3(256), 0, s>>>(
         h->Apre, static_cast<const E *>(h->dH), P, (int)p.m, (int)p.nb1, gl, static_cast<E *>(h->dA));
     hip_check(hipGetLastError());
     // dz_perm = dA W1_e^T; dz[t] = sum over t's slots -> dX[:, N' .. N' + l)
@@ -1012,8 +1020,8 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     gc.K = (int)p.nb1;
     grouped_gemm<E, kTagBwd>(gc, max_mt, gbm, false, s);
     {
-        const int64_t n = (int64_t)T * p.l;
-        gather_sum_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+        const int64_t n = (int64_t)T * p.l / 8;
+        gather_sum8_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
             static_cast<const E *>(h->dzp), h->pos, T, K, (int)p.l, static_cast<E *>(h->dX), nxp, N);
         hip_check(hipGetLastError());
     }
