@@ -376,6 +376,50 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
     }
 }
 
+// The staged epilogue of an all-fp32 output (c_split >= N: every column
+// goes to C32, no bias, no scales): each wave stages 32 rows x WTN floats,
+// then writes whole 16-byte chunks of output rows (chunk c of staged row r
+// at position c ^ (r % CPR)).
+template <int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void store_tile_staged_f32(const GemmParams &p, const f32x16 (&acc)[TM][TN],
+                                                      int64_t row_base, int rows_valid, int n0, int wm, int wn,
+                                                      int lane, uint4 *stg)
+{
+    constexpr int CPR = WTN * 4 / 16;  // 16-byte chunks per staged row
+    constexpr int RPI = 64 / CPR;      // staged rows per store instruction
+    static_assert(CPR >= 1 && CPR <= 64 && (CPR & (CPR - 1)) == 0, "staged row");
+    const int lr = lane & 31, lc = lane >> 5;
+    const int cbase = n0 + wn * WTN;  // first output column of this wave
+    const int rows_here = rows_valid - wm * WTM;
+    const int cw = lane % CPR;
+    const bool col_ok = cbase + cw * 4 < p.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        if (i * 32 >= rows_here)  // uniform: nothing left to store
+            break;
+#pragma unroll
+        for (int jn = 0; jn < TN; ++jn)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int ch = jn * 8 + 2 * g + lc;  // 16-byte chunk of columns jn 32 + 8 g + 4 lc ..
+                stg[lr * CPR + (ch ^ (lr & (CPR - 1)))] =
+                    make_uint4(__float_as_uint(acc[i][jn][4 * g]), __float_as_uint(acc[i][jn][4 * g + 1]),
+                               __float_as_uint(acc[i][jn][4 * g + 2]), __float_as_uint(acc[i][jn][4 * g + 3]));
+            }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int r0 = 0; r0 < 32; r0 += RPI) {
+            const int rl = r0 + lane / CPR;
+            const uint4 v = stg[rl * CPR + (cw ^ (rl & (CPR - 1)))];
+            if (col_ok && i * 32 + rl < rows_here)
+                *reinterpret_cast<uint4 *>(p.C32 + (row_base + wm * WTM + i * 32 + rl) * p.ldc32 + cbase + cw * 4) = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // The staged epilogue of a wave block whose B columns are all gated pairs
 // (bcol0 = n0 + wn WTN >= glu_from): the wave stages 32 rows x WTN / 2
 // outputs silu(gate) * value, then writes whole 16-byte chunks of output
@@ -637,6 +681,21 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     }
 
     const float *cs = (BQ8 && p.scaleB) ? p.scaleB + (int64_t)expert * p.N : nullptr;  // column scales
+    // an all-fp32 output without bias or scales: staged through LDS when the
+    // waves' areas fit in two stage arrays
+    constexpr int WAVE_F = 32 * WTN * 4 / 16;  // 16-byte units of a wave's fp32 area
+    constexpr bool F32_IN_A = NW <= 2 * ((BM * 8) / WAVE_F);
+    constexpr bool F32_FITS = F32_IN_A || NW <= 2 * ((BN * CHB) / WAVE_F);
+    if constexpr (F32_FITS) {
+        if (p.c_split >= p.N && p.glu_from >= p.N && !p.bias32 && !cs) {
+            constexpr int PER = (F32_IN_A ? BM * 8 : BN * CHB) / WAVE_F;
+            wait_vm_lgkm0<0>();
+            __builtin_amdgcn_s_barrier();
+            uint4 *stg = (F32_IN_A ? (wave < PER ? sA0 : sA1) : (wave < PER ? sB0 : sB1)) + (wave % PER) * WAVE_F;
+            store_tile_staged_f32<TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg);
+            return;
+        }
+    }
     // fp32 outputs, and tiles that hold router columns or straddle the start
     // of the gated pairs: straight from the registers
     if (sizeof(E) != 2 || n0 < p.c_split || (n0 < p.glu_from && n0 + BN > p.glu_from)) {
