@@ -389,7 +389,11 @@ void repack_weights(latentmoe_handle *h, const latentmoe_weights *w, hipStream_t
 // ---- kernel launch helpers -------------------------------------------------
 
 // GEMM stage tags (one kernel symbol per layer stage)
-constexpr int kTagX = 0, kTagG1 = 1, kTagG2 = 2, kTagUp = 3, kTagBwd = 4;
+constexpr int kTagX = 0, kTagG1 = 1, kTagG2 = 2, kTagUp = 3;
+// backward: data gradients, dense weight gradients, expert-bank weight gradients
+constexpr int kTagDgrad = 4, kTagWgrad = 5, kTagWgradE = 6;
+// the backward's forward recompute: x-pass and grouped GEMM 1 with raw outputs
+constexpr int kTagXRaw = 7, kTagG1Raw = 8;
 
 template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG>
 void launch_dense(const GemmParams &gp, hipStream_t s)
@@ -604,7 +608,10 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
         g.glu_from = kNoColumn;
     }
     tm.begin(ST_GEMM_X);
-    dense_gemm<E, kTagX>(g, h->partial, h->partial_cap, s);
+    if (train)
+        dense_gemm<E, kTagXRaw>(g, h->partial, h->partial_cap, s);
+    else
+        dense_gemm<E, kTagX>(g, h->partial, h->partial_cap, s);
     if (train) {
         const int64_t n = (int64_t)T * p.ld_zh;
         xpass_act_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
@@ -678,7 +685,10 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
         g1.glu_from = kNoColumn;
     }
     tm.begin(ST_GEMM1);
-    grouped_gemm<E, kTagG1>(g1, max_mt, gbm, p.fp8, s);
+    if (train)
+        grouped_gemm<E, kTagG1Raw>(g1, max_mt, gbm, false, s);
+    else
+        grouped_gemm<E, kTagG1>(g1, max_mt, gbm, p.fp8, s);
     if (train) {
         expert_act8_kernel<E><<<dim3((unsigned)((P * p.m / 8 + 255) / 256)), dim3(256), 0, s>>>(
             h->Apre, P, (int)p.m, (int)p.nb1, p.glu ? 1 : 0, static_cast<E *>(h->H));
@@ -971,7 +981,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     ga.N = (int)p.ld_zh;
     ga.K = (int)p.d;
     ga.group_m = 8;
-    dense_gemm<E, kTagBwd>(ga, h->partial, h->partial_cap, s);
+    dense_gemm<E, kTagDgrad>(ga, h->partial, h->partial_cap, s);
     // shared experts: the gradient of their pre-activations -> dX[:, N' + l ..]
     if (sms > 0) {
         const int64_t n = (int64_t)T * sms;
@@ -1002,7 +1012,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     gb.tile_row0 = h->tile_row0;
     gb.n_mtiles = h->n_mtiles;
     gb.offsets = h->offsets;
-    grouped_gemm<E, kTagBwd>(gb, max_mt, gbm, false, s);
+    grouped_gemm<E, kTagDgrad>(gb, max_mt, gbm, false, s);
     expert_act_grad8_kernel<E><<<dim3((unsigned)((P * p.m / 8 + 255) / 256)), dim3(256), 0, s>>>(
         h->Apre, static_cast<const E *>(h->dH), P, (int)p.m, (int)p.nb1, gl, static_cast<E *>(h->dA));
     hip_check(hipGetLastError());
@@ -1018,7 +1028,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     gc.ldc = p.l;
     gc.N = (int)p.l;
     gc.K = (int)p.nb1;
-    grouped_gemm<E, kTagBwd>(gc, max_mt, gbm, false, s);
+    grouped_gemm<E, kTagDgrad>(gc, max_mt, gbm, false, s);
     {
         const int64_t n = (int64_t)T * p.l / 8;
         gather_sum8_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
@@ -1040,7 +1050,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
         gd.N = (int)p.d;
         gd.K = (int)nxp;
         gd.group_m = 8;
-        dense_gemm<E, kTagBwd>(gd, h->partial, h->partial_cap, s);
+        dense_gemm<E, kTagDgrad>(gd, h->partial, h->partial_cap, s);
     }
 
     // ---- weight gradients (fp32), sums over tokens / an expert's rows ----
@@ -1067,7 +1077,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     launch_pad_transpose<E>(dy, p.d, T, (int)p.d, nullptr, nullptr, nullptr, 0, h->dyT, Tp, s);
     if (gr->dw_router || gr->dw_down || gr->dw1_shared || gr->dw1_shared_gate) {
         GemmParams g = wgrad(h->xT, p.d, h->dXT, p.n_x, Tp, h->dWx);
-        launch_dense<E, 128, 128, 2, 2, 2, kTagBwd>(g, s);
+        launch_dense<E, 128, 128, 2, 2, 2, kTagWgrad>(g, s);
         auto split = [&](float *dst, int rows, int col0, int nb, int w, int sel) {
             const int64_t n = (int64_t)nb * rows * w;
             split_cols_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(h->dWx, p.n_x, rows, col0, nb,
@@ -1085,7 +1095,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     }
     if (gr->dw_up || gr->dw2_shared) {
         GemmParams g = wgrad(h->zhT, p.ld_zh, h->dyT, p.d, Tp, h->dWu);
-        launch_dense<E, 128, 128, 2, 2, 2, kTagBwd>(g, s);
+        launch_dense<E, 128, 128, 2, 2, 2, kTagWgrad>(g, s);
         if (gr->dw_up)
             hip_check(hipMemcpyAsync(gr->dw_up, h->dWu, 4 * p.l * p.d, hipMemcpyDeviceToDevice, s));
         if (p.S > 0 && gr->dw2_shared)
@@ -1109,7 +1119,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
         GemmParams g = wgrad(h->HT, p.m, h->dYpT, p.l, h->Ppad, gr->dw2);
         g.k_offsets = h->koff;
         g.n_batches = N;
-        launch_batched_k<E, kTagBwd>(g, s);
+        launch_batched_k<E, kTagWgradE>(g, s);
     }
     if (need1) {
         launch_pad_transpose<E>(h->XA, ldxa, (int)P, (int)p.l, h->perm, h->offsets, h->koff, N, h->zpT, h->Ppad, s);
@@ -1119,7 +1129,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
         GemmParams g = wgrad(h->zpT, p.l, h->dAT, p.nb1, h->Ppad, dst);
         g.k_offsets = h->koff;
         g.n_batches = N;
-        launch_batched_k<E, kTagBwd>(g, s);
+        launch_batched_k<E, kTagWgradE>(g, s);
         if (p.glu) {  // [N' l, 2m] gated pairs -> W1 (value) and W_g (gate)
             const int64_t n = p.N * p.l * p.m;
             for (int sel = 0; sel < 2; ++sel) {
