@@ -3,8 +3,10 @@
 // Gated experts keep the forward's B-column order throughout: in every
 // block of 16 columns, 8 gate columns then the 8 value columns of the same
 // outputs (the interleave of transpose_kernel's row map).  Pre-activations
-// of the routed experts are fp32 [P, nb1]; those of the shared experts sit
-// in the x-pass's raw output XA [T, l + g S m_s] (z first) in E.
+// of the routed experts are fp32 [P, nb1] (their activation and its
+// gradient are formed in the epilogues of the grouped GEMMs that produce
+// them and dH); those of the shared experts sit in the x-pass's raw output
+// XA [T, l + g S m_s] (z first) in E.
 #pragma once
 
 #include "common.hpp"
@@ -79,75 +81,6 @@ template <typename E> __device__ __forceinline__ void store8(E *p, const float (
     } else {
         *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-    }
-}
-
-// H[p, 8 g .. 8 g + 7] = act(A[p, :]) for one group of 8 outputs; with the
-// gated block layout the group's gate columns are 16 g .. 16 g + 7 and its
-// value columns the next 8.  m is a multiple of 8.
-template <typename E>
-__global__ __launch_bounds__(256) void expert_act8_kernel(const float *__restrict__ A, int64_t P, int m, int nb1,
-                                                          int gated, E *__restrict__ H)
-{
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int gpr = m / 8;
-    if (q >= P * gpr)
-        return;
-    const int64_t p = q / gpr;
-    const int g = (int)(q - p * gpr);
-    float v[8];
-    if (!gated) {
-        load8(A + p * nb1 + 8 * g, v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float a = fmaxf(v[i], 0.f);
-            v[i] = a * a;
-        }
-    } else {
-        float gt[8], va[8];
-        load8(A + p * nb1 + 16 * g, gt);
-        load8(A + p * nb1 + 16 * g + 8, va);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            v[i] = bwd_silu(gt[i]) * va[i];
-    }
-    store8(H + p * m + 8 * g, v);
-}
-
-// dA for one group of 8 outputs of the routed experts (see act_grad).
-template <typename E>
-__global__ __launch_bounds__(256) void expert_act_grad8_kernel(const float *__restrict__ A, const E *__restrict__ dH,
-                                                               int64_t P, int m, int nb1, int gated,
-                                                               E *__restrict__ dA)
-{
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int gpr = m / 8;
-    if (q >= P * gpr)
-        return;
-    const int64_t p = q / gpr;
-    const int g = (int)(q - p * gpr);
-    float d[8];
-    load8(dH + p * m + 8 * g, d);
-    if (!gated) {
-        float a[8];
-        load8(A + p * nb1 + 8 * g, a);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            a[i] = a[i] > 0.f ? 2.f * a[i] * d[i] : 0.f;
-        store8(dA + p * nb1 + 8 * g, a);
-    } else {
-        float gt[8], va[8];
-        load8(A + p * nb1 + 16 * g, gt);
-        load8(A + p * nb1 + 16 * g + 8, va);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float sg = bwd_sigmoid(gt[i]);
-            const float dg = d[i] * va[i] * sg * (1.f + gt[i] * (1.f - sg));
-            va[i] = d[i] * gt[i] * sg;
-            gt[i] = dg;
-        }
-        store8(dA + p * nb1 + 16 * g, gt);
-        store8(dA + p * nb1 + 16 * g + 8, va);
     }
 }
 

@@ -79,7 +79,24 @@ struct GemmParams {
     // an empty range gives zeros) and writes output rows e M .. e M + M - 1
     const int *k_offsets;
     int n_batches;
+    // pre-activations (fp32, row stride ld_pre) read by the gradient
+    // epilogues (gemm_kernel's ACT 3 and 4)
+    const float *act_pre;
+    int64_t ld_pre;
 };
+
+// Epilogues of the fp32 staged store (template parameter ACT of gemm_kernel):
+//  ACT_NONE      the sums to C32;
+//  ACT_RELU2     the sums to C32 and relu(sum)^2 to C (N columns);
+//  ACT_GLU       the sums to C32 and, for the gated pairs (16-column blocks:
+//                8 gates, then their 8 values), silu(gate) * value to C (N / 2
+//                columns);
+//  ACT_RELU2_GRAD instead of the sums dH, dA = dH * 2 relu(a) to C (N columns),
+//                a from act_pre;
+//  ACT_GLU_GRAD  for output column j, gate column g = 16 (j / 8) + j % 8 and
+//                value column g + 8 of act_pre: dH * v * silu'(gate) to C
+//                column g and dH * silu(gate) to C column g + 8 (2 N columns).
+enum { ACT_NONE = 0, ACT_RELU2 = 1, ACT_GLU = 2, ACT_RELU2_GRAD = 3, ACT_GLU_GRAD = 4 };
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
@@ -380,7 +397,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
 // goes to C32, no bias, no scales): each wave stages 32 rows x WTN floats,
 // then writes whole 16-byte chunks of output rows (chunk c of staged row r
 // at position c ^ (r % CPR)).
-template <int TM, int TN, int WTM, int WTN>
+template <typename E, int TM, int TN, int WTM, int WTN, int ACT>
 __device__ __forceinline__ void store_tile_staged_f32(const GemmParams &p, const f32x16 (&acc)[TM][TN],
                                                       int64_t row_base, int rows_valid, int n0, int wm, int wn,
                                                       int lane, uint4 *stg)
@@ -393,10 +410,31 @@ __device__ __forceinline__ void store_tile_staged_f32(const GemmParams &p, const
     const int rows_here = rows_valid - wm * WTM;
     const int cw = lane % CPR;
     const bool col_ok = cbase + cw * 4 < p.N;
+    constexpr int NQ = 32 / RPI;  // store instructions per 32 staged rows
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
         if (i * 32 >= rows_here)  // uniform: nothing left to store
             break;
+        // gradient epilogues: this block's pre-activations, all loads in flight before
+        // the staging (gate chunk, and for gated pairs the value chunk)
+        float4 pg[ACT >= ACT_RELU2_GRAD ? NQ : 1], pv[ACT == ACT_GLU_GRAD ? NQ : 1];
+        if constexpr (ACT >= ACT_RELU2_GRAD) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int rl = q * RPI + lane / CPR;
+                const int col = cbase + cw * 4;
+                const int pc = ACT == ACT_GLU_GRAD ? 16 * (col >> 3) + (col & 7) : col;
+                pg[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if constexpr (ACT == ACT_GLU_GRAD)
+                    pv[q] = pg[q];
+                if (col_ok && i * 32 + rl < rows_here) {
+                    const float *src = p.act_pre + (row_base + wm * WTM + i * 32 + rl) * p.ld_pre + pc;
+                    pg[q] = *reinterpret_cast<const float4 *>(src);
+                    if constexpr (ACT == ACT_GLU_GRAD)
+                        pv[q] = *reinterpret_cast<const float4 *>(src + 8);
+                }
+            }
+        }
 #pragma unroll
         for (int jn = 0; jn < TN; ++jn)
 #pragma unroll
@@ -409,11 +447,53 @@ __device__ __forceinline__ void store_tile_staged_f32(const GemmParams &p, const
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int r0 = 0; r0 < 32; r0 += RPI) {
-            const int rl = r0 + lane / CPR;
+        for (int q = 0; q < NQ; ++q) {
+            const int rl = q * RPI + lane / CPR;
             const uint4 v = stg[rl * CPR + (cw ^ (rl & (CPR - 1)))];
-            if (col_ok && i * 32 + rl < rows_here)
-                *reinterpret_cast<uint4 *>(p.C32 + (row_base + wm * WTM + i * 32 + rl) * p.ldc32 + cbase + cw * 4) = v;
+            if (!col_ok || i * 32 + rl >= rows_here)
+                continue;
+            const int64_t row = row_base + wm * WTM + i * 32 + rl;
+            const int col = cbase + cw * 4;
+            float s4[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+            if constexpr (ACT < ACT_RELU2_GRAD)
+                *reinterpret_cast<uint4 *>(p.C32 + row * p.ldc32 + col) = v;
+            if constexpr (ACT == ACT_RELU2) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float t = fmaxf(s4[r], 0.f);
+                    s4[r] = t * t;
+                }
+                store4(static_cast<E *>(p.C) + row * p.ldc + col, s4[0], s4[1], s4[2], s4[3]);
+            } else if constexpr (ACT == ACT_GLU) {
+                if ((cw & 3) >= 2)  // value chunk: written with its gate chunk
+                    continue;
+                // gate chunk: its values are two chunks on in the staged row
+                const uint4 u = stg[rl * CPR + ((cw + 2) ^ (rl & (CPR - 1)))];
+                const float u4[4] = {__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                     __uint_as_float(u.w)};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    s4[r] = glu_value(s4[r], u4[r]);
+                store4(static_cast<E *>(p.C) + row * p.ldc + (col >> 4) * 8 + (col & 15), s4[0], s4[1], s4[2], s4[3]);
+            } else if constexpr (ACT == ACT_RELU2_GRAD) {
+                const float a4[4] = {pg[q].x, pg[q].y, pg[q].z, pg[q].w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    s4[r] = a4[r] > 0.f ? 2.f * a4[r] * s4[r] : 0.f;
+                store4(static_cast<E *>(p.C) + row * p.ldc + col, s4[0], s4[1], s4[2], s4[3]);
+            } else if constexpr (ACT == ACT_GLU_GRAD) {
+                const int gc = 16 * (col >> 3) + (col & 7);
+                const float g4[4] = {pg[q].x, pg[q].y, pg[q].z, pg[q].w}, v4[4] = {pv[q].x, pv[q].y, pv[q].z, pv[q].w};
+                float dg[4], dv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sg = 1.f / (1.f + expf(-g4[r]));
+                    dg[r] = s4[r] * v4[r] * sg * (1.f + g4[r] * (1.f - sg));
+                    dv[r] = s4[r] * g4[r] * sg;
+                }
+                store4(static_cast<E *>(p.C) + row * p.ldc + gc, dg[0], dg[1], dg[2], dg[3]);
+                store4(static_cast<E *>(p.C) + row * p.ldc + gc + 8, dv[0], dv[1], dv[2], dv[3]);
+            }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -529,7 +609,7 @@ __device__ __forceinline__ void dma_mma(uint4 *__restrict__ na, uint4 *__restric
 // profiles.  BQ8: B holds E4M3 bytes (grouped, bf16 only; see tile_mma) with
 // per-column scales p.scaleB.
 template <typename E, int BM, int BN, int WM, int WN, int NS, bool GROUPED, int MINB = 1, int STAGE = 0,
-          bool BQ8 = false>
+          bool BQ8 = false, int ACT = ACT_NONE>
 __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmParams p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -686,13 +766,14 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     constexpr int WAVE_F = 32 * WTN * 4 / 16;  // 16-byte units of a wave's fp32 area
     constexpr bool F32_IN_A = NW <= 2 * ((BM * 8) / WAVE_F);
     constexpr bool F32_FITS = F32_IN_A || NW <= 2 * ((BN * CHB) / WAVE_F);
+    static_assert(ACT == ACT_NONE || (F32_FITS && !BQ8), "activation epilogues: fp32 staging");
     if constexpr (F32_FITS) {
-        if (p.c_split >= p.N && p.glu_from >= p.N && !p.bias32 && !cs) {
+        if (ACT != ACT_NONE || (p.c_split >= p.N && p.glu_from >= p.N && !p.bias32 && !cs)) {
             constexpr int PER = (F32_IN_A ? BM * 8 : BN * CHB) / WAVE_F;
             wait_vm_lgkm0<0>();
             __builtin_amdgcn_s_barrier();
             uint4 *stg = (F32_IN_A ? (wave < PER ? sA0 : sA1) : (wave < PER ? sB0 : sB1)) + (wave % PER) * WAVE_F;
-            store_tile_staged_f32<TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg);
+            store_tile_staged_f32<E, TM, TN, WTM, WTN, ACT>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg);
             return;
         }
     }

@@ -132,7 +132,7 @@ struct latentmoe_handle {
     void *w1b = nullptr, *w2b = nullptr;     // per expert [nb1 / bk][l][bk], [l / bk][m][bk]
     void *XA = nullptr;   // [Tmax, l + g S m_s] raw x-pass output (z, shared pre-activations)
     float *Apre = nullptr;  // [Pmax, nb1] routed pre-activations
-    void *dUH = nullptr, *dYp = nullptr, *dH = nullptr, *dA = nullptr, *dzp = nullptr, *dX = nullptr;
+    void *dUH = nullptr, *dYp = nullptr, *dA = nullptr, *dzp = nullptr, *dX = nullptr;
     void *xT = nullptr, *dXT = nullptr, *zhT = nullptr, *dyT = nullptr;
     void *HT = nullptr, *dYpT = nullptr, *zpT = nullptr, *dAT = nullptr;
     int *koff = nullptr;
@@ -404,12 +404,12 @@ void launch_dense(const GemmParams &gp, hipStream_t s)
     hip_check(hipGetLastError());
 }
 
-template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG, bool BQ8>
+template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG, bool BQ8, int ACT = ACT_NONE>
 void launch_grouped(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
 {
     const int64_t ntn = (gp.N + BN - 1) / BN;
     const int64_t grid = align_up(max_mtiles * ntn, 8);
-    gemm_kernel<E, BM, BN, WM, WN, NS, true, 1, TAG, BQ8><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
+    gemm_kernel<E, BM, BN, WM, WN, NS, true, 1, TAG, BQ8, ACT><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
     hip_check(hipGetLastError());
 }
 
@@ -487,10 +487,10 @@ void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_
 // fp8: the weights (B) are E4M3 bytes with column scales in gp.scaleB; for few
 // rows, 32x64 tiles of two waves and two stages (small LDS footprint, many
 // workgroups per CU) stream the half-size weights fastest.
-template <typename E, int TAG>
+template <typename E, int TAG, int ACT = ACT_NONE>
 void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hipStream_t s)
 {
-    if constexpr (sizeof(E) == 2) {
+    if constexpr (sizeof(E) == 2 && ACT == ACT_NONE) {
         if (fp8) {
             if (bm == kGroupBMSmall)
                 launch_grouped<E, kGroupBMSmall, 64, 1, 2, 2, TAG, true>(gp, max_mtiles, s);
@@ -500,11 +500,11 @@ void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hi
         }
     }
     if (bm == kGroupBMSmall)
-        launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, false>(gp, max_mtiles, s);
+        launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, false, ACT>(gp, max_mtiles, s);
     else if (sizeof(E) == 2 && gp.N % 256 == 0)
-        launch_grouped<E, kGroupBM, 256, 2, 4, 3, TAG, false>(gp, max_mtiles, s);
+        launch_grouped<E, kGroupBM, 256, 2, 4, 3, TAG, false, ACT>(gp, max_mtiles, s);
     else
-        launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG, false>(gp, max_mtiles, s);
+        launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG, false, ACT>(gp, max_mtiles, s);
 }
 
 int group_bm_for(int64_t P, int64_t N) { return (P / N < 32) ? kGroupBMSmall : kGroupBM; }
@@ -677,7 +677,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g1.n_mtiles = h->n_mtiles;
     g1.offsets = h->offsets;
     g1.scaleB = h->s1;
-    if (train) {  // raw pre-activations, fp32
+    if (train) {  // raw pre-activations in fp32 beside H
         g1.C32 = h->Apre;
         g1.ldc32 = p.nb1;
         g1.c_split = (int)p.nb1;
@@ -685,15 +685,12 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
         g1.glu_from = kNoColumn;
     }
     tm.begin(ST_GEMM1);
-    if (train)
-        grouped_gemm<E, kTagG1Raw>(g1, max_mt, gbm, false, s);
+    if (train && p.glu)
+        grouped_gemm<E, kTagG1Raw, ACT_GLU>(g1, max_mt, gbm, false, s);
+    else if (train)
+        grouped_gemm<E, kTagG1Raw, ACT_RELU2>(g1, max_mt, gbm, false, s);
     else
         grouped_gemm<E, kTagG1>(g1, max_mt, gbm, p.fp8, s);
-    if (train) {
-        expert_act8_kernel<E><<<dim3((unsigned)((P * p.m / 8 + 255) / 256)), dim3(256), 0, s>>>(
-            h->Apre, P, (int)p.m, (int)p.nb1, p.glu ? 1 : 0, static_cast<E *>(h->H));
-        hip_check(hipGetLastError());
-    }
     tm.end(ST_GEMM1);
 
     // 6: Y = H W2_e
@@ -824,7 +821,7 @@ int64_t n_x_padded(const Plan &p) { return align_up(p.n_x, 64); }
 // Bytes of the backward's weight layouts and workspace.
 struct BwdLayout {
     int64_t off_wx, off_wxf, off_wu, off_wuf, off_w1b, off_w2b, wtotal;
-    int64_t off_xa, off_apre, off_duh, off_dyp, off_dh, off_da, off_dzp, off_dx, off_xt, off_dxt, off_zht, off_dyt,
+    int64_t off_xa, off_apre, off_duh, off_dyp, off_da, off_dzp, off_dx, off_xt, off_dxt, off_zht, off_dyt,
         off_ht, off_dypt, off_zpt, off_dat, off_koff, off_dwx, off_dwu, off_dw1g, total;
     int64_t Tpad, Ppad;
 };
@@ -853,7 +850,6 @@ BwdLayout bwd_layout(const Plan &p)
     L.off_apre = take(4 * p.P_max * p.nb1);
     L.off_duh = take(es * p.Tmax * p.ld_zh);
     L.off_dyp = take(es * p.P_max * p.l);
-    L.off_dh = take(es * p.P_max * p.m);
     L.off_da = take(es * p.P_max * p.nb1);
     L.off_dzp = take(es * p.P_max * p.l);
     L.off_dx = take(es * p.Tmax * nxp);
@@ -913,7 +909,6 @@ void backward_setup(latentmoe_handle *h, hipStream_t s)
     h->Apre = reinterpret_cast<float *>(b + L.off_apre);
     h->dUH = b + L.off_duh;
     h->dYp = b + L.off_dyp;
-    h->dH = b + L.off_dh;
     h->dA = b + L.off_da;
     h->dzp = b + L.off_dzp;
     h->dX = b + L.off_dx;
@@ -995,7 +990,8 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
         static_cast<const E *>(h->dUH), p.ld_zh, static_cast<const E *>(h->Yp), h->pos, h->idx, h->gate, K,
         (int)p.l, N, static_cast<E *>(h->dYp), static_cast<E *>(h->dX), nxp);
     hip_check(hipGetLastError());
-    // dH = dY_perm W2_e^T, then the gradient of the routed pre-activations
+    // dH = dY_perm W2_e^T; its epilogue writes the gradient of the routed
+    // pre-activations dA = dH act'(A) instead of dH
     GemmParams gb{};
     gb.A = h->dYp;
     gb.lda = p.l;
@@ -1004,20 +1000,23 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     gb.ldb = p.bk_b;
     gb.b_kstep = p.m * p.bk_b * es;
     gb.strideB = p.m * p.l;
-    gb.C = h->dH;
-    gb.ldc = p.m;
+    gb.C = h->dA;
+    gb.ldc = p.nb1;
+    gb.act_pre = h->Apre;
+    gb.ld_pre = p.nb1;
     gb.N = (int)p.m;
     gb.K = (int)p.l;
     gb.tile_expert = h->tile_expert;
     gb.tile_row0 = h->tile_row0;
     gb.n_mtiles = h->n_mtiles;
     gb.offsets = h->offsets;
-    grouped_gemm<E, kTagDgrad>(gb, max_mt, gbm, false, s);
-    expert_act_grad8_kernel<E><<<dim3((unsigned)((P * p.m / 8 + 255) / 256)), dim3(256), 0, s>>>(
-        h->Apre, static_cast<const E *>(h->dH), P, (int)p.m, (int)p.nb1, gl, static_cast<E *>(h->dA));
-    hip_check(hipGetLastError());
+    if (p.glu)
+        grouped_gemm<E, kTagDgrad, ACT_GLU_GRAD>(gb, max_mt, gbm, false, s);
+    else
+        grouped_gemm<E, kTagDgrad, ACT_RELU2_GRAD>(gb, max_mt, gbm, false, s);
     // dz_perm = dA W1_e^T; dz[t] = sum over t's slots -> dX[:, N' .. N' + l)
     GemmParams gc = gb;
+    gc.act_pre = nullptr;
     gc.A = h->dA;
     gc.lda = p.nb1;
     gc.a_bytes = P * p.nb1 * es;
