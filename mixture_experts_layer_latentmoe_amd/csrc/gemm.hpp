@@ -79,6 +79,8 @@ struct GemmParams {
     // an empty range gives zeros) and writes output rows e M .. e M + M - 1
     const int *k_offsets;
     int n_batches;
+    // MN-major GEMM (gemm_tn.hpp): size of the B buffer in bytes
+    int64_t b_bytes;
     // pre-activations (fp32, row stride ld_pre) read by the gradient
     // epilogues (gemm_kernel's ACT 3 and 4)
     const float *act_pre;

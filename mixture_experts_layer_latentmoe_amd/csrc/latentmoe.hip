@@ -35,6 +35,7 @@
 #include "common.hpp"
 #include "dispatch.hpp"
 #include "gemm.hpp"
+#include "gemm_tn.hpp"
 #include "repack.hpp"
 #include "router.hpp"
 #include "skinny.hpp"
@@ -789,6 +790,34 @@ double log10_comb(double n, double k) { return (std::lgamma(n + 1) - std::lgamma
 
 // ---- backward pass -----------------------------------------------------
 
+// Weight gradients from MN-major bf16 operands (gemm_tn.hpp): 128x128 tiles,
+// one grid over every batch.
+template <int TAG>
+void launch_tn(const GemmParams &gp, hipStream_t s)
+{
+    const int64_t per = ((gp.M + 127) / 128) * ((gp.N + 127) / 128);
+    const int64_t tiles = (gp.k_offsets ? gp.n_batches : 1) * per;
+    gemm_tn_kernel<TAG><<<dim3((unsigned)align_up(tiles, 8)), dim3(256), 0, s>>>(gp);
+    hip_check(hipGetLastError());
+}
+
+// z_perm[p] = z[perm[p]] (the first l columns of the recompute's raw x-pass
+// output XA), 16 bytes per thread.
+template <typename E>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const E *__restrict__ src, int64_t ld_src,
+                                                          const int *__restrict__ perm, int64_t P, int cols,
+                                                          E *__restrict__ dst)
+{
+    constexpr int VEC = 16 / (int)sizeof(E);
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int per = cols / VEC;
+    if (q >= P * per)
+        return;
+    const int64_t r = q / per;
+    const int c = (int)(q - r * per) * VEC;
+    *reinterpret_cast<uint4 *>(dst + r * cols + c) = *reinterpret_cast<const uint4 *>(src + perm[r] * ld_src + c);
+}
+
 template <typename E, int TAG>
 void launch_batched_k(const GemmParams &gp, hipStream_t s)
 {
@@ -853,14 +882,18 @@ BwdLayout bwd_layout(const Plan &p)
     L.off_da = take(es * p.P_max * p.nb1);
     L.off_dzp = take(es * p.P_max * p.l);
     L.off_dx = take(es * p.Tmax * nxp);
-    L.off_xt = take(es * p.d * L.Tpad);
-    L.off_dxt = take(es * nxp * L.Tpad);
-    L.off_zht = take(es * p.ld_zh * L.Tpad);
-    L.off_dyt = take(es * p.d * L.Tpad);
-    L.off_ht = take(es * p.m * L.Ppad);
-    L.off_dypt = take(es * p.l * L.Ppad);
-    L.off_zpt = take(es * p.l * L.Ppad);
-    L.off_dat = take(es * p.nb1 * L.Ppad);
+    // transposed, zero-padded operands of the fp32 layers' weight gradients;
+    // bf16 layers read the activations in place (gemm_tn.hpp) and need only
+    // z_perm (P x l, in the zpT area)
+    const bool tr = es == 4;
+    L.off_xt = take(tr ? es * p.d * L.Tpad : 0);
+    L.off_dxt = take(tr ? es * nxp * L.Tpad : 0);
+    L.off_zht = take(tr ? es * p.ld_zh * L.Tpad : 0);
+    L.off_dyt = take(tr ? es * p.d * L.Tpad : 0);
+    L.off_ht = take(tr ? es * p.m * L.Ppad : 0);
+    L.off_dypt = take(tr ? es * p.l * L.Ppad : 0);
+    L.off_zpt = take(tr ? es * p.l * L.Ppad : es * p.P_max * p.l);
+    L.off_dat = take(tr ? es * p.nb1 * L.Ppad : 0);
     L.off_koff = take(4 * (p.N + 1));
     L.off_dwx = take(4 * p.d * p.n_x);
     L.off_dwu = take(4 * p.ld_zh * p.d);
@@ -877,11 +910,17 @@ bool bwd_fits(const Plan &p)
     const int64_t es = p.esize, lim = (int64_t(1) << 31) - 1;
     const int64_t sizes[] = {es * p.d * n_x_padded(p), es * p.ld_zh * p.d, es * p.l * p.nb1, es * p.m * p.l,
                              4 * p.P_max * p.nb1, es * p.P_max * p.nb1, es * p.Tmax * n_x_padded(p),
-                             es * n_x_padded(p) * L.Tpad, es * p.d * L.Tpad, es * p.ld_zh * L.Tpad,
-                             es * p.m * L.Ppad, es * p.l * L.Ppad, es * p.nb1 * L.Ppad};
+                             es * p.P_max * p.m, es * p.P_max * p.l};
     for (int64_t v : sizes)
         if (v > lim)
             return false;
+    if (es == 4) {  // the transposed operands of the fp32 layers' weight gradients
+        const int64_t tr[] = {es * n_x_padded(p) * L.Tpad, es * p.d * L.Tpad, es * p.ld_zh * L.Tpad,
+                              es * p.m * L.Ppad, es * p.l * L.Ppad, es * p.nb1 * L.Ppad};
+        for (int64_t v : tr)
+            if (v > lim)
+                return false;
+    }
     return true;
 }
 
@@ -945,6 +984,93 @@ void backward_setup(latentmoe_handle *h, hipStream_t s)
     retile_kernel<E, BK><<<dim3((unsigned)(p.l / BK), (unsigned)(p.m / BK), (unsigned)p.N), dim3(256), 0, s>>>(
         static_cast<const E *>(h->w2T), (int)p.m, (int)p.l, static_cast<E *>(h->w2b));
     hip_check(hipGetLastError());
+}
+
+// Weight gradients of a bf16 layer, read straight from the row-major
+// activations by the MN-major GEMM: dW_x = x^T [ds | dz | d pre_s],
+// [dW_up ; dW2_s] = [u | h_s]^T dy, and per expert dW2 = H^T dY_perm and
+// [dW_g | dW1] = z_perm^T dA over the expert's dispatch rows.
+void weight_grads_tn(latentmoe_handle *h, const void *x, const void *dy, int T, hipStream_t s,
+                     const latentmoe_grads *gr)
+{
+    const Plan &p = h->plan;
+    const int N = (int)p.N;
+    const int64_t P = (int64_t)T * p.K, es = 2, nxp = n_x_padded(p), ldxa = p.n_x - p.N;
+    auto tn = [&](const void *A, int64_t lda, int64_t a_rows, const void *B, int64_t ldb, int M, int Nn, float *C) {
+        GemmParams g{};
+        g.A = A;
+        g.lda = lda;
+        g.a_bytes = a_rows * lda * es;
+        g.B = B;
+        g.ldb = ldb;
+        g.b_bytes = a_rows * ldb * es;
+        g.M = M;
+        g.N = Nn;
+        g.K = (int)a_rows;
+        g.C32 = C;
+        g.ldc32 = Nn;
+        g.c_split = Nn;
+        g.group_m = 8;
+        return g;
+    };
+    if (gr->dw_router || gr->dw_down || gr->dw1_shared || gr->dw1_shared_gate) {
+        launch_tn<kTagWgrad>(tn(x, p.d, T, h->dX, nxp, (int)p.d, (int)p.n_x, h->dWx), s);
+        auto split = [&](float *dst, int rows, int col0, int nb, int w, int sel) {
+            const int64_t n = (int64_t)nb * rows * w;
+            split_cols_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(h->dWx, p.n_x, rows, col0, nb,
+                                                                                    w, sel, dst);
+            hip_check(hipGetLastError());
+        };
+        if (gr->dw_router)
+            split(gr->dw_router, (int)p.d, 0, 1, N, -1);
+        if (gr->dw_down)
+            split(gr->dw_down, (int)p.d, N, 1, (int)p.l, -1);
+        if (p.S > 0 && gr->dw1_shared)
+            split(gr->dw1_shared, (int)p.d, (int)(p.N + p.l), (int)p.S, (int)p.ms, p.glu ? 1 : -1);
+        if (p.S > 0 && p.glu && gr->dw1_shared_gate)
+            split(gr->dw1_shared_gate, (int)p.d, (int)(p.N + p.l), (int)p.S, (int)p.ms, 0);
+    }
+    if (gr->dw_up || gr->dw2_shared) {
+        launch_tn<kTagWgrad>(tn(h->zh, p.ld_zh, T, dy, p.d, (int)p.ld_zh, (int)p.d, h->dWu), s);
+        if (gr->dw_up)
+            hip_check(hipMemcpyAsync(gr->dw_up, h->dWu, 4 * p.l * p.d, hipMemcpyDeviceToDevice, s));
+        if (p.S > 0 && gr->dw2_shared)
+            hip_check(hipMemcpyAsync(gr->dw2_shared, h->dWu + p.l * p.d, 4 * p.S * p.ms * p.d,
+                                     hipMemcpyDeviceToDevice, s));
+    }
+    if (h->cfg.has_router_bias && gr->db_router) {
+        col_sum_kernel<bf16><<<dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s>>>(
+            static_cast<const bf16 *>(h->dX), nxp, T, N, gr->db_router);
+        hip_check(hipGetLastError());
+    }
+    if (gr->dw2) {
+        GemmParams g = tn(h->H, p.m, P, h->dYp, p.l, (int)p.m, (int)p.l, gr->dw2);
+        g.k_offsets = h->offsets;
+        g.n_batches = N;
+        launch_tn<kTagWgradE>(g, s);
+    }
+    if (gr->dw1 || (p.glu && gr->dw1_gate)) {
+        const int64_t n = P * p.l / 8;
+        gather_rows_kernel<bf16><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+            static_cast<const bf16 *>(h->XA), ldxa, h->perm, P, (int)p.l, static_cast<bf16 *>(h->zpT));
+        hip_check(hipGetLastError());
+        float *dst = p.glu ? h->dW1g : gr->dw1;
+        GemmParams g = tn(h->zpT, p.l, P, h->dA, p.nb1, (int)p.l, (int)p.nb1, dst);
+        g.k_offsets = h->offsets;
+        g.n_batches = N;
+        launch_tn<kTagWgradE>(g, s);
+        if (p.glu) {  // [N' l, 2m] gated pairs -> W1 (value) and W_g (gate)
+            const int64_t nn = p.N * p.l * p.m;
+            for (int sel = 0; sel < 2; ++sel) {
+                float *out = sel ? gr->dw1 : gr->dw1_gate;
+                if (!out)
+                    continue;
+                split_cols_kernel<<<dim3((unsigned)((nn + 255) / 256)), dim3(256), 0, s>>>(
+                    h->dW1g, p.nb1, (int)(p.N * p.l), 0, 1, (int)p.m, sel, out);
+                hip_check(hipGetLastError());
+            }
+        }
+    }
 }
 
 template <typename E>
@@ -1053,6 +1179,10 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     }
 
     // ---- weight gradients (fp32), sums over tokens / an expert's rows ----
+    if constexpr (sizeof(E) == 2) {
+        weight_grads_tn(h, x, dy, T, s, gr);
+        return;
+    }
     auto wgrad = [&](const void *A, int64_t M, const void *B, int64_t Nn, int64_t lda, float *C) {
         GemmParams g{};
         g.A = A;
