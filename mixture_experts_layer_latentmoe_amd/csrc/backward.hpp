@@ -19,18 +19,6 @@ __device__ __forceinline__ float bwd_sigmoid(float g) { return 1.f / (1.f + expf
 // Column j of a gated block layout: the gate and value column of output j.
 __device__ __forceinline__ int glu_gate_col(int j) { return 16 * (j >> 3) + (j & 7); }
 
-// Activation of the hidden layer from its pre-activation: relu(a)^2, or
-// silu(gate) * value for gated experts.
-__device__ __forceinline__ float act_of(const float *pre, int j, bool gated)
-{
-    if (!gated) {
-        const float a = fmaxf(pre[j], 0.f);
-        return a * a;
-    }
-    const int c = glu_gate_col(j);
-    return bwd_silu(pre[c]) * pre[c + 8];
-}
-
 // zh[t] = [z | act(shared pre-activations)] from the x-pass's raw output.
 template <typename E>
 __global__ __launch_bounds__(256) void xpass_act_kernel(const E *__restrict__ XA, int64_t ld_xa, int T, int l, int sms,
