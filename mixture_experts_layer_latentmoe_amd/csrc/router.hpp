@@ -50,6 +50,78 @@ __device__ __forceinline__ float wave_sum_f32(float v)
     return v;
 }
 
+// Steps 1-3 for one token (one wave): the K' selected experts, each
+// selected lane's rank and renormalised gate (lanes < K' hold slot `lane`).
+// wkey, wexp: this wave's K'-entry LDS scratch.
+template <int NPL>
+__device__ __forceinline__ void select_token(const float *__restrict__ row, int N, int K, int lane, unsigned *wkey,
+                                             int *wexp, int &me_out, int &rank_out, float &gate_out)
+{
+    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    unsigned key[NPL];
+    float val[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int e = lane + 64 * j;
+        val[j] = (e < N) ? row[e] : 0.f;
+        key[j] = (e < N) ? ordered_key(val[j]) : 0u;
+    }
+    // 1. the K'-th largest key: largest th with #{key >= th} >= K'
+    unsigned th = 0u;
+    for (int b = 31; b >= 0; --b) {
+        const unsigned cand = th | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j)
+            cnt += wave_count(key[j] >= cand);
+        if (cnt >= K)
+            th = cand;
+    }
+    int need = K;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j)
+        need -= wave_count(key[j] > th);
+    // selection, compacted into LDS slots in (j, lane) order
+    int base = 0;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const bool tie = key[j] == th;
+        const unsigned long long tmask = __ballot(tie);
+        const int tie_rank = __popcll(tmask & lt_mask);   // among this j's ties, lower lanes first
+        const bool sel = key[j] > th || (tie && tie_rank < need);
+        need -= min(need, (int)__popcll(tmask));
+        const unsigned long long smask = __ballot(sel);
+        if (sel) {
+            const int slot = base + __popcll(smask & lt_mask);
+            wkey[slot] = key[j];
+            wexp[slot] = lane + 64 * j;
+        }
+        base += __popcll(smask);
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    // 2. rank of slot `lane` by (key descending, index ascending)
+    unsigned mk = 0u;
+    int me = 0x7fffffff, rank = 0;
+    if (lane < K) {
+        mk = wkey[lane];
+        me = wexp[lane];
+        for (int q = 0; q < K; ++q) {
+            const unsigned ok = wkey[q];
+            const int oe = wexp[q];
+            rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
+        }
+    }
+    // 3. gates
+    const float s_mine = (lane < K) ? row[me < N ? me : 0] : 0.f;
+    const float s_top = __shfl(s_mine, __ffsll((long long)__ballot(lane < K && rank == 0)) - 1, 64);
+    const float g = (lane < K) ? expf(s_mine - s_top) : 0.f;
+    const float gsum = wave_sum_f32(g);
+    me_out = me;
+    rank_out = rank;
+    gate_out = g / gsum;
+}
+
 // NPL = ceil(N' / 64) scores held per lane (expert e = lane + 64 j).
 template <int NPL>
 __global__ __launch_bounds__(64 * kSelectWaves) void router_select_kernel(
@@ -67,75 +139,18 @@ __global__ __launch_bounds__(64 * kSelectWaves) void router_select_kernel(
         s_mask[e] = 0u;
     unsigned *wkey = s_key + wave * K;
     int *wexp = s_exp + wave * K;
-    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
     for (int r = wave; r < kRouterTokens; r += kSelectWaves) {
         const int t = t0 + r;
         if (t >= T)
             break;
         const float *row = scores + (int64_t)t * N;
-        unsigned key[NPL];
-        float val[NPL];
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-            const int e = lane + 64 * j;
-            val[j] = (e < N) ? row[e] : 0.f;
-            key[j] = (e < N) ? ordered_key(val[j]) : 0u;
-        }
-        // 1. the K'-th largest key: largest th with #{key >= th} >= K'
-        unsigned th = 0u;
-        for (int b = 31; b >= 0; --b) {
-            const unsigned cand = th | (1u << b);
-            int cnt = 0;
-#pragma unroll
-            for (int j = 0; j < NPL; ++j)
-                cnt += wave_count(key[j] >= cand);
-            if (cnt >= K)
-                th = cand;
-        }
-        int need = K;
-#pragma unroll
-        for (int j = 0; j < NPL; ++j)
-            need -= wave_count(key[j] > th);
-        // selection, compacted into LDS slots in (j, lane) order
-        int base = 0;
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-            const bool tie = key[j] == th;
-            const unsigned long long tmask = __ballot(tie);
-            const int tie_rank = __popcll(tmask & lt_mask);   // among this j's ties, lower lanes first
-            const bool sel = key[j] > th || (tie && tie_rank < need);
-            need -= min(need, (int)__popcll(tmask));
-            const unsigned long long smask = __ballot(sel);
-            if (sel) {
-                const int slot = base + __popcll(smask & lt_mask);
-                wkey[slot] = key[j];
-                wexp[slot] = lane + 64 * j;
-            }
-            base += __popcll(smask);
-        }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        // 2. rank of slot `lane` by (key descending, index ascending)
-        unsigned mk = 0u;
-        int me = 0x7fffffff, rank = 0;
-        if (lane < K) {
-            mk = wkey[lane];
-            me = wexp[lane];
-            for (int q = 0; q < K; ++q) {
-                const unsigned ok = wkey[q];
-                const int oe = wexp[q];
-                rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
-            }
-        }
-        // 3. gates
-        const float s_mine = (lane < K) ? row[me < N ? me : 0] : 0.f;
-        const float s_top = __shfl(s_mine, __ffsll((long long)__ballot(lane < K && rank == 0)) - 1, 64);
-        const float g = (lane < K) ? expf(s_mine - s_top) : 0.f;
-        const float gsum = wave_sum_f32(g);
+        int me, rank;
+        float gate;
+        select_token<NPL>(row, N, K, lane, wkey, wexp, me, rank, gate);
         if (lane < K) {
             idx_out[(int64_t)t * K + rank] = me;
-            gate_out[(int64_t)t * K + rank] = g / gsum;
+            gate_out[(int64_t)t * K + rank] = gate;
             s_idx[r * K + rank] = me;
         }
         __builtin_amdgcn_wave_barrier();
