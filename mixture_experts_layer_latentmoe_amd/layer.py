@@ -83,7 +83,7 @@ class LatentMoE:
             dev[k] = (torch.from_numpy(np.ascontiguousarray(arrays[k], dtype=np.float32).copy()).to(self.device)
                       if fp8 and (gated or k != "w1g_scale") else None)
         b = arrays.get("b_router")
-        dev["b_router"] = (torch.from_numpy(np.asarray(b, np.float32)).to(self.device)
+        dev["b_router"] = (torch.from_numpy(np.array(b, np.float32)).to(self.device)
                            if (shape.has_bias and b is not None) else None)
 
         def ptr(t):
