@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="also time the layer's backward pass (its forward recompute included) over the same "
                          "steps and report it under \"backward\"")
+    ap.add_argument("--graph", action="store_true",
+                    help="also replay the forward from captured HIP graphs (one per weight copy) over the same "
+                         "steps and report it under \"graph\"; the headline value stays the eager forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (3 launches) so that profiler "
                          "byte counters can be scaled by a kernel of known traffic")
@@ -237,6 +240,33 @@ def main():
                 "avg_us": timed["avg_us"], "launches": timed["launches"],
                 "traffic": profiled_traffic(sh.name, dom)}
     total_flop = sum(f for f, _ in work.values() if f)
+    graph_out = None
+    if args.graph:
+        # one graph per weight copy, captured on a side stream after a warm-up
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for L in layers:
+                L.forward(x, y)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for L in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                L.forward(x, y)
+            graphs.append(g)
+        for i in range(max(args.warmup, R)):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        tg0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        tg = (time.perf_counter() - tg0) / args.steps
+        graph_out = {"ms_per_step": round(tg * 1e3, 4), "tokens_per_s": round(T / tg, 1),
+                     "note": "forward replayed from HIP graphs, same weight-copy rotation"}
+        del graphs
     bwd = None
     if args.backward and sh.expert_dtype != "fp8":
         # algorithmic work: the recomputed forward (no up-projection), the
@@ -280,6 +310,7 @@ def main():
         "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
         "roofline": roof, "cpu_baseline": cpu, "stages": stage_out,
         **({"backward": bwd} if bwd else {}),
+        **({"graph": graph_out} if graph_out else {}),
         "stages_note": "per-stage HIP-event times from an untimed pass of min(steps, 10) forwards; "
                        "roofline.avg_us is the dominant kernel timed over the timed region",
     }
