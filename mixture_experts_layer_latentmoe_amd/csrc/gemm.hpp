@@ -116,6 +116,15 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned o
 
 constexpr unsigned kOOB = 0x80000000u;  // offset that is always out of range
 
+// 16-byte store of a staged epilogue, marked non-temporal (streamed through
+// L2 without displacing the operands other tiles still read).
+__device__ __forceinline__ void store16_stream(void *base, int64_t byte_off, uint4 v)
+{
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(__builtin_bit_cast(v4u, v),
+                                reinterpret_cast<v4u *>(static_cast<char *>(base) + byte_off));
+}
+
 #define LMOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // vmcnt <= N and lgkmcnt == 0 (gfx9 s_waitcnt: vmcnt[3:0] + vmcnt[15:14],
@@ -388,7 +397,7 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
             const int rl = r0 + lane / CPR;
             const uint4 v = stg[rl * CPR + (cw ^ (rl & (CPR - 1)))];
             if (col_ok && i * 32 + rl < rows_here)
-                *reinterpret_cast<uint4 *>(C + (row_base + wm * WTM + i * 32 + rl) * p.ldc + cbase + cw * (16 / ES)) = v;
+                store16_stream(C, ((row_base + wm * WTM + i * 32 + rl) * p.ldc + cbase + cw * (16 / ES)) * ES, v);
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -458,7 +467,7 @@ __device__ __forceinline__ void store_tile_staged_f32(const GemmParams &p, const
             const int col = cbase + cw * 4;
             float s4[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
             if constexpr (ACT < ACT_RELU2_GRAD)
-                *reinterpret_cast<uint4 *>(p.C32 + row * p.ldc32 + col) = v;
+                store16_stream(p.C32, (row * p.ldc32 + col) * 4, v);
             if constexpr (ACT == ACT_RELU2) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -559,7 +568,7 @@ __device__ __forceinline__ void store_tile_staged_glu(const GemmParams &p, const
             const int rl = r0 + lane / CPR;
             const uint4 v = stg[rl * CPR + (cw ^ (rl & (CPR - 1)))];
             if (col_ok && i * 32 + rl < rows_here)
-                *reinterpret_cast<uint4 *>(C + (row_base + wm * WTM + i * 32 + rl) * p.ldc + cbase + cw * (16 / ES)) = v;
+                store16_stream(C, ((row_base + wm * WTM + i * 32 + rl) * p.ldc + cbase + cw * (16 / ES)) * ES, v);
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
