@@ -11,20 +11,27 @@
 // row parity and the swizzled position then give 16 distinct 16-byte bank
 // groups (the plain c ^ (r & 7) maps rows r and r + 8 to the same banks).
 //
-// Global loads are buffer loads: a row outside the valid range gets an
+// Global loads are buffer loads with the LDS bit (HBM/L2 straight into the
+// LDS stage, no staging registers): a row outside the valid range gets an
 // offset beyond the buffer's size, and the hardware returns zeros for it, so
-// the main loop has no branches.  The next k-tile is loaded into registers
-// while the current one is multiplied from LDS.
+// the main loop has no branches.  With NS stages, k-tiles j + 1 .. j + NS - 1
+// are in flight while k-tile j is multiplied; one barrier per k-tile.
 //
 // Dense mode: rows = M; tiles walk grouped-by-M order inside each XCD.
 // Grouped mode (routed experts): the dispatch rows of expert e are the
 // contiguous range [offsets[e], offsets[e+1]); a device-built tile table
 // lists (expert, first row) for every BM-row tile, so no host round trip is
 // needed.  A rows may be gathered through `gather` (dispatch row -> token).
+// Batched-K mode: products that differ only in their K range (k_offsets).
+// Split-K (dense, few rows): fp32 partials and a fixed-order reduce kernel.
 //
 // Epilogue: the first c_split columns (router scores) are stored in fp32 with
 // a per-column bias; the rest go to C, where columns >= relu2_from get
-// relu(v)^2 (squared-ReLU expert activation), rounded to E.
+// relu(v)^2 (squared-ReLU expert activation) and, from glu_from on, gated
+// pairs give silu(gate) * value, rounded to E.  Whole tiles of E outputs and
+// all-fp32 outputs are staged through LDS and written as whole rows with
+// non-temporal stores; the compile-time ACT variants add the expert
+// activation beside fp32 sums, or replace dH by the activation gradient.
 //
 // E4M3 expert weights (grouped GEMMs of a bf16 layer): B tiles hold the bytes
 // (64 per row and k-tile), fragments are widened to bf16 in registers (exact:
