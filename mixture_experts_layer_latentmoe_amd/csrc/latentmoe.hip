@@ -1,4 +1,5 @@
-// LatentMoE layer forward pass on MI355X (gfx950): host plan and C ABI.
+// LatentMoE layer on MI355X (gfx950): host plan, forward and backward
+// launch sequences, and the C ABI.
 //
 // The layer is the one of the explainer page "LatentMoE: NVIDIA's Latent
 // Mixture of Experts Explained Through Equations, Architecture, Code and
@@ -11,15 +12,21 @@
 //                       in fp32 (+ bias), z, and the squared-ReLU hidden layer of
 //                       the shared experts -- one MFMA pass over x
 //   1 router_select     top-K', gates, chunk ranks / counts
-//   2 dispatch_scan     per-expert scan over 32-token chunks, counts
+//   2 dispatch_scan     per-expert scan over 16-token chunks, counts
 //   3 dispatch_finalize offsets, grouped-GEMM tile table, pos[t,k], perm_token[p]
+//                       (up to 64 chunks: 2 and 3 in one workgroup, one launch)
 //   4 grouped_gemm1     H = relu(z[perm] W1_e)^2 per expert
 //   5 grouped_gemm2     Y = H W2_e per expert
 //   6 combine           u[t] = sum_k gate[t,k] Y[pos[t,k]], written over z
 //   7 gemm_up_shared2   y = [u | h_s] [W_up ; W2_s]
-// Stages 0 and 8 fold the router and the always-on shared experts into the
+// Stages 0 and 7 fold the router and the always-on shared experts into the
 // down- and up-projection GEMMs: all of them read x (resp. produce y) at
-// width d, so one pass over x and one output write serve every path.
+// width d, so one pass over x and one output write serve every path.  Up to
+// 64 tokens, stages 0 and 7 run the few-row kernel (skinny.hpp).
+//
+// The backward (backward_impl) recomputes the forward with raw outputs and
+// then runs the data-gradient and weight-gradient products (backward.hpp,
+// gemm_tn.hpp).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
