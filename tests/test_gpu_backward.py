@@ -118,6 +118,14 @@ def test_backward_shapes(cfg, dtype):
     _check(random_workload(shape(dtype=dtype, **cfg), seed=cfg["T"] + 3))
 
 
+@pytest.mark.parametrize("T", [1, 2])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_one_and_two_tokens(T, dtype):
+    # every expert but K' (or 2 K') has no rows: their bank gradients are zeros
+    cfg = dict(T=T, d=256, l=128, m=128, n_experts=16, top_k=4, n_shared=1, m_shared=192, alpha=2)
+    _check(random_workload(shape(dtype=dtype, **cfg), seed=40 + T))
+
+
 @pytest.mark.parametrize("T", [300, 64])
 def test_backward_readme_widths(T):
     _check(make_workload(get_config("readme_acc"), T=T), experts=[0, 7, 100, 255])
