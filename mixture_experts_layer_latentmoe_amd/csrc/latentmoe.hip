@@ -99,7 +99,7 @@ struct Plan {
     int64_t max_mtiles;  // tile table capacity (smallest grouped M tile)
 };
 
-constexpr int kGroupBM = 128, kGroupBMSmall = 32, kMinGroupBM = 32;
+constexpr int kGroupBM = 128, kGroupBMBig = 256, kGroupBMSmall = 32, kMinGroupBM = 32;
 constexpr int kNoColumn = 1 << 30;  // relu2_from / glu_from: no such columns
 constexpr int kSplitKMaxRows = 256, kSplitKMax = 16;
 
@@ -488,10 +488,12 @@ void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_
     hip_check(hipGetLastError());
 }
 
-// Grouped GEMMs: 128x256 tiles (8 waves, three LDS stages, one workgroup per
-// CU) when N is a multiple of 256, else 128x128 (two workgroups per CU); when
-// experts average few rows (decode), 32x128 tiles with four LDS stages so
-// that more weight bytes are in flight.
+// Grouped GEMMs: the forward of a bf16 layer with bf16 expert banks takes
+// 256x256 tiles (8 waves, two LDS stages) on a 256-row tile table (bm =
+// kGroupBMBig); otherwise 128x256 tiles (8 waves, three LDS stages, one
+// workgroup per CU) when N is a multiple of 256, else 128x128 (two
+// workgroups per CU); when experts average few rows (decode), 32x128 tiles
+// with four LDS stages so that more weight bytes are in flight.
 // fp8: the weights (B) are E4M3 bytes with column scales in gp.scaleB; for few
 // rows, 32x64 tiles of two waves and two stages (small LDS footprint, many
 // workgroups per CU) stream the half-size weights fastest.
@@ -499,6 +501,10 @@ template <typename E, int TAG, int ACT = ACT_NONE>
 void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hipStream_t s)
 {
     if constexpr (sizeof(E) == 2 && ACT == ACT_NONE) {
+        if (bm == kGroupBMBig && !fp8) {
+            launch_grouped<E, kGroupBMBig, 256, 4, 2, 2, TAG, false>(gp, max_mtiles, s);
+            return;
+        }
         if (fp8) {
             if (bm == kGroupBMSmall)
                 launch_grouped<E, kGroupBMSmall, 64, 1, 2, 2, TAG, true>(gp, max_mtiles, s);
@@ -507,6 +513,8 @@ void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hi
             return;
         }
     }
+    if (bm != kGroupBMSmall && bm != kGroupBM)  // a tile table these kernels cannot walk
+        throw HipError{hipErrorInvalidValue};
     if (bm == kGroupBMSmall)
         launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, false, ACT>(gp, max_mtiles, s);
     else if (sizeof(E) == 2 && gp.N % 256 == 0)
@@ -515,7 +523,15 @@ void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hi
         launch_grouped<E, kGroupBM, 128, 2, 2, 2, TAG, false, ACT>(gp, max_mtiles, s);
 }
 
-int group_bm_for(int64_t P, int64_t N) { return (P / N < 32) ? kGroupBMSmall : kGroupBM; }
+// Rows per tile of the grouped GEMMs' tile table: 32 when experts average
+// fewer than 32 rows; else 256 where the 256x256 kernel serves both grouped
+// GEMMs (big: the forward of a bf16 layer with bf16 banks; measured on the
+// layer at t_exp = 256..512 rows per expert, its lower cost per row outweighs
+// the longer padding of each expert's last tile), else 128.
+int group_bm_for(int64_t P, int64_t N, bool big = false)
+{
+    return (P / N < 32) ? kGroupBMSmall : big ? kGroupBMBig : kGroupBM;
+}
 
 template <int NPL>
 void launch_select_n(latentmoe_handle *h, int T, hipStream_t s)
@@ -582,7 +598,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     const int64_t P = (int64_t)T * K;
     const int nchunks = (T + kRouterTokens - 1) / kRouterTokens;
     const int es = p.esize;
-    const int gbm = group_bm_for(P, N);
+    const int gbm = group_bm_for(P, N, !train && !p.fp8 && es == 2);
     const int64_t max_mt = max_mtiles_for(P, N, gbm);
     StageTimer tm{h, s, -1};
     if (h->prof && h->prof_used < h->prof_cap)

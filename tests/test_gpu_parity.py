@@ -100,6 +100,32 @@ def test_zero_router_ties_fill_first_experts():
     G.check_stages(out, wl, ref, toks, np.ones(len(toks), dtype=bool))
 
 
+@pytest.mark.parametrize("T", [255, 256, 257, 513])
+def test_expert_rows_at_tile_boundaries(T):
+    """W_r = 0 on a bf16 prefill shape: experts 0..3 hold exactly T rows each
+    and the other 12 none, so each expert's last grouped-GEMM tile (256 rows
+    in the bf16 forward) is full, one row short or one row long.  Every token
+    is checked, stage by stage."""
+    sh = shape(T=T, d=256, l=128, m=192, n_experts=16, top_k=4, n_shared=1, m_shared=128, dtype="bf16")
+    arr = random_arrays(sh, np.random.default_rng(T))
+    arr["w_router"] = np.zeros_like(arr["w_router"])
+    wl = workload_from_arrays(sh, arr)
+    out = G.run_gpu(wl)
+    assert np.all(out["idx"] == np.arange(4, dtype=np.int32)[None, :])
+    assert np.array_equal(out["counts"], np.array([T] * 4 + [0] * 12, dtype=out["counts"].dtype))
+    toks = np.arange(T)
+    ref = oracle.forward(wl, tokens=toks, want=("logits", "idx", "gate", "z", "h", "o", "u", "hs", "y"))
+    G.check_stages(out, wl, ref, toks, np.ones(T, dtype=bool))
+
+
+def test_expert_rows_straddle_tile_height():
+    """2048 tokens over 16 experts with K' = 2: about 256 rows per expert,
+    some just under and some just over one 256-row tile."""
+    sh = shape(T=2048, d=256, l=128, m=192, n_experts=16, top_k=2, n_shared=1, m_shared=128, dtype="bf16")
+    out = _full_check(random_workload(sh, seed=11))
+    assert out["counts"].min() < 256 < out["counts"].max()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_exact_score_ties_follow_index_order(dtype):
     """Router weights in {-1/4, 0, 1/4} and x in {-1, 0, 1}: every score is a
