@@ -50,20 +50,29 @@ __device__ __forceinline__ float wave_sum_f32(float v)
     return v;
 }
 
-// Steps 1-3 for one token (one wave): the K' selected experts, each
-// selected lane's rank and renormalised gate (lanes < K' hold slot `lane`).
-// wkey, wexp: this wave's K'-entry LDS scratch.
+// A token's scores in registers: expert e = lane + 64 j in val[j] (0 past N').
 template <int NPL>
-__device__ __forceinline__ void select_token(const float *__restrict__ row, int N, int K, int lane, unsigned *wkey,
-                                             int *wexp, int &me_out, int &rank_out, float &gate_out)
+__device__ __forceinline__ void load_scores(const float *__restrict__ row, int N, int lane, float (&val)[NPL])
 {
-    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    unsigned key[NPL];
-    float val[NPL];
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
         const int e = lane + 64 * j;
         val[j] = (e < N) ? row[e] : 0.f;
+    }
+}
+
+// Steps 1-3 for one token (one wave) from its scores in registers: the K'
+// selected experts, each selected lane's rank and renormalised gate (lanes <
+// K' hold slot `lane`).  wkey, wexp: this wave's K'-entry LDS scratch.
+template <int NPL>
+__device__ __forceinline__ void select_token_vals(const float (&val)[NPL], int N, int K, int lane, unsigned *wkey,
+                                                  int *wexp, int &me_out, int &rank_out, float &gate_out)
+{
+    const unsigned long long lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    unsigned key[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const int e = lane + 64 * j;
         key[j] = (e < N) ? ordered_key(val[j]) : 0u;
     }
     // 1. the K'-th largest key: largest th with #{key >= th} >= K'
@@ -112,14 +121,30 @@ __device__ __forceinline__ void select_token(const float *__restrict__ row, int 
             rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
         }
     }
-    // 3. gates
-    const float s_mine = (lane < K) ? row[me < N ? me : 0] : 0.f;
+    // 3. gates; the score of slot `lane`'s expert from the lane that holds it
+    float s_pick = 0.f;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+        const float v = __shfl(val[j], me & 63, 64);
+        if ((me >> 6) == j)
+            s_pick = v;
+    }
+    const float s_mine = (lane < K) ? s_pick : 0.f;
     const float s_top = __shfl(s_mine, __ffsll((long long)__ballot(lane < K && rank == 0)) - 1, 64);
     const float g = (lane < K) ? expf(s_mine - s_top) : 0.f;
     const float gsum = wave_sum_f32(g);
     me_out = me;
     rank_out = rank;
     gate_out = g / gsum;
+}
+
+template <int NPL>
+__device__ __forceinline__ void select_token(const float *__restrict__ row, int N, int K, int lane, unsigned *wkey,
+                                             int *wexp, int &me_out, int &rank_out, float &gate_out)
+{
+    float val[NPL];
+    load_scores<NPL>(row, N, lane, val);
+    select_token_vals<NPL>(val, N, K, lane, wkey, wexp, me_out, rank_out, gate_out);
 }
 
 // NPL = ceil(N' / 64) scores held per lane (expert e = lane + 64 j).

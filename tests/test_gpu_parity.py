@@ -161,6 +161,10 @@ def test_exact_score_ties_follow_index_order(dtype):
     # then 65 chunks and 1008 experts (two-kernel path, a partial last batch)
     dict(T=1024, d=128, l=64, m=64, n_experts=1024, top_k=8, n_shared=1, m_shared=64, alpha=2),
     dict(T=1040, d=128, l=64, m=64, n_experts=1008, top_k=6, n_shared=0, m_shared=0, alpha=2, variant="eff"),
+    # decode-sized batches at the selection's limits: 64 tokens, 1024 experts,
+    # K' = 64; and 48 experts (a partial group of 64 scores per lane)
+    dict(T=64, d=128, l=64, m=64, n_experts=1024, top_k=64, n_shared=1, m_shared=64, alpha=2),
+    dict(T=33, d=128, l=64, m=64, n_experts=48, top_k=6, n_shared=1, m_shared=64, alpha=2),
 ])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_shape_edge_cases(cfg, dtype):
