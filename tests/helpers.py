@@ -93,3 +93,32 @@ def random_fp8_workload(sh: LayerShape, seed=0, pow2_scales=False) -> Workload:
             sc = np.ldexp(np.float32(1.0), rng.integers(-9, -3, size=sc.shape)).astype(np.float32)
         t[k], t[k + "_scale"] = q, sc
     return Workload(sh, t)
+
+
+# ---- comparison metrics (used by the GPU parity tests and by the CPU test
+# that derives their tolerances from the emulated bf16 rounding points) ----
+
+DELTA = 2e-5  # decided-token margin on the scores
+
+
+def rel_max_err(got, ref):
+    """max |got - ref| / RMS(ref): the layer output's contract metric."""
+    rms = float(np.sqrt(np.mean(np.square(ref)))) if ref.size else 0.0
+    return float(np.max(np.abs(got - ref))) / max(rms, 1e-30)
+
+
+def elem_err(got, ref):
+    """max |got - ref| / (|ref| + RMS(ref)): relative for large entries,
+    RMS-relative for small ones (suits heavy-tailed squared-ReLU outputs)."""
+    rms = float(np.sqrt(np.mean(np.square(ref)))) if ref.size else 0.0
+    return float(np.max(np.abs(got - ref) / (np.abs(ref) + max(rms, 1e-30))))
+
+
+def decided_mask(logits, K, delta=DELTA):
+    """True for tokens whose top-(K'+1) scores are pairwise at least delta
+    apart: no rounding smaller than delta / 2 can change their routing."""
+    N = logits.shape[1]
+    srt = -np.sort(-logits, axis=1)[:, :min(K + 1, N)]
+    if srt.shape[1] < 2:
+        return np.ones(logits.shape[0], dtype=bool)
+    return np.all(srt[:, :-1] - srt[:, 1:] >= delta, axis=1)

@@ -120,8 +120,9 @@ def test_gated_create_needs_gate_banks_before_any_gpu_call(fp8, shared):
 
 
 def test_gated_cost_counts_three_matrices():
-    # "three matrices in place of two": every expert term scales by 3/2, the
-    # projections and the router do not
+    # a gated expert holds a third matrix beside W1 (the explainer page's
+    # feed-forward paragraph near Figure 9): every expert term scales by 3/2,
+    # the projections and the router do not
     sh = CONFIGS["readme_acc"]
     a = _abi.latentmoe_cost(_cfg(sh))
     b = _abi.latentmoe_cost(_cfg(sh, expert_act="swiglu"))

@@ -8,13 +8,11 @@ contributes to no gradient on either side.
 
 Bars (|d| / (|ref| + RMS(ref)) elementwise, the forward's stage metric):
   * f32 layers: 1e-4 (measured: 1e-5 and below);
-  * bf16 layers: 6e-2 for dx and the dense weight gradients, 1.2e-1 for the
-    expert banks.  The backward rounds dY, dH, dA, dz, ds and the recomputed
-    forward's intermediates to bf16 once each; an exact numpy emulation of
-    those rounding points (no kernel) reaches 1.1-3.1e-2 and 2.2-5.0e-2 on
-    these shapes (expert banks at readme widths over 64 tokens hold about 6
-    rows each), which the GPU matches to three digits.  The bars are twice the
-    worst emulated value.
+  * bf16 layers: one bar per gradient (tests/tolerances.py), each at least
+    twice the error that an exact emulation of the backward's bf16 rounding
+    points (dY, dH, dA, dz, ds and the recomputed forward's intermediates
+    rounded once each, sums exact) reaches on these shapes and seeds;
+    tests/test_tolerance_derivation.py recomputes them.
 """
 
 import ctypes
@@ -28,12 +26,12 @@ from mixture_experts_layer_latentmoe_amd.layer import LatentMoE, to_device
 from oracle import oracle
 from synth import get_config, make_workload
 from synth.generate import bf16_bits_to_f32, f32_to_bf16_bits
+from tests import cases as C
 from tests import gpu_util as G
+from tests import tolerances as TOL
 from tests.helpers import near_tie_mask, random_workload, shape
 
 pytestmark = pytest.mark.gpu
-
-BAR = {"f32": (1e-4, 1e-4), "bf16": (6e-2, 1.2e-1)}  # (dx and dense weights, expert banks)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -77,7 +75,6 @@ def _check(wl, experts=None):
     ref = oracle.backward(wl, dy64, experts=ex)
     got = _gpu_grads(wl, dy_store)
     names = {"dw1g": "dw1_gate", "dw1g_s": "dw1_shared_gate", "dw1_s": "dw1_shared", "dw2_s": "dw2_shared"}
-    bar_dense, bar_bank = BAR[sh.dtype]
     errs = {}
     for k, v in ref.items():
         gk = names.get(k, k)
@@ -88,7 +85,7 @@ def _check(wl, experts=None):
         if bank:
             g = g[ex]
         errs[gk] = G.elem_err(g, v)
-        assert errs[gk] <= (bar_bank if bank else bar_dense), (gk, errs[gk])
+        assert errs[gk] <= TOL.backward_bar(sh, gk), (gk, errs[gk])
     G.say("[gpu]   gradient errors, max |d| / (|ref| + RMS): " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     expected = {"dx", "dw_router", "dw_down", "dw1", "dw2", "dw_up"}
     if sh.n_shared > 0:
@@ -104,18 +101,12 @@ def test_backward_tiny_f32():
     _check(make_workload(get_config("tiny_f32")))
 
 
-@pytest.mark.parametrize("cfg", [
-    dict(T=300, d=256, l=128, m=128, n_experts=16, top_k=4, n_shared=1, m_shared=192, alpha=2),
-    dict(T=300, d=256, l=128, m=128, n_experts=16, top_k=4, n_shared=1, m_shared=192, alpha=2, expert_act="swiglu"),
-    dict(T=40, d=256, l=128, m=128, n_experts=16, top_k=4, n_shared=1, m_shared=192, alpha=2, zipf_s=1.1),
-    dict(T=9, d=128, l=64, m=64, n_experts=32, top_k=8, n_shared=0, m_shared=0, alpha=2),
-    dict(T=130, d=128, l=64, m=192, n_experts=16, top_k=16, n_shared=2, m_shared=64, alpha=2, variant="eff"),
-])
+@pytest.mark.parametrize("cfg", C.BACKWARD_SHAPES)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_backward_shapes(cfg, dtype):
     # 300 rows: tiled x-pass and grouped GEMMs; 40 and 9: the few-row kernel;
     # 130: split-K; a router bias; no shared expert; K' = N'
-    _check(random_workload(shape(dtype=dtype, **cfg), seed=cfg["T"] + 3))
+    _check(C.backward_workload(cfg, dtype))
 
 
 @pytest.mark.parametrize("T", [1, 2])
@@ -146,7 +137,7 @@ def test_backward_full_size_readme_dx_sample():
     ref = oracle.backward(sub, dy64[toks], experts=[])
     err = G.elem_err(got["dx"][toks], ref["dx"])
     G.say(f"[gpu] backward readme_acc full size: dx on {len(toks)} sampled tokens, max |d| / (|ref| + RMS) = {err:.2e}")
-    assert err <= BAR["bf16"][0], err
+    assert err <= TOL.backward_bar(wl.shape, "dx"), err
     for k, v in got.items():
         assert np.all(np.isfinite(v)), k
 

@@ -1,0 +1,98 @@
+"""Tolerances of the GPU parity tests, and the metric of the layer output.
+
+The layer-output bar is the contract: max |y - y_oracle| <= 2e-2 RMS(y_oracle)
+for bf16 layers, 1e-4 for fp32 layers, over tokens whose K'-th and (K'+1)-th
+oracle scores differ by at least 1e-3.  The bound is on the computation; the
+output format's own quantisation step is not part of it, so each element is
+allowed half a unit in the last place of the output format at its reference
+value on top of the bar (the exactly rounded result itself is that far off,
+and a computed value can land half an ulp to the other side).
+
+Every other bar below is this build's own and is derived, not chosen: it is
+at least twice the largest error that an exact emulation of the HIP path's
+bf16 rounding points (tests/bf16_emulation.py: fp64 sums, one rounding to
+bf16 wherever the HIP path stores bf16) reaches against the fp64 oracle on
+the shapes and seeds the bar governs.  tests/test_tolerance_derivation.py
+recomputes every one of them on those inputs and fails if a bar is less than
+twice its emulated error.
+"""
+
+import numpy as np
+
+# the contract (layer output, named workloads)
+Y_BAR = {"bf16": 2e-2, "f32": 1e-4}
+
+# fp32 layers: every stage and gradient at the contract's fp32 bar
+F32_BAR = 1e-4
+
+# bf16 layers narrower than the named workloads (d <= 256): few terms per
+# sum, so the bf16 roundings average out less.  Largest emulated value 3.21e-2
+# (1040 tokens, l 64, 1008 experts, K' 6, no shared expert: y is the
+# up-projection of u alone, a sum of 64 terms).
+Y_BAR_NARROW_BF16 = 6.5e-2
+
+# bf16 stage checks, max |d| / (|ref| + RMS(ref)) elementwise over the
+# decided tokens; largest emulated value over every governed shape in brackets
+STAGE_BAR_BF16 = {
+    "z": 7e-3,          # (0.0031)
+    "h_shared": 8e-3,   # (0.0035)
+    "h": 2e-2,          # (0.0099) squared-ReLU experts
+    "h_gated": 7e-2,    # (0.0324) SwiGLU experts: silu(g) v, two rounded sums
+    "y_perm": 4.5e-2,   # (0.0205)
+    "u": 4.5e-2,        # (0.0201)
+    "y": 4e-2,          # (0.0189)
+}
+
+# bf16 backward, max |d| / (|ref| + RMS(ref)) elementwise
+BACKWARD_BAR_BF16 = {
+    "dx": 3.5e-2,               # (0.0156)
+    "dw_router": 8e-2,          # (0.0379)
+    "db_router": 2e-2,          # (0.0082)
+    "dw_down": 6e-2,            # (0.0258)
+    "dw_up": 4e-2,              # (0.0174)
+    "dw1_shared": 6e-2,         # (0.0267)
+    "dw1_shared_gate": 5e-2,    # (0.0224)
+    "dw2_shared": 8e-2,         # (0.0377)
+    "dw1": 1.2e-1,              # (0.0571)
+    "dw1_gate": 9e-2,           # (0.043)
+    "dw2": 1e-1,                # (0.0471)
+}
+
+
+def half_ulp(v, dtype):
+    """Half a unit in the last place of |v| in the output format (8
+    significand bits for bf16, 24 for fp32); 0 at 0."""
+    p = 8 if dtype == "bf16" else 24
+    _, E = np.frexp(np.abs(np.asarray(v, dtype=np.float64)))
+    return np.where(v == 0, 0.0, np.ldexp(1.0, E - p - 1))
+
+
+def y_err(got, ref, dtype):
+    """The contract's metric: max over elements of (|got - ref| - half an
+    output-format ulp of ref), over RMS(ref)."""
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(np.square(ref)))) if ref.size else 0.0
+    d = np.abs(np.asarray(got, dtype=np.float64) - ref) - half_ulp(ref, dtype)
+    return max(0.0, float(np.max(d))) / max(rms, 1e-30)
+
+
+def is_narrow(sh):
+    return sh.name == "custom" and sh.d <= 256
+
+
+def y_bar(sh):
+    if sh.dtype == "bf16" and is_narrow(sh):
+        return Y_BAR_NARROW_BF16
+    return Y_BAR[sh.dtype]
+
+
+def stage_bar(sh, stage):
+    if sh.dtype != "bf16":
+        return F32_BAR
+    if stage == "h" and sh.expert_act == "swiglu":
+        return STAGE_BAR_BF16["h_gated"]
+    return STAGE_BAR_BF16[stage]
+
+
+def backward_bar(sh, name):
+    return F32_BAR if sh.dtype != "bf16" else BACKWARD_BAR_BF16[name]
