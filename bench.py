@@ -1,13 +1,26 @@
 """Benchmark of the LatentMoE layer forward pass on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config readme_acc] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--config wide_prefill] [--also readme_acc,...]
+                    [--no-cpu-baseline]
 
 One step = one forward of the whole layer (router + top-K', dispatch order,
 down-projection and shared experts, both grouped expert GEMMs, combine,
 up-projection) over one batch of seeded synthetic tokens already resident in
-HBM.  Prints one JSON line: whole-job tokens/s, the roofline position of the
-dominant kernel (timed with HIP events on the forward's stream during the
-timed steps), and the fp64 CPU oracle timed on a bounded token sample.
+HBM.  Prints one JSON line: whole-job tokens/s of the headline workload
+(wide_prefill, the largest of the named single-GPU workloads), the roofline
+position of its dominant kernel (timed with HIP events on the forward's
+stream during the timed steps), the fp64 CPU oracle timed on a bounded token
+sample, and the same measurements for the other named workloads under
+"workloads".
+
+Algorithmic work of a kernel: its flops, and the bytes of the weights it
+touches plus its own inputs and outputs as the layer defines them (x, z and
+the gathered z rows, Y, u, y).  Intermediates that exist only because the
+layer runs as separate kernels -- the hidden activations H between the two
+expert GEMMs, and the fp32 router scores between the pass over x and the
+selection -- are reported as staged bytes beside it, not counted.  A
+kernel's roof is MFMA when its flops at peak take longer than its
+algorithmic bytes at HBM peak, else HBM.
 """
 
 import argparse
@@ -25,14 +38,14 @@ if ROOT not in sys.path:
 METRIC = "LatentMoE layer fwd tokens/s at 1 GPU; % bf16 MFMA peak / % HBM BW"
 PEAK = {"bf16": 2500.0, "f32": 157.3}      # dense MFMA TFLOP/s (MI355X published)
 HBM_PEAK_GBS = 8000.0
+HEADLINE = "wide_prefill"
+ALSO = "readme_acc,zipf_skew,decode_eff,decode_eff_fp8"
 
 
 def stage_work(sh, T, n_active):
-    """Algorithmic work per launch of each stage: (flop, bytes).
-
-    bytes counts every operand once: weights, activations read, outputs
-    written.  n_active = experts that receive at least one token (the grouped
-    GEMMs stream only those experts' weights).  None = not counted."""
+    """Algorithmic work per launch of each stage: (flop, algorithmic bytes,
+    staged bytes).  n_active = experts that receive at least one token (the
+    grouped GEMMs stream only those experts' weights).  None = not counted."""
     P = T * sh.top_k
     es = 2 if sh.dtype == "bf16" else 4
     fp8 = sh.expert_dtype == "fp8"
@@ -42,23 +55,39 @@ def stage_work(sh, T, n_active):
     N, d, l, m = sh.n_experts, sh.d, sh.l, sh.m
     g = 2 if sh.expert_act == "swiglu" else 1  # gated: a gate matrix beside each W1
     nx = N + l + g * ms                         # B columns of the pass over x
+    w1 = g * (ew * n_active * l * m + (4.0 * n_active * m if fp8 else 0.0))
+    w2 = ew * n_active * m * l + (4.0 * n_active * l if fp8 else 0.0)
     return {
-        # one pass over x: router scores (fp32 out), z and the shared-expert hidden layer
-        "gemm_x_router_down_shared1": (2.0 * T * d * nx,
-                                       es * (T * d + d * nx + T * ldzh) + 4.0 * T * N),
-        # expert weights (+ their fp32 column scales for E4M3 banks), rows in and out
-        "grouped_gemm1_relu2": (2.0 * P * l * m * g, g * (ew * n_active * l * m + (4.0 * n_active * m if fp8 else 0.0))
-                                + es * (P * l + P * m) + 4.0 * P),
-        "grouped_gemm2": (2.0 * P * m * l, ew * n_active * m * l + (4.0 * n_active * l if fp8 else 0.0)
-                          + es * (P * m + P * l)),
-        "gemm_up_shared2": (2.0 * T * ldzh * d, es * (ldzh * d + T * ldzh + T * d)),
-        # gather P rows of l, write T rows of l, read pos and gate
-        "combine": (None, float(P * l * es + T * l * es + P * 8)),
-        # read the T x N' fp32 scores, write idx/gate/rank (12 bytes per slot)
-        "router_select": (None, float(T * N * 4 + P * 12)),
-        "dispatch_scan": (None, None),
-        "dispatch_finalize": (None, None),
+        # one pass over x: z and the shared-expert hidden layer out; the fp32
+        # router scores are staged for the selection
+        "gemm_x_router_down_shared1": (2.0 * T * d * nx, es * (T * d + d * nx + T * ldzh), 4.0 * T * N),
+        # scores in, experts and gates out
+        "router_select": (None, float(T * N * 4 + P * 8), float(P * 4)),
+        "dispatch_scan": (None, None, None),
+        "dispatch_finalize": (None, None, None),
+        # W1 of the active experts, the gathered z rows (and their indices) in;
+        # H out is staged
+        "grouped_gemm1_relu2": (2.0 * P * l * m * g, w1 + es * P * l + 4.0 * P, float(es * P * m)),
+        # W2 of the active experts, Y out; H in is staged
+        "grouped_gemm2": (2.0 * P * m * l, w2 + es * P * l, float(es * P * m)),
+        # Y rows gathered, u written, positions and gates read
+        "combine": (None, float(P * l * es + T * l * es + P * 8), 0.0),
+        "gemm_up_shared2": (2.0 * T * ldzh * d, es * (ldzh * d + T * ldzh + T * d), 0.0),
     }
+
+
+def layer_work(sh, T, n_active):
+    """The whole layer: flops of every GEMM, and the bytes of the weights it
+    touches plus x in and y out."""
+    es = 2 if sh.dtype == "bf16" else 4
+    ew = 1 if sh.expert_dtype == "fp8" else es
+    g = 2 if sh.expert_act == "swiglu" else 1
+    ms = sh.n_shared * sh.m_shared
+    N, d, l, m = sh.n_experts, sh.d, sh.l, sh.m
+    w = (es * d * (N + l + g * ms) + es * (l + ms) * d + ew * n_active * (g + 1) * l * m
+         + (4.0 * n_active * (g * m + l) if sh.expert_dtype == "fp8" else 0.0))
+    flop = sum(f for f, _, _ in stage_work(sh, T, n_active).values() if f)
+    return flop, w + 2.0 * es * T * d
 
 
 def roofline_of(flop, nbytes, avg_s, dtype):
@@ -127,40 +156,23 @@ def weight_bytes(sh) -> int:
     return 2 * dense * es + mats * sh.n_experts * sh.l * sh.m * eb  # the dense part twice: tiled + fragment-major
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="readme_acc")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-stage-timing", action="store_true")
-    ap.add_argument("--weight-copies", type=int, default=0,
-                    help="independently repacked weight copies that consecutive steps rotate through "
-                         "(0: enough for 2 GB of weights, at least 2, at most 8), so that no step finds "
-                         "its weights in the 256 MB last-level cache from the step before")
-    ap.add_argument("--backward", action="store_true",
-                    help="also time the layer's backward pass (its forward recompute included) over the same "
-                         "steps and report it under \"backward\"")
-    ap.add_argument("--graph", action="store_true",
-                    help="also replay the forward from captured HIP graphs (one per weight copy) over the same "
-                         "steps and report it under \"graph\"; the headline value stays the eager forward")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain elementwise copy of 256 MiB (3 launches) so that profiler "
-                         "byte counters can be scaled by a kernel of known traffic")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this layer is measured on one "
-              "GPU's share and has no multi-GPU path.", file=sys.stderr)
-        sys.exit(2)
+def describe(sh):
+    return (f"{sh.name}: LatentMoE layer forward, T={sh.T} d={sh.d} l={sh.l} m={sh.m} "
+            f"N'={sh.n_experts} K'={sh.top_k} S={sh.n_shared}x{sh.m_shared} {sh.variant} {sh.dtype}"
+            + (" (routed experts E4M3 + per-column scales)" if sh.expert_dtype == "fp8" else "")
+            + (" SwiGLU experts" if sh.expert_act == "swiglu" else ""))
 
+
+def measure(name, args, log):
+    """Time `args.steps` forwards of workload `name` (weights rotated over R
+    independent copies); returns the measurement dict and the workload."""
     import torch
     from mixture_experts_layer_latentmoe_amd import _abi
     from mixture_experts_layer_latentmoe_amd.layer import LatentMoE, to_device
     from synth import get_config, make_workload
 
-    sh = get_config(args.config)
-    print(f"[bench] generating {sh.name} (seeded)", file=sys.stderr, flush=True)
+    sh = get_config(name)
+    log(f"generating {sh.name} (seeded)")
     wl = make_workload(sh)
     dev = "cuda:0"
     R = args.weight_copies or min(8, max(2, -(-2_000_000_000 // weight_bytes(sh))))
@@ -169,7 +181,7 @@ def main():
     x = to_device(wl.tensors["x"], sh.dtype, dev)
     y = torch.empty_like(x)
     T = sh.T
-    print(f"[bench] {R} weight copies; warmup {args.warmup}", file=sys.stderr, flush=True)
+    log(f"{sh.name}: {R} weight copies; warmup {args.warmup}")
     for i in range(max(args.warmup, R)):
         layers[i % R].forward(x, y)
     torch.cuda.synchronize()
@@ -193,22 +205,24 @@ def main():
     names = {_abi.latentmoe_stage_name(i): i for i in range(_abi.LATENTMOE_MAX_STAGES)
              if _abi.latentmoe_stage_name(i)}
 
-    def stage_table(stages):
-        out = {}
-        for name, (ms, n) in stages.items():
-            if n:
-                avg_us = ms / n * 1e3
-                flop, nbytes = work.get(name, (None, None))
-                e = {"avg_us": round(avg_us, 2), "launches": n}
-                if flop:
-                    e["tflops"] = round(flop / (avg_us * 1e-6) / 1e12, 1)
-                if nbytes:
-                    e["gbs"] = round(nbytes / (avg_us * 1e-6) / 1e9, 1)
-                if flop or nbytes:
-                    r = roofline_of(flop, nbytes, avg_us * 1e-6, sh.dtype)
-                    e["bound"], e["frac"] = r["bound"], r["frac"]
-                out[name] = e
-        return out
+    def stage_entry(name, avg_us, n):
+        flop, nbytes, staged = work.get(name, (None, None, None))
+        e = {"avg_us": round(avg_us, 2), "launches": n}
+        if flop:
+            e["tflops"] = round(flop / (avg_us * 1e-6) / 1e12, 1)
+        if nbytes:
+            e["gbs"] = round(nbytes / (avg_us * 1e-6) / 1e9, 1)
+            e["algorithmic_bytes"] = nbytes
+        if staged:
+            e["staged_bytes"] = staged
+        if flop or nbytes:
+            r = roofline_of(flop, nbytes, avg_us * 1e-6, sh.dtype)
+            e["bound"], e["frac"] = r["bound"], r["frac"]
+        tr = profiled_traffic(sh.name, name)
+        if tr is not None and nbytes:
+            e["traffic"] = tr
+            e["traffic_over_algorithmic"] = round(tr / nbytes, 3)
+        return e
 
     # Untimed pass with every stage timed: the per-stage breakdown, and which
     # stage dominates.  (Two event records per stage and forward cost a few
@@ -219,7 +233,7 @@ def main():
         profile_begin(nb)
         for i in range(nb):
             layers[i % R].forward(x, y)
-        stage_out = stage_table(profile_end())
+        stage_out = {k: stage_entry(k, ms / n * 1e3, n) for k, (ms, n) in profile_end().items() if n}
         dom = max((k for k in stage_out if "frac" in stage_out[k]), key=lambda k: stage_out[k]["avg_us"])
         # the timed region records events around the dominant stage only
         profile_begin(args.steps, 1 << names[dom])
@@ -229,18 +243,29 @@ def main():
         layers[i % R].forward(x, y)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    print(f"[bench] timed {args.steps} steps in {dt:.3f} s", file=sys.stderr, flush=True)
+    log(f"{sh.name}: timed {args.steps} steps in {dt:.3f} s")
     ms_per_step = dt / args.steps * 1e3
-    value = T * args.steps / dt
     roof = None
     if timing:
-        timed = stage_table(profile_end())[dom]
-        flop, nbytes = work[dom]
-        roof = {"kernel": dom, **roofline_of(flop, nbytes, timed["avg_us"] * 1e-6, sh.dtype),
-                "avg_us": timed["avg_us"], "launches": timed["launches"],
-                "traffic": profiled_traffic(sh.name, dom)}
-    total_flop = sum(f for f, _ in work.values() if f)
-    graph_out = None
+        tot = profile_end()[dom]
+        e = stage_entry(dom, tot[0] / tot[1] * 1e3, tot[1])
+        flop, nbytes, staged = work[dom]
+        roof = {"kernel": dom, **roofline_of(flop, nbytes, e["avg_us"] * 1e-6, sh.dtype),
+                "traffic": e.get("traffic"), "algorithmic_bytes": nbytes, "staged_bytes": staged,
+                "traffic_over_algorithmic": e.get("traffic_over_algorithmic"), "flop": flop,
+                "avg_us": e["avg_us"], "launches": e["launches"]}
+    lflop, lbytes = layer_work(sh, T, n_active)
+    t_roof = max(lflop / (PEAK[sh.dtype] * 1e12), lbytes / (HBM_PEAK_GBS * 1e9))
+    out = {
+        "tokens_per_s": round(T * args.steps / dt, 1), "ms_per_step": round(ms_per_step, 4),
+        "workload": describe(sh), "tokens": T, "experts_with_tokens": n_active, "weight_copies": R,
+        "layer_tflops": round(lflop / (ms_per_step * 1e-3) / 1e12, 1),
+        "layer_roofline": {"bound": "mfma" if lflop / (PEAK[sh.dtype] * 1e12) >= lbytes / (HBM_PEAK_GBS * 1e9)
+                           else "hbm", "flop": lflop, "algorithmic_bytes": lbytes,
+                           "roofline_tokens_per_s": round(T / t_roof, 1),
+                           "frac": round(t_roof / (ms_per_step * 1e-3), 4)},
+        "roofline": roof, "stages": stage_out,
+    }
     if args.graph:
         # one graph per weight copy, captured on a side stream after a warm-up
         side = torch.cuda.Stream()
@@ -252,10 +277,10 @@ def main():
         torch.cuda.synchronize()
         graphs = []
         for L in layers:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
                 L.forward(x, y)
-            graphs.append(g)
+            graphs.append(gr)
         for i in range(max(args.warmup, R)):
             graphs[i % R].replay()
         torch.cuda.synchronize()
@@ -264,14 +289,13 @@ def main():
             graphs[i % R].replay()
         torch.cuda.synchronize()
         tg = (time.perf_counter() - tg0) / args.steps
-        graph_out = {"ms_per_step": round(tg * 1e3, 4), "tokens_per_s": round(T / tg, 1),
-                     "note": "forward replayed from HIP graphs, same weight-copy rotation"}
+        out["graph"] = {"ms_per_step": round(tg * 1e3, 4), "tokens_per_s": round(T / tg, 1),
+                        "note": "forward replayed from HIP graphs, same weight-copy rotation"}
         del graphs
-    bwd = None
     if args.backward and sh.expert_dtype != "fp8":
         # algorithmic work: the recomputed forward (no up-projection), the
         # data gradients and the weight gradients of every GEMM: 3F - F_up
-        gemm_flop = total_flop - work["gemm_up_shared2"][0] + 2.0 * total_flop
+        gemm_flop = 3.0 * lflop - work["gemm_up_shared2"][0]
         dy = torch.randn_like(x)
         for i in range(max(2, R)):
             layers[i % R].backward(x, dy)
@@ -281,38 +305,84 @@ def main():
             layers[i % R].backward(x, dy)
         torch.cuda.synchronize()
         tb = (time.perf_counter() - tb0) / args.steps
-        bwd = {"ms_per_step": round(tb * 1e3, 4), "tokens_per_s": round(T / tb, 1),
-               "algorithmic_tflops": round(gemm_flop / tb / 1e12, 1),
-               "note": "forward recompute + data and weight gradients (fp32), weight copies rotated as above"}
-        print(f"[bench] backward {args.steps} steps in {tb * args.steps:.3f} s", file=sys.stderr, flush=True)
+        out["backward"] = {"ms_per_step": round(tb * 1e3, 4), "tokens_per_s": round(T / tb, 1),
+                           "algorithmic_tflops": round(gemm_flop / tb / 1e12, 1),
+                           "note": "forward recompute + data and weight gradients (fp32), weight copies "
+                                   "rotated as above"}
+        log(f"{sh.name}: backward {args.steps} steps in {tb * args.steps:.3f} s")
     for L in layers:
         L.close()
+    del layers
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out, wl
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=HEADLINE, help="the headline workload")
+    ap.add_argument("--also", default=ALSO,
+                    help="comma-separated further workloads measured in the same run and reported under "
+                         "\"workloads\" (empty: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--weight-copies", type=int, default=0,
+                    help="independently repacked weight copies that consecutive steps rotate through "
+                         "(0: enough for 2 GB of weights, at least 2, at most 8), so that no step finds "
+                         "its weights in the 256 MB last-level cache from the step before")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the layer's backward pass (its forward recompute included) over the same "
+                         "steps and report it under \"backward\"")
+    ap.add_argument("--graph", action="store_true",
+                    help="also replay the forward from captured HIP graphs (one per weight copy) over the same "
+                         "steps and report it under \"graph\"; the headline value stays the eager forward")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain elementwise copy of 256 MiB (3 launches) so that profiler "
+                         "byte counters can be scaled by a kernel of known traffic")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); this layer is measured on one "
+              "GPU's share and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    head, wl = measure(args.config, args, log)
+    others = {}
+    for name in [n for n in args.also.split(",") if n and n != args.config]:
+        others[name], _ = measure(name, args, log)
     if args.copy_calibration:
         # reads 256 MiB and writes 256 MiB per launch
-        a = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        a = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
         b = torch.empty_like(a)
         for _ in range(3):
             torch.add(a, 0.0, out=b)
         torch.cuda.synchronize()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+    sh = wl.shape
     out = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": sh.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{sh.name}: LatentMoE layer forward, T={T} d={sh.d} l={sh.l} m={sh.m} "
-                               f"N'={sh.n_experts} K'={sh.top_k} S={sh.n_shared}x{sh.m_shared} "
-                               f"{sh.variant} {sh.dtype}"
-                               + (" (routed experts E4M3 + per-column scales)" if sh.expert_dtype == "fp8" else "")
-                               + (" SwiGLU experts" if sh.expert_act == "swiglu" else ""),
-                   "tokens": T, "experts_with_tokens": n_active, "weight_copies": R},
-        "layer_tflops": round(total_flop / (ms_per_step * 1e-3) / 1e12, 1),
-        "roofline": roof, "cpu_baseline": cpu, "stages": stage_out,
-        **({"backward": bwd} if bwd else {}),
-        **({"graph": graph_out} if graph_out else {}),
+        "config": {"workload": head["workload"], "tokens": head["tokens"],
+                   "experts_with_tokens": head["experts_with_tokens"], "weight_copies": head["weight_copies"]},
+        "layer_tflops": head["layer_tflops"], "layer_roofline": head["layer_roofline"],
+        "roofline": head["roofline"], "cpu_baseline": cpu, "stages": head["stages"],
+        **({"backward": head["backward"]} if "backward" in head else {}),
+        **({"graph": head["graph"]} if "graph" in head else {}),
+        "workloads": others,
         "stages_note": "per-stage HIP-event times from an untimed pass of min(steps, 10) forwards; "
-                       "roofline.avg_us is the dominant kernel timed over the timed region",
+                       "roofline.avg_us is the dominant kernel timed over the timed region; algorithmic "
+                       "bytes = weights touched + the kernel's own inputs and outputs, staged_bytes = H "
+                       "between the expert GEMMs and the fp32 router scores",
     }
     print(json.dumps(out), flush=True)
 
