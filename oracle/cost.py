@@ -18,9 +18,9 @@ N' routed experts (N = N'/alpha in the baseline), K' active (K = K'/alpha for
 variant acc, K = K' for eff), S shared experts of hidden width m_s.
 b_w bytes per expert weight; b_out / b_back bytes per element sent to /
 returned from an expert.  FLOPs count 2 per multiply-add.  Gated experts
-(the explainer's feed-forward section: with a gated activation such as
-SwiGLU a third matrix stands beside W1 and everything else carries over)
-hold and touch three expert matrices in place of two: ``matrices=3``.
+(the explainer's feed-forward section: a gated activation such as SwiGLU
+adds a gate matrix next to W1 and changes nothing else) hold and touch
+three expert matrices instead of two: ``matrices=3``.
 """
 
 from dataclasses import dataclass

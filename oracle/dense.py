@@ -13,7 +13,7 @@ Equations, Architecture, Code and ..." -- Figure 3 (router, softmax, top-K),
 Figure 6 (down/up projections), Figure 8 (the three paths of the layer),
 Figure 9 (latent expert = two matrices around a squared ReLU), and the MoE
 code block (renormalisation of the K selected weights).  Gated experts (the
-explainer's feed-forward section: a third matrix beside W1) use torch's
+explainer's feed-forward section: a gate matrix next to W1) use torch's
 ``silu`` as the activation of the gate branch, so this file and the C
 oracle do not share the activation either.
 """

@@ -45,9 +45,9 @@
  * column: W_e[i][j] = decode(q_e[i][j]) * scale_e[j], formed exactly in
  * double.
  *
- * Gated experts: the explainer notes (its feed-forward section) that with a
- * gated activation such as SwiGLU a third matrix stands beside W1 and all
- * else carries over; the shaping paper's rank tables name an expert's three
+ * Gated experts: the explainer notes (its feed-forward section) that a
+ * gated activation such as SwiGLU adds a gate matrix next to W1 and changes
+ * nothing else; the shaping paper's rank tables name an expert's three
  * matrices W_g, W_u, W_o.  The reading taken: a gated expert computes
  *   h = silu(W_g a) * (W1 a),  silu(v) = v / (1 + exp(-v)),  out = W2 h,
  * with W_g of W1's shape (W1 playing W_u, W2 playing W_o), for the routed

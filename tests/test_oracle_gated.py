@@ -2,8 +2,8 @@
 
 The explainer page ("LatentMoE: NVIDIA's Latent Mixture of Experts Explained
 Through Equations, Architecture, Code and ...", its feed-forward section)
-says a gated activation such as SwiGLU puts a third matrix beside W1 and
-that everything else carries over; the shaping paper ("Shaping Latent
+says a gated activation such as SwiGLU adds a gate matrix next to W1 and
+changes nothing else; the shaping paper ("Shaping Latent
 Mixture-of-Experts ...", its rank tables) names an expert's three matrices
 W_g, W_u, W_o.  The reading taken: h = silu(a W_g) * (a W1), out = h W2, for
 routed and shared experts alike, with silu(v) = v / (1 + e^-v).
