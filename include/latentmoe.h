@@ -38,7 +38,9 @@ typedef enum latentmoe_status {
     LATENTMOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, inconsistent shape, T out of range */
     LATENTMOE_ERR_UNSUPPORTED = 2,      /* valid layer, but outside what the kernels handle */
     LATENTMOE_ERR_OUT_OF_MEMORY = 3,    /* device allocation failed */
-    LATENTMOE_ERR_HIP = 4               /* a HIP runtime call failed */
+    LATENTMOE_ERR_HIP = 4,              /* a HIP runtime call failed */
+    LATENTMOE_ERR_EXCEEDS_SCRATCH = 5   /* latentmoe_forward_noalloc: T needs more workspace
+                                           than the library's static scratch holds */
 } latentmoe_status;
 
 /* Two ways to spend the saving of the latent projection (README "Two
@@ -65,8 +67,8 @@ typedef enum latentmoe_expert_format {
 
 /* Expert activation.  RELU2: out = W2 relu(W1 a)^2 (the explainer's Expert
  * class and Figure 9).  SWIGLU: the gated form the explainer's feed-forward
- * section allows ("a third matrix beside W1"; the shaping paper's W_g, W_u,
- * W_o): out = W2 (silu(W_g a) * (W1 a)), silu(v) = v / (1 + e^-v), for the
+ * section allows, which adds a gate matrix next to W1 (the shaping paper's
+ * W_g, W_u, W_o): out = W2 (silu(W_g a) * (W1 a)), silu(v) = v / (1 + e^-v), for the
  * routed experts (a = z) and the shared experts (a = x) alike; the gate
  * matrices come in w1_gate and w1_shared_gate. */
 typedef enum latentmoe_expert_act { LATENTMOE_ACT_RELU2 = 0, LATENTMOE_ACT_SWIGLU = 1 } latentmoe_expert_act;
@@ -171,6 +173,27 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w,
  * the same bits. */
 int latentmoe_forward(latentmoe_handle *h, const void *x, void *y, int64_t T,
                       void *hip_stream, const latentmoe_debug *dbg);
+
+/* latentmoe_forward without device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same layer, same kernels, same arguments (no
+ * debug outputs); the forward's workspace for T tokens (scores, routing,
+ * dispatch order, tile table, z/u and h_s, H, Y, split-K partial sums) lives
+ * in a static device array of LATENTMOE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing, neither does anything it launches.  The bits equal
+ * latentmoe_forward's whenever the split-K GEMMs of 65..256 rows get as
+ * many partial sums as there (always true when T <= 64 or T > 256); else
+ * they differ by the fp32 summation order only.  Every call on one GPU
+ * shares that GPU's array and leaves its contents behind: calls that
+ * overlap on one GPU (two streams, two handles, two host threads) race and
+ * must be serialised by the caller.  Nothing in the array needs clearing
+ * between calls.  The workspace needed is about T (K' (4 + 2 (m + l)) +
+ * 4 N' + 2 (l + S m_s)) bytes for bf16 layers (e.g. readme widths: about 100
+ * KB per token, about 650 tokens fit).  Errors: as latentmoe_forward, and
+ * LATENTMOE_ERR_EXCEEDS_SCRATCH when T tokens need more than the array. */
+#define LATENTMOE_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int latentmoe_forward_noalloc(latentmoe_handle *h, const void *x, void *y, int64_t T, void *hip_stream);
 
 /* Gradients of a scalar loss L through the layer (device pointers; NULL
  * skips that gradient).  Weight gradients are fp32 in the weights' own

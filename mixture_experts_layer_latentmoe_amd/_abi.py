@@ -15,13 +15,16 @@ LATENTMOE_ERR_INVALID_ARGUMENT = 1
 LATENTMOE_ERR_UNSUPPORTED = 2
 LATENTMOE_ERR_OUT_OF_MEMORY = 3
 LATENTMOE_ERR_HIP = 4
+LATENTMOE_ERR_EXCEEDS_SCRATCH = 5
+LATENTMOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 LATENTMOE_VARIANT_ACC, LATENTMOE_VARIANT_EFF = 0, 1
 LATENTMOE_DTYPE_F32, LATENTMOE_DTYPE_BF16 = 0, 1
 LATENTMOE_EXPERT_AS_DTYPE, LATENTMOE_EXPERT_FP8_E4M3 = 0, 1
 LATENTMOE_ACT_RELU2, LATENTMOE_ACT_SWIGLU = 0, 1
 LATENTMOE_MAX_STAGES = 16
 
-EXPORTED = ("latentmoe_create", "latentmoe_forward", "latentmoe_backward", "latentmoe_destroy",
+EXPORTED = ("latentmoe_create", "latentmoe_forward", "latentmoe_forward_noalloc", "latentmoe_backward",
+            "latentmoe_destroy",
             "latentmoe_validate_config",
             "latentmoe_workspace_bytes", "latentmoe_cost", "latentmoe_status_string",
             "latentmoe_last_hip_error", "latentmoe_profile_begin", "latentmoe_profile_end",
@@ -92,6 +95,7 @@ def lib():
         P = C.POINTER
         L.latentmoe_create.argtypes = [P(latentmoe_config), P(latentmoe_weights), _vp, P(_vp)]
         L.latentmoe_forward.argtypes = [_vp, _vp, _vp, _i64, _vp, P(latentmoe_debug)]
+        L.latentmoe_forward_noalloc.argtypes = [_vp, _vp, _vp, _i64, _vp]
         L.latentmoe_backward.argtypes = [_vp, _vp, _vp, _i64, _vp, P(latentmoe_grads)]
         L.latentmoe_destroy.argtypes = [_vp]
         L.latentmoe_validate_config.argtypes = [P(latentmoe_config)]
@@ -157,6 +161,11 @@ def latentmoe_forward(handle: int, x_ptr: int, y_ptr: int, T: int, stream: int,
                       dbg: latentmoe_debug = None) -> None:
     _check("latentmoe_forward", lib().latentmoe_forward(_vp(handle), _vp(x_ptr), _vp(y_ptr), int(T),
                                                         _vp(stream), C.byref(dbg) if dbg is not None else None))
+
+
+def latentmoe_forward_noalloc(handle: int, x_ptr: int, y_ptr: int, T: int, stream: int) -> None:
+    _check("latentmoe_forward_noalloc",
+           lib().latentmoe_forward_noalloc(_vp(handle), _vp(x_ptr), _vp(y_ptr), int(T), _vp(stream)))
 
 
 def latentmoe_backward(handle: int, x_ptr: int, dy_ptr: int, T: int, stream: int, grads: latentmoe_grads) -> None:

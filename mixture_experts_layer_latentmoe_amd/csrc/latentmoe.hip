@@ -33,6 +33,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -93,10 +94,21 @@ struct Plan {
     int64_t nb1;    // B columns of grouped GEMM 1: m, or 2m when gated
     int64_t ld_zh;  // l + S*ms: row of [z|u , h_s]
     int64_t n_x;    // N' + l + S*ms (gated: N' + l + 2 S*ms): B columns of the pass over x
-    int64_t nchunks_max;
-    int64_t ld_chunks;  // row length of the expert-major chunk arrays (multiple of 4)
     int64_t P_max;
-    int64_t max_mtiles;  // tile table capacity (smallest grouped M tile)
+};
+
+// The forward's workspace for up to T tokens: routing, dispatch order, the
+// grouped GEMMs' tile table, scores, [z|u, h_s], H, Y and split-K partials.
+// Rows of expert e sit in [offsets[e], offsets[e+1]) of H and Y.
+struct Workspace {
+    int *idx, *rank, *pos, *perm;
+    float *gate, *logits;
+    int *chunk_counts, *chunk_base, *counts, *offsets;
+    int *tile_expert, *tile_row0, *n_mtiles;
+    void *zh, *H, *Yp;
+    float *partial;
+    int64_t partial_cap;  // floats at `partial`
+    int64_t ld_chunks;    // row length of the expert-major chunk arrays
 };
 
 constexpr int kGroupBM = 128, kGroupBMBig = 256, kGroupBMSmall = 32, kMinGroupBM = 32;
@@ -117,15 +129,12 @@ struct latentmoe_handle {
     void *frag1 = nullptr, *frag2 = nullptr;  // fragment-major copies of wcat1T, wcat2T
     float *s1 = nullptr, *s2 = nullptr;  // E4M3 column scales [N', m], [N', l]
     float *bias = nullptr;
-    // workspace (one allocation)
+    // workspace (one allocation, sized for max_tokens)
     void *ws = nullptr;
-    int *idx = nullptr, *rank = nullptr, *pos = nullptr, *perm = nullptr;
-    float *gate = nullptr, *logits = nullptr;
-    int *chunk_counts = nullptr, *chunk_base = nullptr, *counts = nullptr, *offsets = nullptr;
-    int *tile_expert = nullptr, *tile_row0 = nullptr, *n_mtiles = nullptr;
-    void *zh = nullptr, *H = nullptr, *Yp = nullptr;
-    float *partial = nullptr;
-    int64_t partial_cap = 0;
+    Workspace wk{};
+    // this device's address of the static scratch array (latentmoe_forward_noalloc)
+    void *scratch = nullptr;
+    hipError_t scratch_err = hipSuccess;
     // profiling
     bool prof = false;
     int prof_cap = 0, prof_used = 0;
@@ -223,26 +232,26 @@ Plan make_plan(const latentmoe_config *c)
     p.nb1 = p.glu ? 2 * p.m : p.m;
     p.ld_zh = p.l + p.S * p.ms;
     p.n_x = p.N + p.l + p.S * p.ms * (p.glu ? 2 : 1);
-    p.nchunks_max = (p.Tmax + kRouterTokens - 1) / kRouterTokens;
-    p.ld_chunks = align_up(p.nchunks_max, 4);
     p.P_max = p.Tmax * p.K;
-    p.max_mtiles = max_mtiles_for(p.P_max, p.N, kMinGroupBM);
     return p;
 }
 
 // fp32 partial sums of split-K GEMMs: up to kSplitKMax splits of the widest
-// dense output, for up to kSplitKMaxRows rows
-int64_t split_partial_floats(const Plan &p)
+// dense output, for up to kSplitKMaxRows rows of T
+int64_t split_partial_floats(const Plan &p, int64_t T)
 {
-    return (int64_t)kSplitKMax * std::min<int64_t>(p.Tmax, kSplitKMaxRows) * std::max(p.n_x, p.d);
+    return (int64_t)kSplitKMax * std::min<int64_t>(T, kSplitKMaxRows) * std::max(p.n_x, p.d);
 }
 
 struct Layout {
     int64_t off_idx, off_gate, off_rank, off_pos, off_perm, off_cc, off_cb, off_counts, off_offsets, off_te, off_tr,
         off_nmt, off_logits, off_zh, off_H, off_Yp, off_part, total;
+    int64_t ld_chunks, partial_floats;
 };
 
-Layout ws_layout(const Plan &p)
+// Byte offsets of a workspace for T tokens with room for `partial_floats`
+// split-K partial sums (256-byte aligned pieces).
+Layout ws_layout(const Plan &p, int64_t T, int64_t partial_floats)
 {
     Layout L;
     int64_t o = 0;
@@ -251,25 +260,55 @@ Layout ws_layout(const Plan &p)
         o = align_up(o + bytes, 256);
         return at;
     };
-    L.off_idx = take(4 * p.P_max);
-    L.off_gate = take(4 * p.P_max);
-    L.off_rank = take(4 * p.P_max);
-    L.off_pos = take(4 * p.P_max);
-    L.off_perm = take(4 * p.P_max);
-    L.off_cc = take(4 * p.ld_chunks * p.N);
-    L.off_cb = take(4 * p.ld_chunks * p.N);
+    const int64_t P = T * p.K;
+    L.ld_chunks = align_up((T + kRouterTokens - 1) / kRouterTokens, 4);
+    L.partial_floats = partial_floats;
+    const int64_t mt = max_mtiles_for(P, p.N, kMinGroupBM);
+    L.off_idx = take(4 * P);
+    L.off_gate = take(4 * P);
+    L.off_rank = take(4 * P);
+    L.off_pos = take(4 * P);
+    L.off_perm = take(4 * P);
+    L.off_cc = take(4 * L.ld_chunks * p.N);
+    L.off_cb = take(4 * L.ld_chunks * p.N);
     L.off_counts = take(4 * p.N);
     L.off_offsets = take(4 * (p.N + 1));
-    L.off_te = take(4 * p.max_mtiles);
-    L.off_tr = take(4 * p.max_mtiles);
+    L.off_te = take(4 * mt);
+    L.off_tr = take(4 * mt);
     L.off_nmt = take(4);
-    L.off_logits = take(4 * p.Tmax * p.N);
-    L.off_zh = take((int64_t)p.esize * p.Tmax * p.ld_zh);
-    L.off_H = take((int64_t)p.esize * p.P_max * p.m);
-    L.off_Yp = take((int64_t)p.esize * p.P_max * p.l);
-    L.off_part = take(4 * split_partial_floats(p));
+    L.off_logits = take(4 * T * p.N);
+    L.off_zh = take((int64_t)p.esize * T * p.ld_zh);
+    L.off_H = take((int64_t)p.esize * P * p.m);
+    L.off_Yp = take((int64_t)p.esize * P * p.l);
+    L.off_part = take(4 * partial_floats);
     L.total = o;
     return L;
+}
+
+Workspace carve_ws(void *base, const Layout &L)
+{
+    char *b = static_cast<char *>(base);
+    Workspace w;
+    w.idx = reinterpret_cast<int *>(b + L.off_idx);
+    w.gate = reinterpret_cast<float *>(b + L.off_gate);
+    w.rank = reinterpret_cast<int *>(b + L.off_rank);
+    w.pos = reinterpret_cast<int *>(b + L.off_pos);
+    w.perm = reinterpret_cast<int *>(b + L.off_perm);
+    w.chunk_counts = reinterpret_cast<int *>(b + L.off_cc);
+    w.chunk_base = reinterpret_cast<int *>(b + L.off_cb);
+    w.counts = reinterpret_cast<int *>(b + L.off_counts);
+    w.offsets = reinterpret_cast<int *>(b + L.off_offsets);
+    w.tile_expert = reinterpret_cast<int *>(b + L.off_te);
+    w.tile_row0 = reinterpret_cast<int *>(b + L.off_tr);
+    w.n_mtiles = reinterpret_cast<int *>(b + L.off_nmt);
+    w.logits = reinterpret_cast<float *>(b + L.off_logits);
+    w.zh = b + L.off_zh;
+    w.H = b + L.off_H;
+    w.Yp = b + L.off_Yp;
+    w.partial = reinterpret_cast<float *>(b + L.off_part);
+    w.partial_cap = L.partial_floats;
+    w.ld_chunks = L.ld_chunks;
+    return w;
 }
 
 struct WLayout {
@@ -534,29 +573,28 @@ int group_bm_for(int64_t P, int64_t N, bool big = false)
 }
 
 template <int NPL>
-void launch_select_n(latentmoe_handle *h, int T, hipStream_t s)
+void launch_select_n(const Plan &p, const Workspace &w, int T, hipStream_t s)
 {
-    const Plan &p = h->plan;
     const int blocks = (T + kRouterTokens - 1) / kRouterTokens;
     router_select_kernel<NPL><<<dim3(blocks), dim3(64 * kSelectWaves), router_select_smem_bytes((int)p.N, (int)p.K),
-                                s>>>(h->logits, T, (int)p.N, (int)p.K, h->idx, h->gate, h->rank, h->chunk_counts,
-                                     (int)p.ld_chunks);
+                                s>>>(w.logits, T, (int)p.N, (int)p.K, w.idx, w.gate, w.rank, w.chunk_counts,
+                                     (int)w.ld_chunks);
     hip_check(hipGetLastError());
 }
 
-void launch_select(latentmoe_handle *h, int T, hipStream_t s)
+void launch_select(const Plan &p, const Workspace &w, int T, hipStream_t s)
 {
-    const int64_t npl = (h->plan.N + 63) / 64;
+    const int64_t npl = (p.N + 63) / 64;
     if (npl <= 1)
-        launch_select_n<1>(h, T, s);
+        launch_select_n<1>(p, w, T, s);
     else if (npl <= 2)
-        launch_select_n<2>(h, T, s);
+        launch_select_n<2>(p, w, T, s);
     else if (npl <= 4)
-        launch_select_n<4>(h, T, s);
+        launch_select_n<4>(p, w, T, s);
     else if (npl <= 8)
-        launch_select_n<8>(h, T, s);
+        launch_select_n<8>(p, w, T, s);
     else
-        launch_select_n<16>(h, T, s);
+        launch_select_n<16>(p, w, T, s);
 }
 
 // ---- the forward -----------------------------------------------------------
@@ -590,8 +628,8 @@ void copy2d(void *dst, int64_t dst_pitch, const void *src, int64_t src_pitch, in
 // pre-activations in fp32 to Apre; small kernels then form h_s and H.  u
 // ends in zh beside h_s; y is not formed.
 template <typename E>
-void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_t s, const latentmoe_debug *dbg,
-                  bool train = false)
+void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *y, int T, hipStream_t s,
+                  const latentmoe_debug *dbg, bool train = false)
 {
     const Plan &p = h->plan;
     const int N = (int)p.N, K = (int)p.K;
@@ -612,11 +650,11 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g.B = h->wcat1T;
     g.Bfrag = h->frag1;
     g.ldb = p.d;
-    g.C32 = h->logits;
+    g.C32 = w.logits;
     g.ldc32 = p.N;
     g.bias32 = h->cfg.has_router_bias ? h->bias : nullptr;
     g.c_split = N;
-    g.C = h->zh;
+    g.C = w.zh;
     g.ldc = p.ld_zh;
     g.M = T;
     g.N = (int)p.n_x;
@@ -633,73 +671,73 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     }
     tm.begin(ST_GEMM_X);
     if (train)
-        dense_gemm<E, kTagXRaw>(g, h->partial, h->partial_cap, s);
+        dense_gemm<E, kTagXRaw>(g, w.partial, w.partial_cap, s);
     else
-        dense_gemm<E, kTagX>(g, h->partial, h->partial_cap, s);
+        dense_gemm<E, kTagX>(g, w.partial, w.partial_cap, s);
     if (train) {
         const int64_t n = (int64_t)T * p.ld_zh;
         xpass_act_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
             static_cast<const E *>(h->XA), ld_xa, T, (int)p.l, (int)(p.S * p.ms), p.glu ? 1 : 0,
-            static_cast<E *>(h->zh), p.ld_zh);
+            static_cast<E *>(w.zh), p.ld_zh);
         hip_check(hipGetLastError());
     }
     tm.end(ST_GEMM_X);
     if (dbg && dbg->logits)
-        hip_check(hipMemcpyAsync(dbg->logits, h->logits, 4 * (size_t)T * N, hipMemcpyDeviceToDevice, s));
+        hip_check(hipMemcpyAsync(dbg->logits, w.logits, 4 * (size_t)T * N, hipMemcpyDeviceToDevice, s));
     if (dbg && dbg->z)
-        copy2d(dbg->z, es * p.l, h->zh, es * p.ld_zh, es * p.l, T, s);
+        copy2d(dbg->z, es * p.l, w.zh, es * p.ld_zh, es * p.l, T, s);
     if (dbg && dbg->h_shared && p.S > 0)
-        copy2d(dbg->h_shared, es * (p.ld_zh - p.l), static_cast<char *>(h->zh) + es * p.l, es * p.ld_zh,
+        copy2d(dbg->h_shared, es * (p.ld_zh - p.l), static_cast<char *>(w.zh) + es * p.l, es * p.ld_zh,
                es * (p.ld_zh - p.l), T, s);
 
     // 1: top-K', gates, chunk ranks
     tm.begin(ST_SELECT);
-    launch_select(h, T, s);
+    launch_select(p, w, T, s);
     tm.end(ST_SELECT);
     // 2-4: dispatch order (small batches: one workgroup, one launch)
     if (nchunks <= 64) {
         tm.begin(ST_FINALIZE);
         dispatch_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(
-            h->chunk_counts, nchunks, h->idx, h->rank, T, K, N, kRouterTokens, (int)p.ld_chunks, gbm, h->chunk_base,
-            h->counts, h->offsets, h->tile_expert, h->tile_row0, h->n_mtiles, h->pos, h->perm);
+            w.chunk_counts, nchunks, w.idx, w.rank, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm, w.chunk_base,
+            w.counts, w.offsets, w.tile_expert, w.tile_row0, w.n_mtiles, w.pos, w.perm);
         hip_check(hipGetLastError());
         tm.end(ST_FINALIZE);
     } else {
         tm.begin(ST_SCAN);
-        chunk_scan_kernel<<<dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s>>>(h->chunk_counts, nchunks,
-                                                                              (int)p.ld_chunks, N, h->chunk_base,
-                                                                              h->counts);
+        chunk_scan_kernel<<<dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s>>>(w.chunk_counts, nchunks,
+                                                                              (int)w.ld_chunks, N, w.chunk_base,
+                                                                              w.counts);
         hip_check(hipGetLastError());
         tm.end(ST_SCAN);
         tm.begin(ST_FINALIZE);
         const int64_t blocks = std::min<int64_t>((P + 1023) / 1024, 256);
         finalize_kernel<<<dim3((unsigned)blocks), dim3(1024), 0, s>>>(
-            h->idx, h->rank, h->chunk_base, h->counts, T, K, N, kRouterTokens, (int)p.ld_chunks, gbm,
-            h->offsets, h->tile_expert, h->tile_row0, h->n_mtiles, h->pos, h->perm);
+            w.idx, w.rank, w.chunk_base, w.counts, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm,
+            w.offsets, w.tile_expert, w.tile_row0, w.n_mtiles, w.pos, w.perm);
         hip_check(hipGetLastError());
         tm.end(ST_FINALIZE);
     }
 
     // 5: H = relu(z[perm] W1_e)^2
     GemmParams g1{};
-    g1.A = h->zh;
+    g1.A = w.zh;
     g1.lda = p.ld_zh;
     g1.a_bytes = (int64_t)T * p.ld_zh * es;
     g1.B = h->w1T;
     g1.ldb = p.bk_b;
     g1.b_kstep = p.nb1 * p.bk_b * p.wesize;
     g1.strideB = p.nb1 * p.l;
-    g1.C = h->H;
+    g1.C = w.H;
     g1.ldc = p.m;
     g1.N = (int)p.nb1;
     g1.K = (int)p.l;
     g1.relu2_from = p.glu ? kNoColumn : 0;
     g1.glu_from = p.glu ? 0 : kNoColumn;
-    g1.gather = h->perm;
-    g1.tile_expert = h->tile_expert;
-    g1.tile_row0 = h->tile_row0;
-    g1.n_mtiles = h->n_mtiles;
-    g1.offsets = h->offsets;
+    g1.gather = w.perm;
+    g1.tile_expert = w.tile_expert;
+    g1.tile_row0 = w.tile_row0;
+    g1.n_mtiles = w.n_mtiles;
+    g1.offsets = w.offsets;
     g1.scaleB = h->s1;
     if (train) {  // raw pre-activations in fp32 beside H
         g1.C32 = h->Apre;
@@ -719,14 +757,14 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
 
     // 6: Y = H W2_e
     GemmParams g2 = g1;
-    g2.A = h->H;
+    g2.A = w.H;
     g2.lda = p.m;
     g2.a_bytes = P * p.m * es;
     g2.B = h->w2T;
     g2.ldb = p.bk_b;
     g2.b_kstep = p.l * p.bk_b * p.wesize;
     g2.strideB = p.l * p.m;
-    g2.C = h->Yp;
+    g2.C = w.Yp;
     g2.ldc = p.l;
     g2.N = (int)p.l;
     g2.K = (int)p.m;
@@ -743,7 +781,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     // 7: u = sum_k gate Y[pos], written over z (z is dead after stage 5)
     tm.begin(ST_COMBINE);
     combine_kernel<E><<<dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s>>>(
-        static_cast<const E *>(h->Yp), h->pos, h->gate, T, K, (int)p.l, static_cast<E *>(h->zh), p.ld_zh);
+        static_cast<const E *>(w.Yp), w.pos, w.gate, T, K, (int)p.l, static_cast<E *>(w.zh), p.ld_zh);
     hip_check(hipGetLastError());
     tm.end(ST_COMBINE);
     if (train)
@@ -751,7 +789,7 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
 
     // 8: y = [u | h_s] [W_up ; W2_s]
     GemmParams g3{};
-    g3.A = h->zh;
+    g3.A = w.zh;
     g3.lda = p.ld_zh;
     g3.a_bytes = (int64_t)T * p.ld_zh * es;
     g3.B = h->wcat2T;
@@ -766,29 +804,64 @@ void forward_impl(latentmoe_handle *h, const void *x, void *y, int T, hipStream_
     g3.glu_from = kNoColumn;
     g3.group_m = 8;
     tm.begin(ST_GEMM_UP);
-    dense_gemm<E, kTagUp>(g3, h->partial, h->partial_cap, s);
+    dense_gemm<E, kTagUp>(g3, w.partial, w.partial_cap, s);
     tm.end(ST_GEMM_UP);
 
     if (dbg) {
         if (dbg->idx)
-            hip_check(hipMemcpyAsync(dbg->idx, h->idx, 4 * P, hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpyAsync(dbg->idx, w.idx, 4 * P, hipMemcpyDeviceToDevice, s));
         if (dbg->gate)
-            hip_check(hipMemcpyAsync(dbg->gate, h->gate, 4 * P, hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpyAsync(dbg->gate, w.gate, 4 * P, hipMemcpyDeviceToDevice, s));
         if (dbg->counts)
-            hip_check(hipMemcpyAsync(dbg->counts, h->counts, 4 * p.N, hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpyAsync(dbg->counts, w.counts, 4 * p.N, hipMemcpyDeviceToDevice, s));
         if (dbg->offsets)
-            hip_check(hipMemcpyAsync(dbg->offsets, h->offsets, 4 * (p.N + 1), hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpyAsync(dbg->offsets, w.offsets, 4 * (p.N + 1), hipMemcpyDeviceToDevice, s));
         if (dbg->perm_token)
-            hip_check(hipMemcpyAsync(dbg->perm_token, h->perm, 4 * P, hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpyAsync(dbg->perm_token, w.perm, 4 * P, hipMemcpyDeviceToDevice, s));
         if (dbg->pos)
-            hip_check(hipMemcpyAsync(dbg->pos, h->pos, 4 * P, hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpyAsync(dbg->pos, w.pos, 4 * P, hipMemcpyDeviceToDevice, s));
         if (dbg->h)
-            hip_check(hipMemcpyAsync(dbg->h, h->H, (size_t)es * P * p.m, hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpyAsync(dbg->h, w.H, (size_t)es * P * p.m, hipMemcpyDeviceToDevice, s));
         if (dbg->y_perm)
-            hip_check(hipMemcpyAsync(dbg->y_perm, h->Yp, (size_t)es * P * p.l, hipMemcpyDeviceToDevice, s));
+            hip_check(hipMemcpyAsync(dbg->y_perm, w.Yp, (size_t)es * P * p.l, hipMemcpyDeviceToDevice, s));
         if (dbg->u)
-            copy2d(dbg->u, es * p.l, h->zh, es * p.ld_zh, es * p.l, T, s);
+            copy2d(dbg->u, es * p.l, w.zh, es * p.ld_zh, es * p.l, T, s);
     }
+}
+
+const Workspace &handle_ws(const latentmoe_handle *h) { return h->wk; }
+
+// ---- workspace of latentmoe_forward_noalloc ---------------------------------
+
+// The forward's workspace for callers that cannot allocate: a static array in
+// the code object, one copy on each GPU the library runs on, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: its device address is looked up with hipGetSymbolAddress
+// (once per device, with that device current, from latentmoe_create) and only
+// that address is ever handed to kernels.
+constexpr int64_t kScratchBytes = LATENTMOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on `device` (which must be current).
+hipError_t scratch_address(int device, void **out)
+{
+    *out = nullptr;
+    if (device < 0 || device >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[device]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        g_scratch_addr[device] = ptr;
+    }
+    *out = g_scratch_addr[device];
+    return hipSuccess;
 }
 
 void free_handle(latentmoe_handle *h)
@@ -1054,7 +1127,7 @@ void weight_grads_tn(latentmoe_handle *h, const void *x, const void *dy, int T, 
             split(gr->dw1_shared_gate, (int)p.d, (int)(p.N + p.l), (int)p.S, (int)p.ms, 0);
     }
     if (gr->dw_up || gr->dw2_shared) {
-        launch_tn<kTagWgrad>(tn(h->zh, p.ld_zh, T, dy, p.d, (int)p.ld_zh, (int)p.d, h->dWu), s);
+        launch_tn<kTagWgrad>(tn(h->wk.zh, p.ld_zh, T, dy, p.d, (int)p.ld_zh, (int)p.d, h->dWu), s);
         if (gr->dw_up)
             hip_check(hipMemcpyAsync(gr->dw_up, h->dWu, 4 * p.l * p.d, hipMemcpyDeviceToDevice, s));
         if (p.S > 0 && gr->dw2_shared)
@@ -1067,19 +1140,19 @@ void weight_grads_tn(latentmoe_handle *h, const void *x, const void *dy, int T, 
         hip_check(hipGetLastError());
     }
     if (gr->dw2) {
-        GemmParams g = tn(h->H, p.m, P, h->dYp, p.l, (int)p.m, (int)p.l, gr->dw2);
-        g.k_offsets = h->offsets;
+        GemmParams g = tn(h->wk.H, p.m, P, h->dYp, p.l, (int)p.m, (int)p.l, gr->dw2);
+        g.k_offsets = h->wk.offsets;
         g.n_batches = N;
         launch_tn<kTagWgradE>(g, s);
     }
     if (gr->dw1 || (p.glu && gr->dw1_gate)) {
         const int64_t n = P * p.l / 8;
         gather_rows_kernel<bf16><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
-            static_cast<const bf16 *>(h->XA), ldxa, h->perm, P, (int)p.l, static_cast<bf16 *>(h->zpT));
+            static_cast<const bf16 *>(h->XA), ldxa, h->wk.perm, P, (int)p.l, static_cast<bf16 *>(h->zpT));
         hip_check(hipGetLastError());
         float *dst = p.glu ? h->dW1g : gr->dw1;
         GemmParams g = tn(h->zpT, p.l, P, h->dA, p.nb1, (int)p.l, (int)p.nb1, dst);
-        g.k_offsets = h->offsets;
+        g.k_offsets = h->wk.offsets;
         g.n_batches = N;
         launch_tn<kTagWgradE>(g, s);
         if (p.glu) {  // [N' l, 2m] gated pairs -> W1 (value) and W_g (gate)
@@ -1109,7 +1182,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     const int gl = p.glu ? 1 : 0;
     const int sms = (int)(p.S * p.ms);
 
-    forward_impl<E>(h, x, nullptr, T, s, nullptr, true);
+    forward_impl<E>(h, handle_ws(h), x, nullptr, T, s, nullptr, true);
 
     // [du | dh_s] = dy [W_up ; W2_s]^T
     GemmParams ga{};
@@ -1125,7 +1198,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     ga.N = (int)p.ld_zh;
     ga.K = (int)p.d;
     ga.group_m = 8;
-    dense_gemm<E, kTagDgrad>(ga, h->partial, h->partial_cap, s);
+    dense_gemm<E, kTagDgrad>(ga, h->wk.partial, h->wk.partial_cap, s);
     // shared experts: the gradient of their pre-activations -> dX[:, N' + l ..]
     if (sms > 0) {
         const int64_t n = (int64_t)T * sms;
@@ -1136,7 +1209,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     }
     // gates and combine: dY_perm, and ds -> dX[:, 0 .. N')
     gate_combine_grad_kernel<E><<<dim3((unsigned)T), dim3(256), 0, s>>>(
-        static_cast<const E *>(h->dUH), p.ld_zh, static_cast<const E *>(h->Yp), h->pos, h->idx, h->gate, K,
+        static_cast<const E *>(h->dUH), p.ld_zh, static_cast<const E *>(h->wk.Yp), h->wk.pos, h->wk.idx, h->wk.gate, K,
         (int)p.l, N, static_cast<E *>(h->dYp), static_cast<E *>(h->dX), nxp);
     hip_check(hipGetLastError());
     // dH = dY_perm W2_e^T; its epilogue writes the gradient of the routed
@@ -1155,10 +1228,10 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     gb.ld_pre = p.nb1;
     gb.N = (int)p.m;
     gb.K = (int)p.l;
-    gb.tile_expert = h->tile_expert;
-    gb.tile_row0 = h->tile_row0;
-    gb.n_mtiles = h->n_mtiles;
-    gb.offsets = h->offsets;
+    gb.tile_expert = h->wk.tile_expert;
+    gb.tile_row0 = h->wk.tile_row0;
+    gb.n_mtiles = h->wk.n_mtiles;
+    gb.offsets = h->wk.offsets;
     if (p.glu)
         grouped_gemm<E, kTagDgrad, ACT_GLU_GRAD>(gb, max_mt, gbm, false, s);
     else
@@ -1180,7 +1253,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     {
         const int64_t n = (int64_t)T * p.l / 8;
         gather_sum8_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
-            static_cast<const E *>(h->dzp), h->pos, T, K, (int)p.l, static_cast<E *>(h->dX), nxp, N);
+            static_cast<const E *>(h->dzp), h->wk.pos, T, K, (int)p.l, static_cast<E *>(h->dX), nxp, N);
         hip_check(hipGetLastError());
     }
     // dx = [ds | dz | d pre_s] Wx^T
@@ -1198,7 +1271,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
         gd.N = (int)p.d;
         gd.K = (int)nxp;
         gd.group_m = 8;
-        dense_gemm<E, kTagDgrad>(gd, h->partial, h->partial_cap, s);
+        dense_gemm<E, kTagDgrad>(gd, h->wk.partial, h->wk.partial_cap, s);
     }
 
     // ---- weight gradients (fp32), sums over tokens / an expert's rows ----
@@ -1225,7 +1298,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     // tokens padded to 64 with zero columns
     launch_pad_transpose<E>(x, p.d, T, (int)p.d, nullptr, nullptr, nullptr, 0, h->xT, Tp, s);
     launch_pad_transpose<E>(h->dX, nxp, T, (int)p.n_x, nullptr, nullptr, nullptr, 0, h->dXT, Tp, s);
-    launch_pad_transpose<E>(h->zh, p.ld_zh, T, (int)p.ld_zh, nullptr, nullptr, nullptr, 0, h->zhT, Tp, s);
+    launch_pad_transpose<E>(h->wk.zh, p.ld_zh, T, (int)p.ld_zh, nullptr, nullptr, nullptr, 0, h->zhT, Tp, s);
     launch_pad_transpose<E>(dy, p.d, T, (int)p.d, nullptr, nullptr, nullptr, 0, h->dyT, Tp, s);
     if (gr->dw_router || gr->dw_down || gr->dw1_shared || gr->dw1_shared_gate) {
         GemmParams g = wgrad(h->xT, p.d, h->dXT, p.n_x, Tp, h->dWx);
@@ -1262,20 +1335,20 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     // expert banks: per expert a sum over its rows, padded to 64 per expert
     const bool need1 = gr->dw1 || (p.glu && gr->dw1_gate);
     if (gr->dw2 || need1) {
-        padded_offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(h->counts, N, 64, h->koff);
+        padded_offsets_kernel<<<dim3(1), dim3(1024), 0, s>>>(h->wk.counts, N, 64, h->koff);
         hip_check(hipGetLastError());
     }
     if (gr->dw2) {
-        launch_pad_transpose<E>(h->H, p.m, (int)P, (int)p.m, nullptr, h->offsets, h->koff, N, h->HT, h->Ppad, s);
-        launch_pad_transpose<E>(h->dYp, p.l, (int)P, (int)p.l, nullptr, h->offsets, h->koff, N, h->dYpT, h->Ppad, s);
+        launch_pad_transpose<E>(h->wk.H, p.m, (int)P, (int)p.m, nullptr, h->wk.offsets, h->koff, N, h->HT, h->Ppad, s);
+        launch_pad_transpose<E>(h->dYp, p.l, (int)P, (int)p.l, nullptr, h->wk.offsets, h->koff, N, h->dYpT, h->Ppad, s);
         GemmParams g = wgrad(h->HT, p.m, h->dYpT, p.l, h->Ppad, gr->dw2);
         g.k_offsets = h->koff;
         g.n_batches = N;
         launch_batched_k<E, kTagWgradE>(g, s);
     }
     if (need1) {
-        launch_pad_transpose<E>(h->XA, ldxa, (int)P, (int)p.l, h->perm, h->offsets, h->koff, N, h->zpT, h->Ppad, s);
-        launch_pad_transpose<E>(h->dA, p.nb1, (int)P, (int)p.nb1, nullptr, h->offsets, h->koff, N, h->dAT, h->Ppad,
+        launch_pad_transpose<E>(h->XA, ldxa, (int)P, (int)p.l, h->wk.perm, h->wk.offsets, h->koff, N, h->zpT, h->Ppad, s);
+        launch_pad_transpose<E>(h->dA, p.nb1, (int)P, (int)p.nb1, nullptr, h->wk.offsets, h->koff, N, h->dAT, h->Ppad,
                                 s);
         float *dst = p.glu ? h->dW1g : gr->dw1;
         GemmParams g = wgrad(h->zpT, p.l, h->dAT, p.nb1, h->Ppad, dst);
@@ -1308,6 +1381,7 @@ const char *latentmoe_status_string(int status)
     case LATENTMOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case LATENTMOE_ERR_OUT_OF_MEMORY: return "out of device memory";
     case LATENTMOE_ERR_HIP: return "HIP runtime error";
+    case LATENTMOE_ERR_EXCEEDS_SCRATCH: return "token count needs more workspace than the static scratch array holds";
     default: return "unknown status";
     }
 }
@@ -1324,7 +1398,7 @@ int latentmoe_workspace_bytes(const latentmoe_config *cfg, int64_t *bytes)
     if (!bytes)
         return LATENTMOE_ERR_INVALID_ARGUMENT;
     const Plan p = make_plan(cfg);
-    *bytes = ws_layout(p).total + w_layout(p).total;
+    *bytes = ws_layout(p, p.Tmax, split_partial_floats(p, p.Tmax)).total + w_layout(p).total;
     return LATENTMOE_OK;
 }
 
@@ -1394,9 +1468,12 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     try {
         hip_check(hipGetDevice(&h->device));
+        h->scratch_err = scratch_address(h->device, &h->scratch);
+        if (h->scratch_err != hipSuccess)
+            (void)hipGetLastError();  // only latentmoe_forward_noalloc needs it; it reports the error
         const Plan &p = h->plan;
         const WLayout WL = w_layout(p);
-        const Layout L = ws_layout(p);
+        const Layout L = ws_layout(p, p.Tmax, split_partial_floats(p, p.Tmax));
         if (hipMalloc(&h->wbuf, WL.total) != hipSuccess) {
             (void)hipGetLastError();
             free_handle(h);
@@ -1407,25 +1484,7 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
             free_handle(h);
             return LATENTMOE_ERR_OUT_OF_MEMORY;
         }
-        char *b = static_cast<char *>(h->ws);
-        h->idx = reinterpret_cast<int *>(b + L.off_idx);
-        h->gate = reinterpret_cast<float *>(b + L.off_gate);
-        h->rank = reinterpret_cast<int *>(b + L.off_rank);
-        h->pos = reinterpret_cast<int *>(b + L.off_pos);
-        h->perm = reinterpret_cast<int *>(b + L.off_perm);
-        h->chunk_counts = reinterpret_cast<int *>(b + L.off_cc);
-        h->chunk_base = reinterpret_cast<int *>(b + L.off_cb);
-        h->counts = reinterpret_cast<int *>(b + L.off_counts);
-        h->offsets = reinterpret_cast<int *>(b + L.off_offsets);
-        h->tile_expert = reinterpret_cast<int *>(b + L.off_te);
-        h->tile_row0 = reinterpret_cast<int *>(b + L.off_tr);
-        h->n_mtiles = reinterpret_cast<int *>(b + L.off_nmt);
-        h->logits = reinterpret_cast<float *>(b + L.off_logits);
-        h->zh = b + L.off_zh;
-        h->H = b + L.off_H;
-        h->Yp = b + L.off_Yp;
-        h->partial = reinterpret_cast<float *>(b + L.off_part);
-        h->partial_cap = split_partial_floats(p);
+        h->wk = carve_ws(h->ws, L);
         if (p.dtype == LATENTMOE_DTYPE_BF16)
             repack_weights<bf16>(h, w, s);
         else
@@ -1491,9 +1550,45 @@ int latentmoe_forward(latentmoe_handle *h, const void *x, void *y, int64_t T, vo
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     try {
         if (h->plan.dtype == LATENTMOE_DTYPE_BF16)
-            forward_impl<bf16>(h, x, y, (int)T, s, dbg);
+            forward_impl<bf16>(h, handle_ws(h), x, y, (int)T, s, dbg);
         else
-            forward_impl<float>(h, x, y, (int)T, s, dbg);
+            forward_impl<float>(h, handle_ws(h), x, y, (int)T, s, dbg);
+    } catch (const HipError &e) {
+        g_last_hip_error = (int)e.e;
+        return LATENTMOE_ERR_HIP;
+    }
+    return LATENTMOE_OK;
+}
+
+int latentmoe_forward_noalloc(latentmoe_handle *h, const void *x, void *y, int64_t T, void *hip_stream)
+{
+    if (!h || !x || !y || T < 1 || T > h->plan.Tmax)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    const Plan &p = h->plan;
+    const int64_t bytes = T * p.d * p.esize;
+    const char *xb = static_cast<const char *>(x);
+    const char *yb = static_cast<const char *>(y);
+    if (xb < yb + bytes && yb < xb + bytes)
+        return LATENTMOE_ERR_INVALID_ARGUMENT;
+    if (!h->scratch) {
+        g_last_hip_error = (int)h->scratch_err;
+        return LATENTMOE_ERR_HIP;
+    }
+    // the workspace for T tokens; split-K partial sums take what is left
+    const Layout base = ws_layout(p, T, 0);
+    if (base.total > kScratchBytes)
+        return LATENTMOE_ERR_EXCEEDS_SCRATCH;
+    const int64_t room = (kScratchBytes - base.total) / 4;
+    const Layout L = ws_layout(p, T, std::min(split_partial_floats(p, T), room));
+    if (L.total > kScratchBytes)
+        return LATENTMOE_ERR_EXCEEDS_SCRATCH;
+    const Workspace w = carve_ws(h->scratch, L);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    try {
+        if (p.dtype == LATENTMOE_DTYPE_BF16)
+            forward_impl<bf16>(h, w, x, y, (int)T, s, nullptr);
+        else
+            forward_impl<float>(h, w, x, y, (int)T, s, nullptr);
     } catch (const HipError &e) {
         g_last_hip_error = (int)e.e;
         return LATENTMOE_ERR_HIP;

@@ -120,7 +120,7 @@ def test_gated_create_needs_gate_banks_before_any_gpu_call(fp8, shared):
 
 
 def test_gated_cost_counts_three_matrices():
-    # a gated expert holds a third matrix beside W1 (the explainer page's
+    # a gated expert holds a gate matrix next to W1 (the explainer page's
     # feed-forward paragraph near Figure 9): every expert term scales by 3/2,
     # the projections and the router do not
     sh = CONFIGS["readme_acc"]
@@ -160,13 +160,14 @@ def test_null_arguments_rejected_before_any_gpu_call():
         _abi.LATENTMOE_ERR_INVALID_ARGUMENT
     assert L.latentmoe_create(ctypes.byref(cfg), ctypes.byref(w), None, None) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
     assert L.latentmoe_forward(None, None, None, 1, None, None) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
+    assert L.latentmoe_forward_noalloc(None, None, None, 1, None) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
     assert L.latentmoe_destroy(None) == _abi.LATENTMOE_OK
     assert L.latentmoe_profile_begin(None, 1, 0xFFFF) == _abi.LATENTMOE_ERR_INVALID_ARGUMENT
 
 
 def test_status_strings():
-    for s in range(5):
-        assert _abi.status_string(s)
+    for s in range(6):
+        assert _abi.status_string(s) and _abi.status_string(s) != "unknown status"
     assert _abi.status_string(99) == "unknown status"
     assert _abi.latentmoe_stage_name(0) == "gemm_x_router_down_shared1"
     assert _abi.latentmoe_stage_name(1) == "router_select"
