@@ -17,9 +17,9 @@ Algorithmic work of a kernel: its flops, and the bytes of the weights it
 touches plus its own inputs and outputs as the layer defines them (x, z and
 the gathered z rows, Y, u, y).  Intermediates that exist only because the
 layer runs as separate kernels -- the hidden activations H between the two
-expert GEMMs, and the fp32 router scores between the pass over x and the
-selection -- are reported as staged bytes beside it, not counted.  A
-kernel's roof is MFMA when its flops at peak take longer than its
+expert GEMMs where they run unfused, and the fp32 router scores between the
+pass over x and the selection -- are reported as staged bytes beside it, not
+counted.  A kernel's roof is MFMA when its flops at peak take longer than its
 algorithmic bytes at HBM peak, else HBM.
 """
 
@@ -70,6 +70,9 @@ def stage_work(sh, T, n_active):
         "grouped_gemm1_relu2": (2.0 * P * l * m * g, w1 + es * P * l + 4.0 * P, float(es * P * m)),
         # W2 of the active experts, Y out; H in is staged
         "grouped_gemm2": (2.0 * P * m * l, w2 + es * P * l, float(es * P * m)),
+        # both expert GEMMs in one kernel, H on chip: W1 and W2 of the active
+        # experts, the gathered z rows (and their indices) in, Y out
+        "expert_mlp": (2.0 * P * l * m * (g + 1), w1 + w2 + es * P * l + 4.0 * P + es * P * l, 0.0),
         # Y rows gathered, u written, positions and gates read
         "combine": (None, float(P * l * es + T * l * es + P * 8), 0.0),
         "gemm_up_shared2": (2.0 * T * ldzh * d, es * (ldzh * d + T * ldzh + T * d), 0.0),
@@ -86,7 +89,8 @@ def layer_work(sh, T, n_active):
     N, d, l, m = sh.n_experts, sh.d, sh.l, sh.m
     w = (es * d * (N + l + g * ms) + es * (l + ms) * d + ew * n_active * (g + 1) * l * m
          + (4.0 * n_active * (g * m + l) if sh.expert_dtype == "fp8" else 0.0))
-    flop = sum(f for f, _, _ in stage_work(sh, T, n_active).values() if f)
+    # every GEMM once: the fused expert MLP's flops are those of the two grouped GEMMs
+    flop = sum(f for k, (f, _, _) in stage_work(sh, T, n_active).items() if f and k != "expert_mlp")
     return flop, w + 2.0 * es * T * d
 
 

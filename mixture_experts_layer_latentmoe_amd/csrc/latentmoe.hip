@@ -17,6 +17,9 @@
 //                       (up to 64 chunks: 2 and 3 in one workgroup, one launch)
 //   4 grouped_gemm1     H = relu(z[perm] W1_e)^2 per expert
 //   5 grouped_gemm2     Y = H W2_e per expert
+//     (4 + 5 fused: expert_mlp, Y = relu(z[perm] W1_e)^2 W2_e with H kept on
+//     chip, for bf16 layers with bf16 banks at l = 512 and prefill-sized
+//     row counts; expert_mlp.hpp)
 //   6 combine           u[t] = sum_k gate[t,k] Y[pos[t,k]], written over z
 //   7 gemm_up_shared2   y = [u | h_s] [W_up ; W2_s]
 // Stages 0 and 7 fold the router and the always-on shared experts into the
@@ -42,6 +45,7 @@
 #include "combine.hpp"
 #include "common.hpp"
 #include "dispatch.hpp"
+#include "expert_mlp.hpp"
 #include "gemm.hpp"
 #include "gemm_tn.hpp"
 #include "repack.hpp"
@@ -64,12 +68,13 @@ enum Stage {
     ST_GEMM2,
     ST_COMBINE,
     ST_GEMM_UP,
+    ST_MLP,
     ST_COUNT
 };
 
 const char *kStageNames[ST_COUNT] = {"gemm_x_router_down_shared1", "router_select", "dispatch_scan",
                                      "dispatch_finalize", "grouped_gemm1_relu2", "grouped_gemm2",
-                                     "combine", "gemm_up_shared2"};
+                                     "combine", "gemm_up_shared2", "expert_mlp"};
 
 struct HipError {
     hipError_t e;
@@ -572,6 +577,43 @@ int group_bm_for(int64_t P, int64_t N, bool big = false)
     return (P / N < 32) ? kGroupBMSmall : big ? kGroupBMBig : kGroupBM;
 }
 
+// Fused routed-expert MLP (expert_mlp.hpp): Y = act(z[perm] W1_e) W2_e with
+// H kept on chip, for bf16 forwards with bf16 banks and prefill-sized row
+// counts.  Rows per tile (the tile table's BM) and the wave layouts depend
+// on l, which sets the register tile of Y [BM, l]: l = 512 takes 128-row
+// tiles (64 x 128 of Y per wave).  At l = 1024 only 64-row tiles fit, which
+// streams each expert's weights twice as often; measured slower than the two
+// grouped GEMMs there, so that width keeps the unfused path.  Returns 0 where
+// no instance serves the layer.
+constexpr int kMlpMC = 128;  // hidden columns per chunk
+
+int mlp_bm_for(const Plan &p, int64_t P, bool train)
+{
+    if (train || p.fp8 || p.esize != 2 || p.glu || P / p.N < 32 || p.m % kMlpMC)
+        return 0;
+    if (p.l == 512)
+        return 128;
+    return 0;
+}
+
+template <int BM, int LW, int KS2, int NS, int WM1, int WN1, int WM2, int WN2>
+void launch_mlp_n(const MlpParams &mp, int64_t max_mtiles, hipStream_t s)
+{
+    using K = MlpShape<BM, LW, kMlpMC, KS2, NS, WM1, WN1, WM2, WN2, false>;
+    static_assert(K::lds_bytes() <= 160 * 1024, "LDS");
+    expert_mlp_kernel<BM, LW, kMlpMC, KS2, NS, WM1, WN1, WM2, WN2, false, 0>
+        <<<dim3((unsigned)align_up(max_mtiles, 8)), dim3(512), 0, s>>>(mp);
+    hip_check(hipGetLastError());
+}
+
+void launch_mlp(const Plan &p, const MlpParams &mp, int64_t max_mtiles, hipStream_t s)
+{
+    if (p.l == 512)  // four 32 KiB slots: three steps in flight
+        launch_mlp_n<128, 512, 32, 4, 4, 2, 2, 4>(mp, max_mtiles, s);
+    else
+        throw HipError{hipErrorInvalidValue};
+}
+
 template <int NPL>
 void launch_select_n(const Plan &p, const Workspace &w, int T, hipStream_t s)
 {
@@ -636,7 +678,8 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     const int64_t P = (int64_t)T * K;
     const int nchunks = (T + kRouterTokens - 1) / kRouterTokens;
     const int es = p.esize;
-    const int gbm = group_bm_for(P, N, !train && !p.fp8 && es == 2);
+    const int mlp_bm = mlp_bm_for(p, P, train);
+    const int gbm = mlp_bm ? mlp_bm : group_bm_for(P, N, !train && !p.fp8 && es == 2);
     const int64_t max_mt = max_mtiles_for(P, N, gbm);
     StageTimer tm{h, s, -1};
     if (h->prof && h->prof_used < h->prof_cap)
@@ -746,6 +789,32 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
         g1.relu2_from = kNoColumn;
         g1.glu_from = kNoColumn;
     }
+    if (mlp_bm) {
+        // 5 + 6 fused: Y = relu(z[perm] W1_e)^2 W2_e, H on chip
+        MlpParams mp{};
+        mp.Z = w.zh;
+        mp.ldz = p.ld_zh;
+        mp.z_bytes = (int64_t)T * p.ld_zh * es;
+        mp.gather = w.perm;
+        mp.W1 = h->w1T;
+        mp.W2 = h->w2T;
+        mp.Y = w.Yp;
+        mp.l = (int)p.l;
+        mp.m = (int)p.m;
+        mp.nb1 = (int)p.nb1;
+        mp.tile_expert = w.tile_expert;
+        mp.tile_row0 = w.tile_row0;
+        mp.n_mtiles = w.n_mtiles;
+        mp.offsets = w.offsets;
+        tm.begin(ST_MLP);
+        launch_mlp(p, mp, max_mt, s);
+        tm.end(ST_MLP);
+        // H exists only as a debug output here: the grouped GEMM forms it.
+        // On a 64-row tile table its 128-row tiles start at each entry's
+        // first row, so some rows are written twice, with identical bits.
+        if (dbg && dbg->h)
+            grouped_gemm<E, kTagG1>(g1, max_mt, kGroupBM, false, s);
+    } else {
     tm.begin(ST_GEMM1);
     if (train && p.glu)
         grouped_gemm<E, kTagG1Raw, ACT_GLU>(g1, max_mt, gbm, false, s);
@@ -777,6 +846,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     tm.begin(ST_GEMM2);
     grouped_gemm<E, kTagG2>(g2, max_mt, gbm, p.fp8, s);
     tm.end(ST_GEMM2);
+    }
 
     // 7: u = sum_k gate Y[pos], written over z (z is dead after stage 5)
     tm.begin(ST_COMBINE);

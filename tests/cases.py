@@ -76,3 +76,24 @@ def backward_workload(cfg, dtype):
 def swiglu_tokens_workload(T):
     """test_swiglu_token_counts: the gated workload at T tokens."""
     return make_workload(get_config("shape_swiglu"), T=T)
+
+
+# The fused expert MLP (bf16 layers with l = 512: 128-row tiles, l = 1024:
+# 64-row tiles; at least 32 rows per expert on average).
+# test_fused_mlp_rows_at_tile_boundaries: a zero router with K' = N' = 16, so
+# every expert holds exactly T rows (seed = T).
+FUSED_TILE_ROWS = [(512, 128), (512, 129), (512, 255), (512, 257), (1024, 64), (1024, 65), (1024, 127), (1024, 129)]
+# test_fused_mlp_random_routing: scattered rows over many experts (seed = T + 5)
+FUSED_SHAPES = [
+    dict(T=1024, d=1024, l=512, m=384, n_experts=32, top_k=8, n_shared=1, m_shared=256, alpha=2),
+    dict(T=512, d=2048, l=1024, m=256, n_experts=32, top_k=8, n_shared=1, m_shared=256, alpha=2),
+    dict(T=700, d=2048, l=512, m=128, n_experts=64, top_k=16, n_shared=0, m_shared=0, alpha=4),
+]
+
+
+def fused_tile_rows_shape(l, T):
+    return shape(T=T, d=2 * l, l=l, m=256, n_experts=16, top_k=16, n_shared=1, m_shared=128, alpha=2, dtype="bf16")
+
+
+def fused_workload(cfg):
+    return random_workload(shape(dtype="bf16", **cfg), seed=cfg["T"] + 5)

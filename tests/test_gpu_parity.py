@@ -133,6 +133,32 @@ def test_expert_rows_straddle_tile_height():
     assert out["counts"].min() < 256 < out["counts"].max()
 
 
+# --------------------------------------------------------------------------
+# fused expert MLP: H stays on chip; Y is compared stage by stage (the debug
+# H output comes from grouped GEMM 1 run beside it)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("l,T", C.FUSED_TILE_ROWS)
+def test_fused_mlp_rows_at_tile_boundaries(l, T):
+    """Zero router, K' = N' = 16: every expert holds exactly T rows, so its
+    last fused tile (128 rows at l = 512, 64 at l = 1024) is full, one row
+    short or one row long; every token, stage by stage."""
+    sh = C.fused_tile_rows_shape(l, T)
+    arr = random_arrays(sh, np.random.default_rng(T))
+    arr["w_router"] = np.zeros_like(arr["w_router"])
+    wl = workload_from_arrays(sh, arr)
+    out = G.run_gpu(wl)
+    assert np.all(out["idx"] == np.arange(16, dtype=np.int32)[None, :])
+    assert np.array_equal(out["counts"], np.full(16, T, dtype=out["counts"].dtype))
+    toks = np.arange(T)
+    ref = oracle.forward(wl, tokens=toks, want=("logits", "idx", "gate", "z", "h", "o", "u", "hs", "y"))
+    G.check_stages(out, wl, ref, toks, np.ones(T, dtype=bool))
+
+
+@pytest.mark.parametrize("cfg", C.FUSED_SHAPES)
+def test_fused_mlp_random_routing(cfg):
+    _full_check(C.fused_workload(cfg))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_exact_score_ties_follow_index_order(dtype):
     """Router weights in {-1/4, 0, 1/4} and x in {-1, 0, 1}: every score is a

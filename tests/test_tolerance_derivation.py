@@ -48,6 +48,13 @@ NARROW_FWD = (
                                                   m_shared=128, dtype="bf16"), seed=11))]
 )
 
+# custom shapes at model widths (the fused expert MLP's tests)
+WIDE_FWD = (
+    [(f"fused_rows{l}_{T}", (lambda l=l, T=T: _zero_router(C.fused_tile_rows_shape(l, T), T)))
+     for l, T in C.FUSED_TILE_ROWS]
+    + [(f"fused{i}", (lambda c=c: C.fused_workload(c))) for i, c in enumerate(C.FUSED_SHAPES)]
+)
+
 # the named workloads, on token counts that the emulation covers in seconds
 NAMED_FWD = [("readme_acc", 512), ("readme_acc", 1), ("decode_eff", 64), ("decode_eff_fp8", 64),
              ("decode_eff_fp8", 7), ("wide_prefill", 128), ("zipf_skew", 2048), ("shape_swiglu", 1024),
@@ -89,8 +96,19 @@ def test_narrow_forward_bars(label, make):
     wl = make()
     errs, *_ = _forward_errors(wl, exact_ties=label.startswith(("tile_rows", "zero_router")))
     print(label, {k: f"{v:.4f}" for k, v in errs.items()})
-    assert TOL.is_narrow(wl.shape)
-    assert errs["y_contract"] <= TOL.Y_BAR_NARROW_BF16 / 2, errs["y_contract"]
+    assert TOL.is_custom(wl.shape)
+    assert errs["y_contract"] <= TOL.Y_BAR_CUSTOM_BF16 / 2, errs["y_contract"]
+    _check_stage_bars(wl.shape, errs)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("label,make", WIDE_FWD, ids=[n for n, _ in WIDE_FWD])
+def test_wide_custom_forward_bars(label, make):
+    wl = make()
+    errs, *_ = _forward_errors(wl, exact_ties=label.startswith("fused_rows"))
+    print(label, {k: f"{v:.4f}" for k, v in errs.items()})
+    assert TOL.is_custom(wl.shape)
+    assert errs["y_contract"] <= TOL.Y_BAR_CUSTOM_BF16 / 2, errs["y_contract"]
     _check_stage_bars(wl.shape, errs)
 
 

@@ -25,11 +25,11 @@ Y_BAR = {"bf16": 2e-2, "f32": 1e-4}
 # fp32 layers: every stage and gradient at the contract's fp32 bar
 F32_BAR = 1e-4
 
-# bf16 layers narrower than the named workloads (d <= 256): few terms per
-# sum, so the bf16 roundings average out less.  Largest emulated value 3.21e-2
-# (1040 tokens, l 64, 1008 experts, K' 6, no shared expert: y is the
-# up-projection of u alone, a sum of 64 terms).
-Y_BAR_NARROW_BF16 = 6.5e-2
+# bf16 test shapes other than the named workloads (edge cases, tile
+# boundaries): short sums, no shared expert, so the bf16 roundings average out
+# less.  Largest emulated value 3.21e-2 (1040 tokens, l 64, 1008 experts,
+# K' 6, no shared expert: y is the up-projection of u alone, a sum of 64 terms).
+Y_BAR_CUSTOM_BF16 = 6.5e-2
 
 # bf16 stage checks, max |d| / (|ref| + RMS(ref)) elementwise over the
 # decided tokens; largest emulated value over every governed shape in brackets
@@ -40,7 +40,7 @@ STAGE_BAR_BF16 = {
     "h_gated": 7e-2,    # (0.0324) SwiGLU experts: silu(g) v, two rounded sums
     "y_perm": 4.5e-2,   # (0.0205)
     "u": 4.5e-2,        # (0.0201)
-    "y": 4e-2,          # (0.0189)
+    "y": 4.5e-2,        # (0.0208)
 }
 
 # bf16 backward, max |d| / (|ref| + RMS(ref)) elementwise
@@ -76,13 +76,13 @@ def y_err(got, ref, dtype):
     return max(0.0, float(np.max(d))) / max(rms, 1e-30)
 
 
-def is_narrow(sh):
-    return sh.name == "custom" and sh.d <= 256
+def is_custom(sh):
+    return sh.name == "custom"
 
 
 def y_bar(sh):
-    if sh.dtype == "bf16" and is_narrow(sh):
-        return Y_BAR_NARROW_BF16
+    if sh.dtype == "bf16" and is_custom(sh):
+        return Y_BAR_CUSTOM_BF16
     return Y_BAR[sh.dtype]
 
 
