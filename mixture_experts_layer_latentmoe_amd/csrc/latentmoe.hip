@@ -33,7 +33,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -58,6 +60,25 @@ using namespace lmoe;
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+// Every device allocation of the library goes through here.  Test hook:
+// with LATENTMOE_FAIL_ALLOC_AT=n in the environment, the n-th allocation of
+// the process (counting from 1) fails as if the device were out of memory,
+// so that tests can reach the clean-up paths of create and of the backward's
+// first call.
+std::atomic<long long> g_alloc_count{0};
+
+hipError_t device_alloc(void **p, size_t bytes)
+{
+    const long long n = ++g_alloc_count;
+    if (const char *f = std::getenv("LATENTMOE_FAIL_ALLOC_AT")) {
+        if (std::atoll(f) == n) {
+            *p = nullptr;
+            return hipErrorOutOfMemory;
+        }
+    }
+    return hipMalloc(p, bytes);
+}
 
 enum Stage {
     ST_GEMM_X = 0,
@@ -1098,9 +1119,9 @@ void backward_setup(latentmoe_handle *h, hipStream_t s)
     const Plan &p = h->plan;
     const BwdLayout L = bwd_layout(p);
     const int64_t es = p.esize, nxp = n_x_padded(p);
-    if (hipMalloc(&h->bwbuf, L.wtotal) != hipSuccess)
+    if (device_alloc(&h->bwbuf, L.wtotal) != hipSuccess)
         throw HipError{hipErrorOutOfMemory};
-    if (hipMalloc(&h->bws, L.total) != hipSuccess)
+    if (device_alloc(&h->bws, L.total) != hipSuccess)
         throw HipError{hipErrorOutOfMemory};
     char *w = static_cast<char *>(h->bwbuf);
     char *b = static_cast<char *>(h->bws);
@@ -1544,12 +1565,12 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
         const Plan &p = h->plan;
         const WLayout WL = w_layout(p);
         const Layout L = ws_layout(p, p.Tmax, split_partial_floats(p, p.Tmax));
-        if (hipMalloc(&h->wbuf, WL.total) != hipSuccess) {
+        if (device_alloc(&h->wbuf, WL.total) != hipSuccess) {
             (void)hipGetLastError();
             free_handle(h);
             return LATENTMOE_ERR_OUT_OF_MEMORY;
         }
-        if (hipMalloc(&h->ws, L.total) != hipSuccess) {
+        if (device_alloc(&h->ws, L.total) != hipSuccess) {
             (void)hipGetLastError();
             free_handle(h);
             return LATENTMOE_ERR_OUT_OF_MEMORY;
@@ -1597,7 +1618,8 @@ int latentmoe_backward(latentmoe_handle *h, const void *x, const void *dy, int64
             backward_impl<float>(h, x, dy, (int)T, s, g);
     } catch (const HipError &e) {
         g_last_hip_error = (int)e.e;
-        if (e.e == hipErrorOutOfMemory && !h->bws) {
+        if (e.e == hipErrorOutOfMemory && !h->bws) {  // setup failed: the next call tries again
+            (void)hipGetLastError();
             (void)hipFree(h->bwbuf);
             h->bwbuf = nullptr;
             return LATENTMOE_ERR_OUT_OF_MEMORY;

@@ -45,11 +45,16 @@ _lib = None
 
 
 def lib():
+    """The compiled oracle; LATENTMOE_ORACLE_LIB may name another build of the
+    same source (the sanitized one)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(build_oracle.LIB):
+        path = os.environ.get("LATENTMOE_ORACLE_LIB", build_oracle.LIB)
+        if not os.path.exists(path):
+            if path != build_oracle.LIB:
+                raise FileNotFoundError(path)
             build_oracle.build()
-        L = C.CDLL(build_oracle.LIB)
+        L = C.CDLL(path)
         L.orc_forward.argtypes = [C.POINTER(_Shape), C.POINTER(_Tensors), _i64, _vp,
                                   _i64, _vp, C.POINTER(_Outputs), C.c_int]
         L.orc_forward.restype = C.c_int
