@@ -77,10 +77,13 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int *__restrict__
 // The part of the order every workgroup computes: an exclusive scan of the
 // counts into offsets (in LDS), then pos/perm for the pairs q = q0, q0 + qs,
 // ...; `lead` also publishes offsets and the (expert, first row) tile table.
+// Tiles are BM rows from each expert's first row, except that the last one
+// may hold up to BM + slack rows: max(1, ceil((c - slack) / BM)) tiles for an
+// expert with c > 0 rows (slack 0: ceil(c / BM)).
 // 1024 threads, N' <= 1024; c = counts[threadIdx.x] (0 past N').
 __device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int64_t qs, const int *__restrict__ idx,
                                                const int *__restrict__ rank, const int *__restrict__ chunk_base, int T,
-                                               int K, int N, int chunk_tokens, int ld_chunks, int BM,
+                                               int K, int N, int chunk_tokens, int ld_chunks, int BM, int slack,
                                                int *__restrict__ offsets, int *__restrict__ tile_expert,
                                                int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
                                                int *__restrict__ pos, int *__restrict__ perm, int *s_off, int *s_wsum)
@@ -104,7 +107,7 @@ __device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int
         if (tid == N - 1)
             offsets[N] = excl + c;
         // tile table: same scan over the tile counts
-        const int nt = (c + BM - 1) / BM;
+        const int nt = c > 0 ? max(1, (c - slack + BM - 1) / BM) : 0;
         const int tincl = wave_incl_scan(nt, lane);
         __syncthreads();
         if (lane == 63)
@@ -137,7 +140,7 @@ __device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int
 __global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ idx, const int *__restrict__ rank,
                                                        const int *__restrict__ chunk_base,
                                                        const int *__restrict__ counts, int T, int K, int N,
-                                                       int chunk_tokens, int ld_chunks, int BM,
+                                                       int chunk_tokens, int ld_chunks, int BM, int slack,
                                                        int *__restrict__ offsets, int *__restrict__ tile_expert,
                                                        int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
                                                        int *__restrict__ pos, int *__restrict__ perm)
@@ -147,8 +150,8 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ 
     const int tid = threadIdx.x;
     const int c = (tid < N) ? counts[tid] : 0;
     finalize_block(c, blockIdx.x == 0, (int64_t)blockIdx.x * 1024 + tid, (int64_t)gridDim.x * 1024, idx, rank,
-                   chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, offsets, tile_expert, tile_row0, n_mtiles, pos,
-                   perm, s_off, s_wsum);
+                   chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, slack, offsets, tile_expert, tile_row0, n_mtiles,
+                   pos, perm, s_off, s_wsum);
 }
 
 // Small batches (at most 64 chunks): the chunk scan and finalize in one
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ 
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restrict__ chunk_counts, int nchunks,
                                                              const int *__restrict__ idx, const int *__restrict__ rank,
                                                              int T, int K, int N, int chunk_tokens, int ld_chunks,
-                                                             int BM, int *__restrict__ chunk_base,
+                                                             int BM, int slack, int *__restrict__ chunk_base,
                                                              int *__restrict__ counts, int *__restrict__ offsets,
                                                              int *__restrict__ tile_expert, int *__restrict__ tile_row0,
                                                              int *__restrict__ n_mtiles, int *__restrict__ pos,
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restr
     __syncthreads();
     const int c = (tid < N) ? s_off[tid] : 0;
     __syncthreads();  // s_off is reused for the offsets
-    finalize_block(c, true, tid, 1024, idx, rank, chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, offsets,
+    finalize_block(c, true, tid, 1024, idx, rank, chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, slack, offsets,
                    tile_expert, tile_row0, n_mtiles, pos, perm, s_off, s_wsum);
 }
 

@@ -154,7 +154,9 @@ struct TileInfo {
 // Logical tile t (no split-K) -> output tile.  Grouped: t walks the device
 // tile table, N-tiles fastest.  Dense: tiles are walked in groups of group_m
 // M-tiles, so that tiles in flight together share A and B panels.
-template <int BM, int BN, bool GROUPED>
+// XR: grouped tiles whose expert has at most BM + XR rows left take them all
+// (the tile table gives an expert's last tile up to BM + XR rows).
+template <int BM, int BN, bool GROUPED, int XR = 0>
 __device__ __forceinline__ void tile_coords(const GemmParams &p, int t, int ntn, TileInfo &ti)
 {
     int tm, tn;
@@ -168,7 +170,7 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int t, int ntn,
         const int r0 = p.tile_row0[tm];
         const int start = p.offsets[ti.expert];
         const int cnt = p.offsets[ti.expert + 1] - start;
-        ti.rows_valid = min(BM, cnt - r0);
+        ti.rows_valid = (cnt - r0 <= BM + XR) ? cnt - r0 : BM;
         ti.row_base = (int64_t)start + r0;
     } else {
         const int ntm = (p.M + BM - 1) / BM;
@@ -187,7 +189,7 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int t, int ntn,
 }
 
 // The tile of this workgroup (one tile per workgroup, split-K aware).
-template <int BM, int BN, bool GROUPED>
+template <int BM, int BN, bool GROUPED, int XR = 0>
 __device__ __forceinline__ bool locate_tile(const GemmParams &p, TileInfo &ti)
 {
     const int ntn = (p.N + BN - 1) / BN;
@@ -195,7 +197,7 @@ __device__ __forceinline__ bool locate_tile(const GemmParams &p, TileInfo &ti)
         const int t = xcd_logical_tile(blockIdx.x, *p.n_mtiles * ntn);
         if (t < 0)
             return false;
-        tile_coords<BM, BN, true>(p, t, ntn, ti);
+        tile_coords<BM, BN, true, XR>(p, t, ntn, ti);
     } else if (p.k_offsets) {
         const int ntm = (p.M + BM - 1) / BM, per = ntm * ntn;
         const int t = xcd_logical_tile(blockIdx.x, p.n_batches * per);
@@ -235,8 +237,9 @@ __device__ __forceinline__ uint4 e4m3x8_to_bf16(uint2 v)
 // BQ8: the B tile holds E4M3 bytes, 64 per row and k-tile (4 chunks of 16,
 // chunk c of row r at c ^ ((r >> 2) & 3)); a fragment is 8 bytes, widened to
 // bf16 in registers.
-template <typename E, int TM, int TN, int WTM, int WTN, bool BQ8 = false>
-__device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, const uint4 *b, int wm, int wn, int lane)
+template <typename E, int TM, int TN, int WTM, int WTN, bool BQ8 = false, int XM = 0, int BM = 0>
+__device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, const uint4 *b, int wm, int wn, int lane,
+                                         f32x16 (*accx)[XM > 0 ? XM : 1][1] = nullptr, bool xlive = false)
 {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -262,6 +265,20 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = Mfma32<E>::run(bfr[j], af[i], acc[i][j]);
+        if constexpr (XM > 0) {
+            // the extra rows BM .. BM + 32 XM - 1, times the wave's 32 columns
+            // wn WTN + 32 wm .. (one B fragment, read again); skipped (uniform
+            // branch) when the tile has no extra rows
+            if (!xlive)
+                continue;
+            const int rb = wn * WTN + wm * 32 + (lane & 31);
+            const uint4 bx = b[rb * 8 + (c ^ ((rb >> 1) & 7))];
+#pragma unroll
+            for (int i = 0; i < XM; ++i) {
+                const int r = BM + i * 32 + (lane & 31);
+                (*accx)[i][0] = Mfma32<E>::run(bx, a[r * 8 + (c ^ ((r >> 1) & 7))], (*accx)[i][0]);
+            }
+        }
     }
 }
 
@@ -609,16 +626,17 @@ __device__ __forceinline__ void tile_dma(uint4 *na, uint4 *nb, bool issue, unsig
 // tile held in sa, sb into the accumulators.  The four stages are different
 // LDS arrays; the restrict qualifiers tell the compiler so, which keeps it
 // from making the reads of sa, sb wait for the DMA into na, nb.
-template <typename E, int TM, int TN, int WTM, int WTN, bool BQ8, int NIA, int NIB, int NW>
+template <typename E, int TM, int TN, int WTM, int WTN, bool BQ8, int NIA, int NIB, int NW, int XM = 0, int BM = 0>
 __device__ __forceinline__ void dma_mma(uint4 *__restrict__ na, uint4 *__restrict__ nb, const uint4 *__restrict__ sa,
                                         const uint4 *__restrict__ sb, bool issue, unsigned kt,
                                         __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                         const unsigned (&a_off)[NIA], const unsigned (&b_off)[NIB], unsigned bks,
-                                        int wave, bool live, f32x16 (&acc)[TM][TN], int wm, int wn, int lane)
+                                        int wave, bool live, f32x16 (&acc)[TM][TN], int wm, int wn, int lane,
+                                        f32x16 (*accx)[XM > 0 ? XM : 1][1] = nullptr, bool xlive = false)
 {
     tile_dma<NIA, NIB, NW>(na, nb, issue, kt, ra, rb, a_off, b_off, bks, wave);
     if (live)
-        tile_mma<E, TM, TN, WTM, WTN, BQ8>(acc, sa, sb, wm, wn, lane);
+        tile_mma<E, TM, TN, WTM, WTN, BQ8, XM, BM>(acc, sa, sb, wm, wn, lane, accx, xlive);
 }
 
 // NT = 64 * WM * WN threads; NS LDS stages (2 or 3), one barrier per k-tile;
@@ -626,8 +644,14 @@ __device__ __forceinline__ void dma_mma(uint4 *__restrict__ na, uint4 *__restric
 // names the layer stage, so that each stage is its own kernel symbol in
 // profiles.  BQ8: B holds E4M3 bytes (grouped, bf16 only; see tile_mma) with
 // per-column scales p.scaleB.
+//
+// XR > 0 (grouped, bf16 B, no ACT): a tile holds up to BM + XR rows; the
+// extra rows BM .. BM + XR - 1 are a second block of XR / 32 MFMA row tiles
+// per wave, over the wave's 32 columns wn WTN + 32 wm .. (WM 32 = WTN), read
+// from the same A and B k-tiles -- an expert a few rows past a multiple of
+// BM then streams its weights once instead of twice.
 template <typename E, int BM, int BN, int WM, int WN, int NS, bool GROUPED, int MINB = 1, int STAGE = 0,
-          bool BQ8 = false, int ACT = ACT_NONE>
+          bool BQ8 = false, int ACT = ACT_NONE, int XR = 0>
 __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmParams p)
 {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -638,17 +662,21 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     constexpr int TM = WTM / 32, TN = WTN / 32; // 32x32 MFMA tiles per wave
     constexpr int CHB = BQ8 ? 4 : 8;           // 16-byte chunks per B row and k-tile
     constexpr int EB = BQ8 ? 1 : (int)sizeof(E); // bytes per B element
-    constexpr int NIA = BM * 8 / NT, NIB = BN * CHB / NT;  // LDS-DMA instructions per thread
+    constexpr int BMA = BM + XR;                // A rows per tile (the extra block included)
+    constexpr int XM = XR / 32;                 // extra MFMA row tiles per wave
+    constexpr int NIA = BMA * 8 / NT, NIB = BN * CHB / NT;  // LDS-DMA instructions per thread
     static_assert(TM >= 1 && TN >= 1 && NIA >= 1 && NIB >= 1, "tile shape");
-    static_assert(NIA * NT == BM * 8 && NIB * NT == BN * CHB, "tile shape");
+    static_assert(NIA * NT == BMA * 8 && NIB * NT == BN * CHB, "tile shape");
+    static_assert(XR == 0 || (GROUPED && !BQ8 && ACT == ACT_NONE && XR % 32 == 0 && WM * 32 == WTN),
+                  "extra rows: grouped bf16 tiles, one 32-column block per wave row");
     static_assert(NS >= 2 && NS <= 4, "stages");
     static_assert(!BQ8 || (GROUPED && sizeof(E) == 2), "E4M3 B operands: grouped bf16 GEMMs");
 
-    __shared__ uint4 sA0[BM * 8], sA1[BM * 8], sA2[NS > 2 ? BM * 8 : 1], sA3[NS > 3 ? BM * 8 : 1];
+    __shared__ uint4 sA0[BMA * 8], sA1[BMA * 8], sA2[NS > 2 ? BMA * 8 : 1], sA3[NS > 3 ? BMA * 8 : 1];
     __shared__ uint4 sB0[BN * CHB], sB1[BN * CHB], sB2[NS > 2 ? BN * CHB : 1], sB3[NS > 3 ? BN * CHB : 1];
 
     TileInfo ti;
-    if (!locate_tile<BM, BN, GROUPED>(p, ti))
+    if (!locate_tile<BM, BN, GROUPED, XR>(p, ti))
         return;
     const int rows_valid = ti.rows_valid, expert = ti.expert, split = ti.split;
     const int64_t row_base = ti.row_base;
@@ -691,6 +719,12 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
 #pragma unroll
             for (int q = 0; q < 16; ++q)
                 acc[i][j][q] = 0.f;
+    f32x16 accx[XM > 0 ? XM : 1][1];  // the extra rows' block (XR > 0)
+#pragma unroll
+    for (int i = 0; i < (XM > 0 ? XM : 1); ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+            accx[i][0][q] = 0.f;
 
     // A wave whose whole tile is padding (rows past the valid range or
     // columns past N) still loads and syncs but skips its MFMAs, leaving the
@@ -724,9 +758,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         wait_vm_lgkm0<(NS - 2) * NI>();                                                                       \
         __builtin_amdgcn_s_barrier();                                                                         \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
-        dma_mma<E, TM, TN, WTM, WTN, BQ8, NIA, NIB, NW>(NA, NB, SA, SB, j + NS - 1 < nkl,                    \
-                                                        (unsigned)(kt0 + j + NS - 1), ra_rsrc, rb_rsrc, a_off, \
-                                                        b_off, bks, wave, wave_live, acc, wm, wn, lane);      \
+        dma_mma<E, TM, TN, WTM, WTN, BQ8, NIA, NIB, NW, XM, BM>(                                              \
+            NA, NB, SA, SB, j + NS - 1 < nkl, (unsigned)(kt0 + j + NS - 1), ra_rsrc, rb_rsrc, a_off, b_off, bks,  \
+            wave, wave_live, acc, wm, wn, lane, XM > 0 ? &accx : nullptr, rows_valid > BM);                  \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
         if (++j >= nkl)                                                                                       \
             break;                                                                                            \
@@ -799,6 +833,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     // of the gated pairs: straight from the registers
     if (sizeof(E) != 2 || n0 < p.c_split || (n0 < p.glu_from && n0 + BN > p.glu_from)) {
         store_tile_direct<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, cs);
+        if constexpr (XM > 0) {
+            if (rows_valid > BM && wave_live)
+                store_tile_direct<E, XM, 1, XR, 32>(p, accx, c_row_base + BM, rows_valid - BM,
+                                                    n0 + wn * WTN + wm * 32, 0, 0, lane, cs);
+        }
         return;
     }
     if constexpr (sizeof(E) == 2) {
@@ -816,6 +855,12 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
             store_tile_staged_glu<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg, cs);
         else
             store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg, cs);
+        if constexpr (XM > 0) {
+            // the extra rows: XR x 32 outputs per wave, straight from the registers
+            if (rows_valid > BM && wave_live)
+                store_tile_direct<E, XM, 1, XR, 32>(p, accx, c_row_base + BM, rows_valid - BM,
+                                                    n0 + wn * WTN + wm * 32, 0, 0, lane, cs);
+        }
     }
 #endif
 }

@@ -138,6 +138,7 @@ struct Workspace {
 };
 
 constexpr int kGroupBM = 128, kGroupBMBig = 256, kGroupBMSmall = 32, kMinGroupBM = 32;
+constexpr int kGroupSlack = 64;  // extra rows the 256-row tiles take (the kernel's XR)
 constexpr int kNoColumn = 1 << 30;  // relu2_from / glu_from: no such columns
 constexpr int kSplitKMaxRows = 256, kSplitKMax = 16;
 
@@ -477,12 +478,12 @@ void launch_dense(const GemmParams &gp, hipStream_t s)
     hip_check(hipGetLastError());
 }
 
-template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG, bool BQ8, int ACT = ACT_NONE>
+template <typename E, int BM, int BN, int WM, int WN, int NS, int TAG, bool BQ8, int ACT = ACT_NONE, int XR = 0>
 void launch_grouped(const GemmParams &gp, int64_t max_mtiles, hipStream_t s)
 {
     const int64_t ntn = (gp.N + BN - 1) / BN;
     const int64_t grid = align_up(max_mtiles * ntn, 8);
-    gemm_kernel<E, BM, BN, WM, WN, NS, true, 1, TAG, BQ8, ACT><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
+    gemm_kernel<E, BM, BN, WM, WN, NS, true, 1, TAG, BQ8, ACT, XR><<<dim3((unsigned)grid), dim3(64 * WM * WN), 0, s>>>(gp);
     hip_check(hipGetLastError());
 }
 
@@ -563,11 +564,16 @@ void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_
 // rows, 32x64 tiles of two waves and two stages (small LDS footprint, many
 // workgroups per CU) stream the half-size weights fastest.
 template <typename E, int TAG, int ACT = ACT_NONE>
-void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hipStream_t s)
+void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hipStream_t s, int slack = 0)
 {
     if constexpr (sizeof(E) == 2 && ACT == ACT_NONE) {
         if (bm == kGroupBMBig && !fp8) {
-            launch_grouped<E, kGroupBMBig, 256, 4, 2, 2, TAG, false>(gp, max_mtiles, s);
+            if (slack == kGroupSlack)
+                launch_grouped<E, kGroupBMBig, 256, 4, 2, 2, TAG, false, ACT_NONE, kGroupSlack>(gp, max_mtiles, s);
+            else if (slack == 0)
+                launch_grouped<E, kGroupBMBig, 256, 4, 2, 2, TAG, false>(gp, max_mtiles, s);
+            else
+                throw HipError{hipErrorInvalidValue};
             return;
         }
         if (fp8) {
@@ -578,7 +584,7 @@ void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hi
             return;
         }
     }
-    if (bm != kGroupBMSmall && bm != kGroupBM)  // a tile table these kernels cannot walk
+    if ((bm != kGroupBMSmall && bm != kGroupBM) || slack != 0)  // a tile table these kernels cannot walk
         throw HipError{hipErrorInvalidValue};
     if (bm == kGroupBMSmall)
         launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, false, ACT>(gp, max_mtiles, s);
@@ -701,6 +707,12 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     const int es = p.esize;
     const int mlp_bm = mlp_bm_for(p, P, train);
     const int gbm = mlp_bm ? mlp_bm : group_bm_for(P, N, !train && !p.fp8 && es == 2);
+    // 256-row tiles: when experts average at most 256 + kGroupSlack rows, an
+    // expert's last tile takes up to kGroupSlack more rows, so an expert a few
+    // rows past 256 streams its weights once (measured: wide_prefill's grouped
+    // GEMMs -7 %); with more rows per expert (zipf_skew: 512 on average) the
+    // larger A stage of those tiles costs more than the tails it saves (+3 %)
+    const int slack = (gbm == kGroupBMBig && P <= (int64_t)N * (kGroupBMBig + kGroupSlack)) ? kGroupSlack : 0;
     const int64_t max_mt = max_mtiles_for(P, N, gbm);
     StageTimer tm{h, s, -1};
     if (h->prof && h->prof_used < h->prof_cap)
@@ -762,7 +774,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     if (nchunks <= 64) {
         tm.begin(ST_FINALIZE);
         dispatch_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(
-            w.chunk_counts, nchunks, w.idx, w.rank, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm, w.chunk_base,
+            w.chunk_counts, nchunks, w.idx, w.rank, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm, slack, w.chunk_base,
             w.counts, w.offsets, w.tile_expert, w.tile_row0, w.n_mtiles, w.pos, w.perm);
         hip_check(hipGetLastError());
         tm.end(ST_FINALIZE);
@@ -776,7 +788,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
         tm.begin(ST_FINALIZE);
         const int64_t blocks = std::min<int64_t>((P + 1023) / 1024, 256);
         finalize_kernel<<<dim3((unsigned)blocks), dim3(1024), 0, s>>>(
-            w.idx, w.rank, w.chunk_base, w.counts, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm,
+            w.idx, w.rank, w.chunk_base, w.counts, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm, slack,
             w.offsets, w.tile_expert, w.tile_row0, w.n_mtiles, w.pos, w.perm);
         hip_check(hipGetLastError());
         tm.end(ST_FINALIZE);
@@ -842,7 +854,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     else if (train)
         grouped_gemm<E, kTagG1Raw, ACT_RELU2>(g1, max_mt, gbm, false, s);
     else
-        grouped_gemm<E, kTagG1>(g1, max_mt, gbm, p.fp8, s);
+        grouped_gemm<E, kTagG1>(g1, max_mt, gbm, p.fp8, s, slack);
     tm.end(ST_GEMM1);
 
     // 6: Y = H W2_e
@@ -865,7 +877,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     g2.C32 = nullptr;
     g2.c_split = 0;
     tm.begin(ST_GEMM2);
-    grouped_gemm<E, kTagG2>(g2, max_mt, gbm, p.fp8, s);
+    grouped_gemm<E, kTagG2>(g2, max_mt, gbm, p.fp8, s, slack);
     tm.end(ST_GEMM2);
     }
 

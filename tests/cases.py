@@ -52,6 +52,17 @@ BACKWARD_SHAPES = [
 ]
 
 
+# test_expert_rows_at_tile_boundaries: a zero router, four experts holding T
+# rows each (seed = T).  The bf16 forward's 256-row tiles take up to 320 rows
+# in an expert's last tile: 255..320 rows are one tile, 321 two (256 + 65),
+# 513 two (256 + 257), 577 three (256 + 256 + 65).
+TILE_ROWS = [255, 256, 257, 320, 321, 513, 577]
+
+
+def tile_rows_shape(T):
+    return shape(T=T, d=256, l=128, m=192, n_experts=16, top_k=4, n_shared=1, m_shared=128, dtype="bf16")
+
+
 def edge_workload(cfg, dtype):
     return random_workload(shape(dtype=dtype, **cfg), seed=cfg["T"])
 

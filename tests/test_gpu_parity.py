@@ -107,13 +107,14 @@ def test_zero_router_ties_fill_first_experts():
     G.check_stages(out, wl, ref, toks, np.ones(len(toks), dtype=bool))
 
 
-@pytest.mark.parametrize("T", [255, 256, 257, 513])
+@pytest.mark.parametrize("T", C.TILE_ROWS)
 def test_expert_rows_at_tile_boundaries(T):
     """W_r = 0 on a bf16 prefill shape: experts 0..3 hold exactly T rows each
-    and the other 12 none, so each expert's last grouped-GEMM tile (256 rows
-    in the bf16 forward) is full, one row short or one row long.  Every token
-    is checked, stage by stage."""
-    sh = shape(T=T, d=256, l=128, m=192, n_experts=16, top_k=4, n_shared=1, m_shared=128, dtype="bf16")
+    and the other 12 none.  The bf16 forward's grouped GEMMs take 256-row
+    tiles whose last one per expert holds up to 320 rows: full tiles, one row
+    short or long, the 320-row maximum and one past it.  Every token is
+    checked, stage by stage."""
+    sh = C.tile_rows_shape(T)
     arr = random_arrays(sh, np.random.default_rng(T))
     arr["w_router"] = np.zeros_like(arr["w_router"])
     wl = workload_from_arrays(sh, arr)

@@ -39,9 +39,7 @@ NARROW_FWD = (
     + [(f"fp8_{i}", (lambda c=c: C.fp8_workload(c))) for i, c in enumerate(C.FP8_SHAPES)]
     + [(f"swiglu{i}", (lambda c=c: C.swiglu_workload(c, "bf16"))) for i, c in enumerate(C.SWIGLU_SHAPES)]
     + [(f"swiglu_fp8_{i}", (lambda c=c: C.swiglu_fp8_workload(c))) for i, c in enumerate(C.FP8_SHAPES)]
-    + [(f"tile_rows{T}", (lambda T=T: _zero_router(shape(T=T, d=256, l=128, m=192, n_experts=16, top_k=4,
-                                                           n_shared=1, m_shared=128, dtype="bf16"), T)))
-       for T in (255, 256, 257, 513)]
+    + [(f"tile_rows{T}", (lambda T=T: _zero_router(C.tile_rows_shape(T), T))) for T in C.TILE_ROWS]
     + [("zero_router", lambda: _zero_router(shape(T=1000, d=256, l=128, m=192, n_experts=32, top_k=4, n_shared=1,
                                                   m_shared=128, dtype="bf16"), 3)),
        ("straddle", lambda: random_workload(shape(T=2048, d=256, l=128, m=192, n_experts=16, top_k=2, n_shared=1,
