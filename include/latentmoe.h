@@ -187,8 +187,11 @@ int latentmoe_forward(latentmoe_handle *h, const void *x, void *y, int64_t T,
  * they differ by the fp32 summation order only.  Every call on one GPU
  * shares that GPU's array and leaves its contents behind: calls that
  * overlap on one GPU (two streams, two handles, two host threads) race and
- * must be serialised by the caller.  Nothing in the array needs clearing
- * between calls.  The workspace needed is about T (K' (4 + 2 (m + l)) +
+ * must be serialised by the caller -- a race can also leave the arrival
+ * counters of the few-row split GEMMs (at the start of the array, zeroed
+ * once when the first handle on the GPU is created, and left at zero by
+ * every call) nonzero, which makes the later calls on that GPU wrong.
+ * Nothing in the array needs clearing between calls.  The workspace needed is about T (K' (4 + 2 (m + l)) +
  * 4 N' + 2 (l + S m_s)) bytes for bf16 layers (e.g. readme widths: about 100
  * KB per token, about 650 tokens fit).  Errors: as latentmoe_forward, and
  * LATENTMOE_ERR_EXCEEDS_SCRATCH when T tokens need more than the array. */

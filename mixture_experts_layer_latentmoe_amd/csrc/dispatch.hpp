@@ -23,8 +23,13 @@
 //                      and the (expert, first row) tile table of the grouped
 //                      GEMMs
 //   dispatch_small_kernel  both in one workgroup when a batch has at most 64
-//                      chunks (decode-sized batches)
-// All integer, no atomics: the same idx always gives the same bits.
+//                      chunks
+//   dispatch_tiny_kernel   batches of at most 64 tokens, straight from idx:
+//                      per expert the 64-bit mask of the tokens that chose
+//                      it (LDS atomic ORs, whose order does not matter);
+//                      counts[e] = popc(mask[e]) and
+//                      pos[t, k] = offsets[e] + popc(mask[e] & (2^t - 1))
+// All integer, no ordering atomics: the same idx always gives the same bits.
 #pragma once
 
 #include "common.hpp"
@@ -74,22 +79,17 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int *__restrict__
         counts[e] = carry;
 }
 
-// The part of the order every workgroup computes: an exclusive scan of the
-// counts into offsets (in LDS), then pos/perm for the pairs q = q0, q0 + qs,
-// ...; `lead` also publishes offsets and the (expert, first row) tile table.
-// Tiles are BM rows from each expert's first row, except that the last one
-// may hold up to BM + slack rows: max(1, ceil((c - slack) / BM)) tiles for an
-// expert with c > 0 rows (slack 0: ceil(c / BM)).
-// 1024 threads, N' <= 1024; c = counts[threadIdx.x] (0 past N').
-__device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int64_t qs, const int *__restrict__ idx,
-                                               const int *__restrict__ rank, const int *__restrict__ chunk_base, int T,
-                                               int K, int N, int chunk_tokens, int ld_chunks, int BM, int slack,
-                                               int *__restrict__ offsets, int *__restrict__ tile_expert,
-                                               int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
-                                               int *__restrict__ pos, int *__restrict__ perm, int *s_off, int *s_wsum)
+// Exclusive scan of the counts (c = counts[threadIdx.x], 0 past N') into
+// s_off; `lead` also publishes offsets and the (expert, first row) tile table
+// of the grouped GEMMs.  Tiles are BM rows from each expert's first row,
+// except that the last one may hold up to BM + slack rows: max(1, ceil((c -
+// slack) / BM)) tiles for an expert with c > 0 rows (slack 0: ceil(c / BM)).
+// 1024 threads, N' <= 1024; every thread calls it.  s_off is complete on return.
+__device__ __forceinline__ void block_offsets(int c, bool lead, int N, int BM, int slack, int *__restrict__ offsets,
+                                              int *__restrict__ tile_expert, int *__restrict__ tile_row0,
+                                              int *__restrict__ n_mtiles, int *s_off, int *s_wsum)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // block-wide exclusive scan of counts
     const int incl = wave_incl_scan(c, lane);
     if (lane == 63)
         s_wsum[wave] = incl;
@@ -109,7 +109,6 @@ __device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int
         // tile table: same scan over the tile counts
         const int nt = c > 0 ? max(1, (c - slack + BM - 1) / BM) : 0;
         const int tincl = wave_incl_scan(nt, lane);
-        __syncthreads();
         if (lane == 63)
             s_wsum[wave] = tincl;
         __syncthreads();
@@ -124,7 +123,18 @@ __device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int
         if (tid == 1023)
             *n_mtiles = texcl + nt;
     }
+}
 
+// The part of the chunked order every workgroup computes: the offsets (and,
+// if lead, the tile table), then pos/perm for the pairs q = q0, q0 + qs, ...
+__device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int64_t qs, const int *__restrict__ idx,
+                                               const int *__restrict__ rank, const int *__restrict__ chunk_base, int T,
+                                               int K, int N, int chunk_tokens, int ld_chunks, int BM, int slack,
+                                               int *__restrict__ offsets, int *__restrict__ tile_expert,
+                                               int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
+                                               int *__restrict__ pos, int *__restrict__ perm, int *s_off, int *s_wsum)
+{
+    block_offsets(c, lead, N, BM, slack, offsets, tile_expert, tile_row0, n_mtiles, s_off, s_wsum);
     const int64_t P = (int64_t)T * K;
     for (int64_t q = q0; q < P; q += qs) {
         const int t = (int)(q / K);
@@ -155,9 +165,10 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ 
 }
 
 // Small batches (at most 64 chunks): the chunk scan and finalize in one
-// workgroup of 1024 threads -- one launch instead of two.  A wave scans an
-// expert's chunk counts with one lane per chunk; the chunk bases it writes
-// are read back by other waves of this workgroup after the barrier.
+// workgroup of 1024 threads -- one launch instead of two.  Thread e scans
+// expert e's row of chunk counts in registers (every load of the row issued
+// first); the chunk bases it writes are read back by other threads of this
+// workgroup after the barriers of the offsets scan.
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restrict__ chunk_counts, int nchunks,
                                                              const int *__restrict__ idx, const int *__restrict__ rank,
                                                              int T, int K, int N, int chunk_tokens, int ld_chunks,
@@ -169,35 +180,78 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restr
 {
     __shared__ int s_off[1024];
     __shared__ int s_wsum[16];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    // a wave's experts e = wave + 16 u, up to 16 at a time with every load
-    // issued before the scans (a chain of dependent loads would dominate)
-    for (int e0 = wave; e0 < N; e0 += 16 * 16) {
-        int v[16];
+    const int tid = threadIdx.x;
+    int c = 0;
+    if (tid < N) {
+        // ld_chunks is a multiple of 4; entries past nchunks are not counts
+        const int4 *row = reinterpret_cast<const int4 *>(chunk_counts + (int64_t)tid * ld_chunks);
+        int4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+            v[u] = 4 * u < nchunks ? row[u] : make_int4(0, 0, 0, 0);
+        int4 *out = reinterpret_cast<int4 *>(chunk_base + (int64_t)tid * ld_chunks);
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-            const int e = e0 + 16 * u;
-            v[u] = (e < N && lane < nchunks) ? chunk_counts[(int64_t)e * ld_chunks + lane] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = e0 + 16 * u;
-            if (e >= N)
+            if (4 * u >= nchunks)
                 break;
-            const int incl = wave_incl_scan(v[u], lane);
-            if (lane < nchunks)
-                chunk_base[(int64_t)e * ld_chunks + lane] = incl - v[u];
-            if (lane == 63) {
-                s_off[e] = incl;
-                counts[e] = incl;
-            }
+            const int n = nchunks - 4 * u;
+            int4 b;
+            b.x = c;
+            c += v[u].x;
+            b.y = c;
+            c += n > 1 ? v[u].y : 0;
+            b.z = c;
+            c += n > 2 ? v[u].z : 0;
+            b.w = c;
+            c += n > 3 ? v[u].w : 0;
+            out[u] = b;
         }
+        counts[tid] = c;
     }
-    __syncthreads();
-    const int c = (tid < N) ? s_off[tid] : 0;
-    __syncthreads();  // s_off is reused for the offsets
     finalize_block(c, true, tid, 1024, idx, rank, chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, slack, offsets,
                    tile_expert, tile_row0, n_mtiles, pos, perm, s_off, s_wsum);
+}
+
+// Batches of at most 64 tokens (kTinyTokens), one workgroup of 1024 threads,
+// N' <= 1024, T K' <= 4096: every pair's expert is loaded up front, the token
+// masks are ORed together in LDS, and the rest reads LDS only.
+__global__ __launch_bounds__(1024) void dispatch_tiny_kernel(const int *__restrict__ idx, int T, int K, int N, int BM,
+                                                            int slack, int *__restrict__ counts,
+                                                            int *__restrict__ offsets, int *__restrict__ tile_expert,
+                                                            int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
+                                                            int *__restrict__ pos, int *__restrict__ perm)
+{
+    __shared__ unsigned long long s_mask[1024];
+    __shared__ int s_off[1024];
+    __shared__ int s_wsum[16];
+    const int tid = threadIdx.x, P = T * K;
+    int e_q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int q = tid + 1024 * j;
+        e_q[j] = q < P ? idx[q] : -1;
+    }
+    s_mask[tid] = 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (e_q[j] >= 0)
+            atomicOr(&s_mask[e_q[j]], 1ull << ((tid + 1024 * j) / K));
+    __syncthreads();
+    const int c = tid < N ? __popcll(s_mask[tid]) : 0;
+    if (tid < N)
+        counts[tid] = c;
+    block_offsets(c, true, N, BM, slack, offsets, tile_expert, tile_row0, n_mtiles, s_off, s_wsum);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int e = e_q[j];
+        if (e < 0)
+            continue;
+        const int q = tid + 1024 * j, t = q / K;
+        const int p = s_off[e] + __popcll(s_mask[e] & ((1ull << t) - 1ull));
+        pos[q] = p;
+        perm[p] = t;
+    }
 }
 
 }  // namespace lmoe

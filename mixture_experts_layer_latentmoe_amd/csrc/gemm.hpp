@@ -71,6 +71,8 @@ struct GemmParams {
                         // raw fp32 sums go to partial[split][M][N] and a reduce
                         // kernel applies the epilogue
     float *partial;
+    int *counters;      // dense, few rows, splitk > 1: one arrival counter per column group,
+                        // zero between launches (fewrow_split_kernel)
     // grouped mode
     const int *gather;       // dispatch row -> A row, or nullptr (A rows = dispatch rows)
     const int *tile_expert;  // [tiles]

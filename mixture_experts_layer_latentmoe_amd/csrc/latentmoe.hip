@@ -135,12 +135,15 @@ struct Workspace {
     float *partial;
     int64_t partial_cap;  // floats at `partial`
     int64_t ld_chunks;    // row length of the expert-major chunk arrays
+    int *counters;        // [kSplitCounters] arrival counters of fewrow_split_kernel: zero when
+                          // the workspace is made, and each launch leaves them at zero
 };
 
 constexpr int kGroupBM = 128, kGroupBMBig = 256, kGroupBMSmall = 32, kMinGroupBM = 32;
 constexpr int kGroupSlack = 64;  // extra rows the 256-row tiles take (the kernel's XR)
 constexpr int kNoColumn = 1 << 30;  // relu2_from / glu_from: no such columns
 constexpr int kSplitKMaxRows = 256, kSplitKMax = 16;
+constexpr int kSplitCounters = 4096;  // column groups of 32 of the widest few-row split GEMM
 
 int64_t max_mtiles_for(int64_t P, int64_t N, int bm) { return (P + bm - 1) / bm + std::min<int64_t>(N, P); }
 
@@ -264,20 +267,25 @@ Plan make_plan(const latentmoe_config *c)
 }
 
 // fp32 partial sums of split-K GEMMs: up to kSplitKMax splits of the widest
-// dense output, for up to kSplitKMaxRows rows of T
+// dense output, for up to kSplitKMaxRows rows of T, and at least the
+// kFewRowMaxSplits tiles of 32 x 64 per column group of the few-row split
+// kernel (so that its split count does not depend on T)
 int64_t split_partial_floats(const Plan &p, int64_t T)
 {
-    return (int64_t)kSplitKMax * std::min<int64_t>(T, kSplitKMaxRows) * std::max(p.n_x, p.d);
+    const int64_t wide = std::max(p.n_x, p.d);
+    return std::max<int64_t>((int64_t)kSplitKMax * std::min<int64_t>(T, kSplitKMaxRows) * wide,
+                             (int64_t)kFewRowMaxSplits * ((wide + 31) / 32) * 2048);
 }
 
 struct Layout {
-    int64_t off_idx, off_gate, off_rank, off_pos, off_perm, off_cc, off_cb, off_counts, off_offsets, off_te, off_tr,
-        off_nmt, off_logits, off_zh, off_H, off_Yp, off_part, total;
+    int64_t off_cnt, off_idx, off_gate, off_rank, off_pos, off_perm, off_cc, off_cb, off_counts, off_offsets, off_te,
+        off_tr, off_nmt, off_logits, off_zh, off_H, off_Yp, off_part, total;
     int64_t ld_chunks, partial_floats;
 };
 
 // Byte offsets of a workspace for T tokens with room for `partial_floats`
-// split-K partial sums (256-byte aligned pieces).
+// split-K partial sums (256-byte aligned pieces).  The split counters come
+// first, at the same place for every T.
 Layout ws_layout(const Plan &p, int64_t T, int64_t partial_floats)
 {
     Layout L;
@@ -291,6 +299,7 @@ Layout ws_layout(const Plan &p, int64_t T, int64_t partial_floats)
     L.ld_chunks = align_up((T + kRouterTokens - 1) / kRouterTokens, 4);
     L.partial_floats = partial_floats;
     const int64_t mt = max_mtiles_for(P, p.N, kMinGroupBM);
+    L.off_cnt = take(4 * kSplitCounters);
     L.off_idx = take(4 * P);
     L.off_gate = take(4 * P);
     L.off_rank = take(4 * P);
@@ -335,6 +344,7 @@ Workspace carve_ws(void *base, const Layout &L)
     w.partial = reinterpret_cast<float *>(b + L.off_part);
     w.partial_cap = L.partial_floats;
     w.ld_chunks = L.ld_chunks;
+    w.counters = reinterpret_cast<int *>(b + L.off_cnt);
     return w;
 }
 
@@ -498,19 +508,55 @@ void launch_skinny(const GemmParams &gp, hipStream_t s)
     hip_check(hipGetLastError());
 }
 
+// Few-row GEMMs with K split over workgroups (fewrow_split_kernel) when the
+// 16-column kernel would leave more than a quarter of the CUs without a
+// workgroup (N < 3072 columns): 32-column groups, S splits so that about one
+// workgroup per CU runs.  Measured at 64 rows: N = 2048, K = 3328 (the decode
+// up-projection) 9.9 us with S = 4 against 12.1 us for the 16-column kernel;
+// N = 3584, K = 2048 (the decode x-pass) 9.9 us with S = 2 against 9.2 us.
+// Returns false (nothing launched) when it does not apply.
+template <typename E, int TAG>
+bool launch_fewrow(GemmParams gp, float *partial, int64_t cap_floats, int *counters, hipStream_t s)
+{
+    const int ncg = (gp.N + 31) / 32;
+    if (ncg > 96 || ncg > kSplitCounters || !counters)
+        return false;
+    const int MT = gp.M <= 32 ? 1 : 2;
+    const int64_t tile = (int64_t)MT * 1024;  // floats of one split's tile
+    const int nkt = gp.K / (128 / (int)sizeof(E));
+    int S = std::min(std::min(kFewRowMaxSplits, 256 / ncg), nkt);
+    S = (int)std::min<int64_t>(S, cap_floats / (ncg * tile));
+    if (S < 2)
+        return false;
+    const int per = (nkt + S - 1) / S;
+    gp.splitk = (nkt + per - 1) / per;  // every split gets at least one k-tile
+    gp.partial = partial;
+    gp.counters = counters;
+    const dim3 grid((unsigned)(ncg * gp.splitk));
+    if (MT == 1)
+        fewrow_split_kernel<E, 1, 1, 8, TAG><<<grid, dim3(512), 0, s>>>(gp);
+    else
+        fewrow_split_kernel<E, 2, 1, 8, TAG><<<grid, dim3(512), 0, s>>>(gp);
+    hip_check(hipGetLastError());
+    return true;
+}
+
 // Dense GEMMs: 256x256 tiles (8 waves) when they come close to filling the
 // 256 CUs once, else 128x256 (8 waves, three LDS stages) when those fill it,
 // else 128x128 (4 waves, two workgroups per CU) when those do; up to
-// 64 rows (decode) the few-row kernel (K split over the waves of a
-// workgroup); otherwise up to kSplitKMaxRows rows 64x128 tiles with K split
-// so that ~512 workgroups stream the weights, followed by a fixed-order
-// reduce that applies the epilogue.
+// 64 rows (decode) the few-row kernels (K split over the waves of a
+// workgroup, and over workgroups for narrow outputs); otherwise up to
+// kSplitKMaxRows rows 64x128 tiles with K split so that ~512 workgroups
+// stream the weights, followed by a fixed-order reduce that applies the
+// epilogue.
 template <typename E, int TAG>
-void dense_gemm(const GemmParams &gp, float *partial, int64_t cap_floats, hipStream_t s)
+void dense_gemm(const GemmParams &gp, float *partial, int64_t cap_floats, int *counters, hipStream_t s)
 {
     const int64_t big = ((gp.M + 255) / 256) * ((gp.N + 255) / 256);
     const int64_t mid = ((gp.M + 127) / 128) * ((gp.N + 127) / 128);
     if (gp.M <= 64 && mid < 256) {
+        if (launch_fewrow<E, TAG>(gp, partial, cap_floats, counters, s))
+            return;
         if (gp.M <= 32)
             launch_skinny<E, 1, 8, 16, TAG>(gp, s);
         else
@@ -641,29 +687,41 @@ void launch_mlp(const Plan &p, const MlpParams &mp, int64_t max_mtiles, hipStrea
         throw HipError{hipErrorInvalidValue};
 }
 
-template <int NPL>
+// Selection: kRouterTokens tokens per workgroup with the chunk counts and
+// ranks of the chunked dispatch; batches of at most kTinyTokens tokens take
+// kTinySelectWaves tokens per workgroup and the mask dispatch instead.
+template <int NPL, int TOK, bool CHUNKS>
 void launch_select_n(const Plan &p, const Workspace &w, int T, hipStream_t s)
 {
-    const int blocks = (T + kRouterTokens - 1) / kRouterTokens;
-    router_select_kernel<NPL><<<dim3(blocks), dim3(64 * kSelectWaves), router_select_smem_bytes((int)p.N, (int)p.K),
-                                s>>>(w.logits, T, (int)p.N, (int)p.K, w.idx, w.gate, w.rank, w.chunk_counts,
-                                     (int)w.ld_chunks);
+    const int blocks = (T + TOK - 1) / TOK;
+    router_select_kernel<NPL, TOK, CHUNKS>
+        <<<dim3(blocks), dim3(64 * TOK), router_select_smem_bytes((int)p.N, (int)p.K, TOK, CHUNKS), s>>>(
+            w.logits, T, (int)p.N, (int)p.K, w.idx, w.gate, w.rank, w.chunk_counts, (int)w.ld_chunks);
     hip_check(hipGetLastError());
+}
+
+template <int NPL>
+void launch_select_tok(const Plan &p, const Workspace &w, int T, hipStream_t s)
+{
+    if (T <= kTinyTokens)
+        launch_select_n<NPL, kTinySelectWaves, false>(p, w, T, s);
+    else
+        launch_select_n<NPL, kRouterTokens, true>(p, w, T, s);
 }
 
 void launch_select(const Plan &p, const Workspace &w, int T, hipStream_t s)
 {
     const int64_t npl = (p.N + 63) / 64;
     if (npl <= 1)
-        launch_select_n<1>(p, w, T, s);
+        launch_select_tok<1>(p, w, T, s);
     else if (npl <= 2)
-        launch_select_n<2>(p, w, T, s);
+        launch_select_tok<2>(p, w, T, s);
     else if (npl <= 4)
-        launch_select_n<4>(p, w, T, s);
+        launch_select_tok<4>(p, w, T, s);
     else if (npl <= 8)
-        launch_select_n<8>(p, w, T, s);
+        launch_select_tok<8>(p, w, T, s);
     else
-        launch_select_n<16>(p, w, T, s);
+        launch_select_tok<16>(p, w, T, s);
 }
 
 // ---- the forward -----------------------------------------------------------
@@ -747,9 +805,9 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     }
     tm.begin(ST_GEMM_X);
     if (train)
-        dense_gemm<E, kTagXRaw>(g, w.partial, w.partial_cap, s);
+        dense_gemm<E, kTagXRaw>(g, w.partial, w.partial_cap, w.counters, s);
     else
-        dense_gemm<E, kTagX>(g, w.partial, w.partial_cap, s);
+        dense_gemm<E, kTagX>(g, w.partial, w.partial_cap, w.counters, s);
     if (train) {
         const int64_t n = (int64_t)T * p.ld_zh;
         xpass_act_kernel<E><<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
@@ -771,7 +829,13 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     launch_select(p, w, T, s);
     tm.end(ST_SELECT);
     // 2-4: dispatch order (small batches: one workgroup, one launch)
-    if (nchunks <= 64) {
+    if (T <= kTinyTokens) {
+        tm.begin(ST_FINALIZE);
+        dispatch_tiny_kernel<<<dim3(1), dim3(1024), 0, s>>>(w.idx, T, K, N, gbm, slack, w.counts, w.offsets,
+                                                            w.tile_expert, w.tile_row0, w.n_mtiles, w.pos, w.perm);
+        hip_check(hipGetLastError());
+        tm.end(ST_FINALIZE);
+    } else if (nchunks <= 64) {
         tm.begin(ST_FINALIZE);
         dispatch_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(
             w.chunk_counts, nchunks, w.idx, w.rank, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm, slack, w.chunk_base,
@@ -907,7 +971,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     g3.glu_from = kNoColumn;
     g3.group_m = 8;
     tm.begin(ST_GEMM_UP);
-    dense_gemm<E, kTagUp>(g3, w.partial, w.partial_cap, s);
+    dense_gemm<E, kTagUp>(g3, w.partial, w.partial_cap, w.counters, s);
     tm.end(ST_GEMM_UP);
 
     if (dbg) {
@@ -958,9 +1022,16 @@ hipError_t scratch_address(int device, void **out)
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_addr[device]) {
         void *ptr = nullptr;
-        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
         if (e != hipSuccess || !ptr)
             return e != hipSuccess ? e : hipErrorInvalidSymbol;
+        // the split counters at the start of every workspace layout start at
+        // zero (the kernels leave them so)
+        e = hipMemset(ptr, 0, sizeof(int) * kSplitCounters);
+        if (e == hipSuccess)
+            e = hipDeviceSynchronize();
+        if (e != hipSuccess)
+            return e;
         g_scratch_addr[device] = ptr;
     }
     *out = g_scratch_addr[device];
@@ -1301,7 +1372,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     ga.N = (int)p.ld_zh;
     ga.K = (int)p.d;
     ga.group_m = 8;
-    dense_gemm<E, kTagDgrad>(ga, h->wk.partial, h->wk.partial_cap, s);
+    dense_gemm<E, kTagDgrad>(ga, h->wk.partial, h->wk.partial_cap, h->wk.counters, s);
     // shared experts: the gradient of their pre-activations -> dX[:, N' + l ..]
     if (sms > 0) {
         const int64_t n = (int64_t)T * sms;
@@ -1374,7 +1445,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
         gd.N = (int)p.d;
         gd.K = (int)nxp;
         gd.group_m = 8;
-        dense_gemm<E, kTagDgrad>(gd, h->wk.partial, h->wk.partial_cap, s);
+        dense_gemm<E, kTagDgrad>(gd, h->wk.partial, h->wk.partial_cap, h->wk.counters, s);
     }
 
     // ---- weight gradients (fp32), sums over tokens / an expert's rows ----
@@ -1588,6 +1659,7 @@ int latentmoe_create(const latentmoe_config *cfg, const latentmoe_weights *w, vo
             return LATENTMOE_ERR_OUT_OF_MEMORY;
         }
         h->wk = carve_ws(h->ws, L);
+        hip_check(hipMemsetAsync(h->wk.counters, 0, sizeof(int) * kSplitCounters, s));
         if (p.dtype == LATENTMOE_DTYPE_BF16)
             repack_weights<bf16>(h, w, s);
         else

@@ -11,7 +11,10 @@
 // produces z and the shared-expert hidden layer (their weights are one
 // concatenated matrix), stored in fp32.  This kernel owns 16 tokens (one
 // dispatch chunk), 16 waves, one token per wave -- small chunks keep every
-// CU busy at a few thousand tokens:
+// CU busy at a few thousand tokens.  Batches of at most kTinyTokens tokens
+// take workgroups of 4 tokens (one wave per SIMD: the selection is a chain of
+// dependent wave operations, and four waves sharing a SIMD take four times as
+// long) and skip step 4 (dispatch_tiny_kernel orders them by token masks):
 //   1. scores become order-preserving 32-bit keys (-0.0 folded into +0.0, so
 //      signed zeros tie); a 32-round radix search, counting with wave ballots,
 //      finds the K'-th largest key; every key above it is selected, and of the
@@ -19,7 +22,9 @@
 //   2. the selected keys are ranked (score descending, index ascending) by
 //      comparing each against the others through LDS;
 //   3. gate_k = exp(s_k - s_max) / sum_j exp(s_j - s_max) over the selected
-//      set, which is the renormalised softmax (its denominator cancels);
+//      set, which is the renormalised softmax (its denominator cancels); s_k
+//      and s_max come back from the keys, the sum is a fixed-order DPP
+//      reduction;
 //   4. a bit mask per expert marks which tokens of the chunk chose it;
 //      popcounts give each (token, slot) its rank inside the chunk and the
 //      chunk's count per expert -- integer-exact, independent of the order of
@@ -32,6 +37,8 @@ namespace lmoe {
 
 constexpr int kRouterTokens = 16;  // tokens per workgroup = one dispatch chunk
 constexpr int kSelectWaves = 16;
+constexpr int kTinyTokens = 64;    // batches up to this size: mask dispatch (64-bit token masks)
+constexpr int kTinySelectWaves = 4;
 
 __device__ __forceinline__ unsigned ordered_key(float v)
 {
@@ -40,14 +47,26 @@ __device__ __forceinline__ unsigned ordered_key(float v)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // > 0 for every finite v
 }
 
+__device__ __forceinline__ float key_value(unsigned k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
 __device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
 
-__device__ __forceinline__ float wave_sum_f32(float v)
+// Sum over the 64 lanes in a fixed order with DPP moves (no LDS round trips):
+// swaps inside quads, mirrors inside half-rows and rows (every lane then holds
+// its row's sum), row 0 into row 1 and row 2 into row 3, then rows 0-1 into
+// row 3; the total is lane 63's.
+__device__ __forceinline__ float wave_sum_dpp(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // A token's scores in registers: expert e = lane + 64 j in val[j] (0 past N').
@@ -109,8 +128,9 @@ __device__ __forceinline__ void select_token_vals(const float (&val)[NPL], int N
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    // 2. rank of slot `lane` by (key descending, index ascending)
-    unsigned mk = 0u;
+    // 2. rank of slot `lane` by (key descending, index ascending); the
+    // largest selected key on the way
+    unsigned mk = 0u, top = 0u;
     int me = 0x7fffffff, rank = 0;
     if (lane < K) {
         mk = wkey[lane];
@@ -119,20 +139,13 @@ __device__ __forceinline__ void select_token_vals(const float (&val)[NPL], int N
             const unsigned ok = wkey[q];
             const int oe = wexp[q];
             rank += (ok > mk || (ok == mk && oe < me)) ? 1 : 0;
+            top = max(top, ok);
         }
     }
-    // 3. gates; the score of slot `lane`'s expert from the lane that holds it
-    float s_pick = 0.f;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-        const float v = __shfl(val[j], me & 63, 64);
-        if ((me >> 6) == j)
-            s_pick = v;
-    }
-    const float s_mine = (lane < K) ? s_pick : 0.f;
-    const float s_top = __shfl(s_mine, __ffsll((long long)__ballot(lane < K && rank == 0)) - 1, 64);
-    const float g = (lane < K) ? expf(s_mine - s_top) : 0.f;
-    const float gsum = wave_sum_f32(g);
+    // 3. gates from the scores the keys encode (a key maps back to its score
+    // exactly, -0.0 as +0.0, which changes no difference)
+    const float g = (lane < K) ? expf(key_value(mk) - key_value(top)) : 0.f;
+    const float gsum = wave_sum_dpp(g);
     me_out = me;
     rank_out = rank;
     gate_out = g / gsum;
@@ -147,61 +160,58 @@ __device__ __forceinline__ void select_token(const float *__restrict__ row, int 
     select_token_vals<NPL>(val, N, K, lane, wkey, wexp, me_out, rank_out, gate_out);
 }
 
-// NPL = ceil(N' / 64) scores held per lane (expert e = lane + 64 j).
-template <int NPL>
-__global__ __launch_bounds__(64 * kSelectWaves) void router_select_kernel(
+// NPL = ceil(N' / 64) scores held per lane (expert e = lane + 64 j); TOK
+// tokens per workgroup, one per wave; CHUNKS: also step 4 (a workgroup's
+// tokens are one dispatch chunk).
+template <int NPL, int TOK, bool CHUNKS>
+__global__ __launch_bounds__(64 * TOK) void router_select_kernel(
     const float *__restrict__ scores, int T, int N, int K, int *__restrict__ idx_out, float *__restrict__ gate_out,
     int *__restrict__ rank_out, int *__restrict__ chunk_counts, int ld_chunks)
 {
+    static_assert(TOK >= 1 && TOK <= 32, "token mask per chunk");
     extern __shared__ int rsmem[];
-    int *s_idx = rsmem;                                                          // [kRouterTokens][K]
-    unsigned *s_mask = reinterpret_cast<unsigned *>(rsmem + kRouterTokens * K);  // [N]
-    unsigned *s_key = s_mask + N;                                                // [16 waves][K]
-    int *s_exp = reinterpret_cast<int *>(s_key + kSelectWaves * K);              // [16 waves][K]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t0 = blockIdx.x * kRouterTokens;
-    for (int e = tid; e < N; e += 64 * kSelectWaves)
-        s_mask[e] = 0u;
-    unsigned *wkey = s_key + wave * K;
-    int *wexp = s_exp + wave * K;
+    unsigned *s_key = reinterpret_cast<unsigned *>(rsmem);  // [TOK waves][K]
+    int *s_exp = rsmem + TOK * K;                           // [TOK waves][K]
+    int *s_idx = s_exp + TOK * K;                           // [TOK][K]    (CHUNKS)
+    unsigned *s_mask = reinterpret_cast<unsigned *>(s_idx + TOK * K);  // [N] (CHUNKS)
+    const int tid = threadIdx.x, lane = tid & 63, r = tid >> 6;
+    const int t0 = blockIdx.x * TOK, t = t0 + r;
+    if constexpr (CHUNKS)
+        for (int e = tid; e < N; e += 64 * TOK)
+            s_mask[e] = 0u;
 
-    for (int r = wave; r < kRouterTokens; r += kSelectWaves) {
-        const int t = t0 + r;
-        if (t >= T)
-            break;
-        const float *row = scores + (int64_t)t * N;
+    if (t < T) {
         int me, rank;
         float gate;
-        select_token<NPL>(row, N, K, lane, wkey, wexp, me, rank, gate);
+        select_token<NPL>(scores + (int64_t)t * N, N, K, lane, s_key + r * K, s_exp + r * K, me, rank, gate);
         if (lane < K) {
             idx_out[(int64_t)t * K + rank] = me;
             gate_out[(int64_t)t * K + rank] = gate;
-            s_idx[r * K + rank] = me;
+            if constexpr (CHUNKS)
+                s_idx[r * K + rank] = me;
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     }
-    __syncthreads();
-
-    for (int q = tid; q < kRouterTokens * K; q += 64 * kSelectWaves) {
-        const int r = q / K;
-        if (t0 + r < T)
-            atomicOr(&s_mask[s_idx[q]], 1u << r);
+    if constexpr (CHUNKS) {
+        __syncthreads();
+        for (int q = tid; q < TOK * K; q += 64 * TOK) {
+            const int rq = q / K;
+            if (t0 + rq < T)
+                atomicOr(&s_mask[s_idx[q]], 1u << rq);
+        }
+        __syncthreads();
+        for (int q = tid; q < TOK * K; q += 64 * TOK) {
+            const int rq = q / K;
+            if (t0 + rq < T)
+                rank_out[(int64_t)t0 * K + q] = __popc(s_mask[s_idx[q]] & ((1u << rq) - 1u));
+        }
+        for (int e = tid; e < N; e += 64 * TOK)
+            chunk_counts[(int64_t)e * ld_chunks + blockIdx.x] = __popc(s_mask[e]);
     }
-    __syncthreads();
-    for (int q = tid; q < kRouterTokens * K; q += 64 * kSelectWaves) {
-        const int r = q / K;
-        if (t0 + r < T)
-            rank_out[(int64_t)t0 * K + q] = __popc(s_mask[s_idx[q]] & ((1u << r) - 1u));
-    }
-    for (int e = tid; e < N; e += 64 * kSelectWaves)
-        chunk_counts[(int64_t)e * ld_chunks + blockIdx.x] = __popc(s_mask[e]);
 }
 
-inline size_t router_select_smem_bytes(int N, int K)
+inline size_t router_select_smem_bytes(int N, int K, int tok, bool chunks)
 {
-    return sizeof(int) * (size_t)kRouterTokens * K + sizeof(unsigned) * (size_t)N +
-           2 * sizeof(int) * (size_t)kSelectWaves * K;
+    return sizeof(int) * (2 * (size_t)tok * K + (chunks ? (size_t)tok * K + N : 0));
 }
 
 }  // namespace lmoe
