@@ -131,6 +131,132 @@ def profiled_traffic(cfg: str, stage: str):
     return val if (sha == kernel_source_sha() and val is not None) else None
 
 
+# ---- rocprofv3 summaries (profiles/*.txt) -----------------------------------
+
+STAGE_OF_TAG = {0: "gemm_x_router_down_shared1", 1: "grouped_gemm1_relu2", 2: "grouped_gemm2", 3: "gemm_up_shared2",
+                4: "backward_dgrad", 5: "backward_wgrad", 6: "backward_wgrad_experts", 7: "backward_x_recompute",
+                8: "backward_gemm1_recompute"}
+# kernel template -> position of the stage tag among its integer arguments
+TAG_POS = {"gemm_kernel": 7, "skinny_gemm_kernel": 3, "fewrow_split_kernel": 3}
+FIXED_STAGE = {"expert_mlp_kernel": "expert_mlp", "router_select_kernel": "router_select",
+               "dispatch_tiny_kernel": "dispatch_finalize", "dispatch_small_kernel": "dispatch_finalize",
+               "finalize_kernel": "dispatch_finalize", "chunk_scan_kernel": "dispatch_scan",
+               "combine_kernel": "combine", "splitk_reduce_kernel": "splitk_reduce",
+               "transpose_kernel": "repack_transpose (create only)",
+               "fragmajor_kernel": "repack_fragmajor (create only)"}
+
+
+def stage_of_kernel(name: str) -> str:
+    """Layer stage of a kernel symbol as rocprofv3 prints it (mangled or not)."""
+    import re
+    for k, st in FIXED_STAGE.items():
+        if k in name:
+            return st
+    for k, pos in TAG_POS.items():
+        if re.search(r"(^|[^a-z_])" + k, name):
+            if "<" in name:  # demangled: integer arguments after the element type
+                args = name[name.index("<") + 1:name.rindex(">")].split(",")[1:]
+                vals = [a.strip() for a in args]
+                ints = [int(v == "true") if v in ("true", "false") else int(v) for v in vals]
+            else:            # mangled: Li<n>E / Lb<n>E in order
+                ints = [int(v) for v in re.findall(r"L[ib](\d+)E", name)]
+            return STAGE_OF_TAG.get(ints[pos], f"{k}[{ints[pos]}]") if len(ints) > pos else k
+    if "elementwise" in name or "vectorized" in name:
+        return "copy calibration (torch add)"
+    return name.split("(")[0][:60]
+
+
+def _csvs(d, suffix):
+    import glob
+    return sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+
+
+def summarize_trace(d):
+    """Per stage: launches, average / min / max kernel duration (us)."""
+    import csv
+    dur = {}
+    for f in _csvs(d, "kernel_trace.csv"):
+        for r in csv.DictReader(open(f)):
+            st = stage_of_kernel(r["Kernel_Name"])
+            dur.setdefault(st, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"{'stage / kernel':44s} {'calls':>6s} {'avg_us':>12s} {'min_us':>12s} {'max_us':>12s}"]
+    for st, v in sorted(dur.items(), key=lambda kv: -sum(kv[1]) / len(kv[1])):
+        lines.append(f"{st:44s} {len(v):6d} {sum(v) / len(v):12.2f} {min(v):12.2f} {max(v):12.2f}")
+    return "\n".join(lines)
+
+
+def _counters(d):
+    import csv
+    per = {}  # stage -> counter -> [per-dispatch value]
+    dur = {}
+    for f in _csvs(d, "counter_collection.csv"):
+        for r in csv.DictReader(open(f)):
+            st = stage_of_kernel(r["Kernel_Name"])
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            per.setdefault(st, {}).setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[st][r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+            if "End_Timestamp" in r and r.get("End_Timestamp"):
+                dur.setdefault(st, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    return per, dur
+
+
+def summarize_pmc(d):
+    """Per stage: the average per dispatch of every counter collected, and
+    derived figures where their inputs are there: MFMA busy share of the
+    shader cycles (SQ_VALU_MFMA_BUSY_CYCLES over 4 SIMDs x 256 CUs of
+    GRBM_GUI_ACTIVE / 8 XCDs), the vector L1's pending-miss stall share
+    (TCP_PENDING_STALL_CYCLES over TCP_TOTAL_CACHE_ACCESSES' busy cycles is not
+    defined: reported raw), the L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))
+    and the effective shader clock (GRBM_GUI_ACTIVE / 8 per kernel time)."""
+    per, dur = _counters(d)
+    lines = []
+    for st in sorted(per):
+        c = {k: sum(v.values()) / len(v) for k, v in per[st].items()}
+        n = max(len(v) for v in per[st].values())
+        us = dur.get(st, {})
+        avg_us = sum(us.values()) / len(us) if us else None
+        parts = [f"{k}={v:.6g}" for k, v in sorted(c.items())]
+        der = []
+        if "GRBM_GUI_ACTIVE" in c and avg_us:
+            der.append(f"shader_clock_GHz={c['GRBM_GUI_ACTIVE'] / 8 / (avg_us * 1e3):.3f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c:
+            der.append(f"mfma_busy={c['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * 256 * c['GRBM_GUI_ACTIVE'] / 8):.3f}")
+        hit, miss = c.get("TCC_HIT_sum", c.get("TCC_HIT")), c.get("TCC_MISS_sum", c.get("TCC_MISS"))
+        if hit is not None and miss is not None and hit + miss > 0:
+            der.append(f"l2_hit_rate={hit / (hit + miss):.3f}")
+        lines.append(f"{st} (dispatches {n}" + (f", avg {avg_us:.1f} us" if avg_us else "") + "): "
+                     + " ".join(parts + der))
+    return "\n".join(lines)
+
+
+def summarize_traffic(d_fetch, d_write):
+    """HBM bytes per launch and stage from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), scaled by what the counters read for the copy calibration
+    (a torch add of 64 Mi fp32: 256 MiB read and 256 MiB written)."""
+    f, _ = _counters(d_fetch)
+    w, _ = _counters(d_write)
+    cal = "copy calibration (torch add)"
+    fk = f[cal]["FETCH_SIZE"]
+    wk = w[cal]["WRITE_SIZE"]
+    f_cal, w_cal = sum(fk.values()) / len(fk), sum(wk.values()) / len(wk)
+    ff, wf = (256 << 20) / (f_cal * 1024), (256 << 20) / (w_cal * 1024)
+    lines = [f"# calibration: a torch elementwise add of 64Mi fp32 reads 256 MiB and writes 256 MiB per launch;",
+             f"#   it reads FETCH_SIZE {f_cal:.1f} KiB and WRITE_SIZE {w_cal:.1f} KiB,",
+             f"#   so bytes = FETCH_SIZE_KiB * 1024 * {ff:.4f} and WRITE_SIZE_KiB * 1024 * {wf:.4f}",
+             f"fetch_factor: {ff:.4f}", f"write_factor: {wf:.4f}",
+             f"{'stage / kernel':44s} {'launches':>8s} {'FETCH_KiB':>10s} {'WRITE_KiB':>12s} {'read_MB':>12s} "
+             f"{'written_MB':>12s}"]
+    for st in sorted(set(f) & set(w)):
+        if st == cal:
+            continue
+        fv = sum(f[st]["FETCH_SIZE"].values()) / len(f[st]["FETCH_SIZE"])
+        wv = sum(w[st]["WRITE_SIZE"].values()) / len(w[st]["WRITE_SIZE"])
+        rb, wb = fv * 1024 * ff, wv * 1024 * wf
+        lines.append(f"{st:44s} {len(f[st]['FETCH_SIZE']):8d} {fv:10.1f} {wv:12.1f} {rb / 1e6:12.1f} {wb / 1e6:12.1f}")
+        lines.append(f"traffic_bytes[{st}]: {rb + wb:.0f}")
+    return "\n".join(lines)
+
+
 def cpu_baseline(wl, target_s=12.0):
     """The oracle as it stands, on all host threads, on a bounded sample."""
     from oracle import oracle
@@ -323,6 +449,18 @@ def measure(name, args, log):
 
 
 def main():
+    if len(sys.argv) >= 3 and sys.argv[1] == "--summarize":
+        # python bench.py --summarize trace|pmc DIR | traffic FETCH_DIR WRITE_DIR [--title TEXT] [--cmd TEXT]...
+        kind, rest = sys.argv[2], sys.argv[3:]
+        head = []
+        while len(rest) >= 2 and rest[-2] in ("--title", "--cmd"):
+            head.insert(0, ("# " if rest[-2] == "--title" else "# command: ") + rest[-1])
+            rest = rest[:-2]
+        head.append(f"# kernel sources sha256[:16] of csrc/*: {kernel_source_sha()}")
+        body = {"trace": lambda: summarize_trace(rest[0]), "pmc": lambda: summarize_pmc(rest[0]),
+                "traffic": lambda: summarize_traffic(rest[0], rest[1])}[kind]()
+        print("\n".join(head + [body]))
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

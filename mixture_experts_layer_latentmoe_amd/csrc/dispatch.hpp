@@ -20,8 +20,7 @@
 //   finalize_kernel    every workgroup scans counts into offsets in LDS, then
 //                      pos = offsets[e] + chunk_base[e][c] + rank and
 //                      perm_token[pos] = t; workgroup 0 also publishes offsets
-//                      and the (expert, first row) tile table of the grouped
-//                      GEMMs
+//                      and the tile table of the grouped GEMMs
 //   dispatch_small_kernel  both in one workgroup when a batch has at most 64
 //                      chunks
 //   dispatch_tiny_kernel   batches of at most 64 tokens, straight from idx:
@@ -80,13 +79,14 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int *__restrict__
 }
 
 // Exclusive scan of the counts (c = counts[threadIdx.x], 0 past N') into
-// s_off; `lead` also publishes offsets and the (expert, first row) tile table
-// of the grouped GEMMs.  Tiles are BM rows from each expert's first row,
+// s_off; `lead` also publishes offsets and the tile table of the grouped
+// GEMMs: per tile (expert, first dispatch row, rows of the expert from that
+// row on, 0), so that a kernel finds its tile with one load.  Tiles are BM rows from each expert's first row,
 // except that the last one may hold up to BM + slack rows: max(1, ceil((c -
 // slack) / BM)) tiles for an expert with c > 0 rows (slack 0: ceil(c / BM)).
 // 1024 threads, N' <= 1024; every thread calls it.  s_off is complete on return.
 __device__ __forceinline__ void block_offsets(int c, bool lead, int N, int BM, int slack, int *__restrict__ offsets,
-                                              int *__restrict__ tile_expert, int *__restrict__ tile_row0,
+                                              int4 *__restrict__ tile_info,
                                               int *__restrict__ n_mtiles, int *s_off, int *s_wsum)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -116,10 +116,8 @@ __device__ __forceinline__ void block_offsets(int c, bool lead, int N, int BM, i
         for (int w = 0; w < wave; ++w)
             tbefore += s_wsum[w];
         const int texcl = tbefore + tincl - nt;
-        for (int j = 0; j < nt; ++j) {
-            tile_expert[texcl + j] = tid;
-            tile_row0[texcl + j] = j * BM;
-        }
+        for (int j = 0; j < nt; ++j)
+            tile_info[texcl + j] = make_int4(tid, excl + j * BM, c - j * BM, 0);
         if (tid == 1023)
             *n_mtiles = texcl + nt;
     }
@@ -130,11 +128,11 @@ __device__ __forceinline__ void block_offsets(int c, bool lead, int N, int BM, i
 __device__ __forceinline__ void finalize_block(int c, bool lead, int64_t q0, int64_t qs, const int *__restrict__ idx,
                                                const int *__restrict__ rank, const int *__restrict__ chunk_base, int T,
                                                int K, int N, int chunk_tokens, int ld_chunks, int BM, int slack,
-                                               int *__restrict__ offsets, int *__restrict__ tile_expert,
-                                               int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
+                                               int *__restrict__ offsets, int4 *__restrict__ tile_info,
+                                               int *__restrict__ n_mtiles,
                                                int *__restrict__ pos, int *__restrict__ perm, int *s_off, int *s_wsum)
 {
-    block_offsets(c, lead, N, BM, slack, offsets, tile_expert, tile_row0, n_mtiles, s_off, s_wsum);
+    block_offsets(c, lead, N, BM, slack, offsets, tile_info, n_mtiles, s_off, s_wsum);
     const int64_t P = (int64_t)T * K;
     for (int64_t q = q0; q < P; q += qs) {
         const int t = (int)(q / K);
@@ -151,8 +149,8 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ 
                                                        const int *__restrict__ chunk_base,
                                                        const int *__restrict__ counts, int T, int K, int N,
                                                        int chunk_tokens, int ld_chunks, int BM, int slack,
-                                                       int *__restrict__ offsets, int *__restrict__ tile_expert,
-                                                       int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
+                                                       int *__restrict__ offsets, int4 *__restrict__ tile_info,
+                                                       int *__restrict__ n_mtiles,
                                                        int *__restrict__ pos, int *__restrict__ perm)
 {
     __shared__ int s_off[1024];
@@ -160,7 +158,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const int *__restrict__ 
     const int tid = threadIdx.x;
     const int c = (tid < N) ? counts[tid] : 0;
     finalize_block(c, blockIdx.x == 0, (int64_t)blockIdx.x * 1024 + tid, (int64_t)gridDim.x * 1024, idx, rank,
-                   chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, slack, offsets, tile_expert, tile_row0, n_mtiles,
+                   chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, slack, offsets, tile_info, n_mtiles,
                    pos, perm, s_off, s_wsum);
 }
 
@@ -174,7 +172,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restr
                                                              int T, int K, int N, int chunk_tokens, int ld_chunks,
                                                              int BM, int slack, int *__restrict__ chunk_base,
                                                              int *__restrict__ counts, int *__restrict__ offsets,
-                                                             int *__restrict__ tile_expert, int *__restrict__ tile_row0,
+                                                             int4 *__restrict__ tile_info,
                                                              int *__restrict__ n_mtiles, int *__restrict__ pos,
                                                              int *__restrict__ perm)
 {
@@ -209,7 +207,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restr
         counts[tid] = c;
     }
     finalize_block(c, true, tid, 1024, idx, rank, chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, slack, offsets,
-                   tile_expert, tile_row0, n_mtiles, pos, perm, s_off, s_wsum);
+                   tile_info, n_mtiles, pos, perm, s_off, s_wsum);
 }
 
 // Batches of at most 64 tokens (kTinyTokens), one workgroup of 1024 threads,
@@ -217,8 +215,8 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restr
 // masks are ORed together in LDS, and the rest reads LDS only.
 __global__ __launch_bounds__(1024) void dispatch_tiny_kernel(const int *__restrict__ idx, int T, int K, int N, int BM,
                                                             int slack, int *__restrict__ counts,
-                                                            int *__restrict__ offsets, int *__restrict__ tile_expert,
-                                                            int *__restrict__ tile_row0, int *__restrict__ n_mtiles,
+                                                            int *__restrict__ offsets, int4 *__restrict__ tile_info,
+                                                            int *__restrict__ n_mtiles,
                                                             int *__restrict__ pos, int *__restrict__ perm)
 {
     __shared__ unsigned long long s_mask[1024];
@@ -241,7 +239,7 @@ __global__ __launch_bounds__(1024) void dispatch_tiny_kernel(const int *__restri
     const int c = tid < N ? __popcll(s_mask[tid]) : 0;
     if (tid < N)
         counts[tid] = c;
-    block_offsets(c, true, N, BM, slack, offsets, tile_expert, tile_row0, n_mtiles, s_off, s_wsum);
+    block_offsets(c, true, N, BM, slack, offsets, tile_info, n_mtiles, s_off, s_wsum);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = e_q[j];

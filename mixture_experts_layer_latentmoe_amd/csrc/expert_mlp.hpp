@@ -47,7 +47,8 @@ struct MlpParams {
     const void *W2;    // per expert [m / 64][l][64]
     void *Y;           // [P, l] E
     int l, m, nb1;
-    const int *tile_expert, *tile_row0, *n_mtiles, *offsets;
+    const int4 *tile_info;
+    const int *n_mtiles, *offsets;
 };
 
 template <int CH2> __device__ __forceinline__ int swz2(int r) { return (r / (16 / CH2)) & (CH2 - 1); }
@@ -304,11 +305,10 @@ __global__ __launch_bounds__(512, 1) void expert_mlp_kernel(const MlpParams p)
     const int t = xcd_logical_tile(blockIdx.x, *p.n_mtiles);
     if (t < 0)
         return;
-    const int expert = p.tile_expert[t];
-    const int start = p.offsets[expert];
-    const int r0 = p.tile_row0[t];
-    const int rows_valid = min(BM, p.offsets[expert + 1] - start - r0);
-    const int64_t row_base = (int64_t)start + r0;
+    const int4 rec = p.tile_info[t];
+    const int expert = rec.x;
+    const int rows_valid = min(BM, rec.z);
+    const int64_t row_base = rec.y;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

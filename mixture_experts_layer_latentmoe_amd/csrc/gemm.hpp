@@ -75,8 +75,7 @@ struct GemmParams {
                         // zero between launches (fewrow_split_kernel)
     // grouped mode
     const int *gather;       // dispatch row -> A row, or nullptr (A rows = dispatch rows)
-    const int *tile_expert;  // [tiles]
-    const int *tile_row0;    // [tiles] first row of the tile inside its expert
+    const int4 *tile_info;   // [tiles] expert, first dispatch row, rows of the expert from it on, 0
     const int *n_mtiles;     // device scalar: number of valid M tiles
     const int *offsets;      // [N'+1] first dispatch row of each expert
     const float *scaleB;     // grouped, E4M3 B: [N'][N] scale of each expert's output column
@@ -168,12 +167,10 @@ __device__ __forceinline__ void tile_coords(const GemmParams &p, int t, int ntn,
     if constexpr (GROUPED) {
         tm = t / ntn;
         tn = t - tm * ntn;
-        ti.expert = p.tile_expert[tm];
-        const int r0 = p.tile_row0[tm];
-        const int start = p.offsets[ti.expert];
-        const int cnt = p.offsets[ti.expert + 1] - start;
-        ti.rows_valid = (cnt - r0 <= BM + XR) ? cnt - r0 : BM;
-        ti.row_base = (int64_t)start + r0;
+        const int4 rec = p.tile_info[tm];
+        ti.expert = rec.x;
+        ti.rows_valid = (rec.z <= BM + XR) ? rec.z : BM;
+        ti.row_base = rec.y;
     } else {
         const int ntm = (p.M + BM - 1) / BM;
         const int gm = p.group_m;
@@ -195,7 +192,18 @@ template <int BM, int BN, bool GROUPED, int XR = 0>
 __device__ __forceinline__ bool locate_tile(const GemmParams &p, TileInfo &ti)
 {
     const int ntn = (p.N + BN - 1) / BN;
-    if constexpr (GROUPED) {
+    if constexpr (GROUPED && BM == 32) {
+        // decode-sized tile tables: tiles in grid order (tiles of one expert
+        // share only a few A rows, nothing to keep in one L2), so that the
+        // tile record and the tile count load together; the record of a
+        // workgroup past the table is read (the table has room) but not used
+        const int t = blockIdx.x;
+        const int nmt = *p.n_mtiles;
+        tile_coords<BM, BN, true, XR>(p, t, ntn, ti);
+        __builtin_amdgcn_sched_barrier(0);  // both loads go out before either is waited for
+        if (t >= nmt * ntn || ti.expert < 0)  // (testing the record keeps its load above the branch)
+            return false;
+    } else if constexpr (GROUPED) {
         const int t = xcd_logical_tile(blockIdx.x, *p.n_mtiles * ntn);
         if (t < 0)
             return false;

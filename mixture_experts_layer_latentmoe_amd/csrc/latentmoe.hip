@@ -130,7 +130,8 @@ struct Workspace {
     int *idx, *rank, *pos, *perm;
     float *gate, *logits;
     int *chunk_counts, *chunk_base, *counts, *offsets;
-    int *tile_expert, *tile_row0, *n_mtiles;
+    int4 *tile_info;
+    int *n_mtiles;
     void *zh, *H, *Yp;
     float *partial;
     int64_t partial_cap;  // floats at `partial`
@@ -278,8 +279,8 @@ int64_t split_partial_floats(const Plan &p, int64_t T)
 }
 
 struct Layout {
-    int64_t off_cnt, off_idx, off_gate, off_rank, off_pos, off_perm, off_cc, off_cb, off_counts, off_offsets, off_te,
-        off_tr, off_nmt, off_logits, off_zh, off_H, off_Yp, off_part, total;
+    int64_t off_cnt, off_idx, off_gate, off_rank, off_pos, off_perm, off_cc, off_cb, off_counts, off_offsets, off_ti,
+        off_nmt, off_logits, off_zh, off_H, off_Yp, off_part, total;
     int64_t ld_chunks, partial_floats;
 };
 
@@ -309,8 +310,7 @@ Layout ws_layout(const Plan &p, int64_t T, int64_t partial_floats)
     L.off_cb = take(4 * L.ld_chunks * p.N);
     L.off_counts = take(4 * p.N);
     L.off_offsets = take(4 * (p.N + 1));
-    L.off_te = take(4 * mt);
-    L.off_tr = take(4 * mt);
+    L.off_ti = take(16 * (mt + 8));  // a decode tile grid reads up to 8 entries past the table
     L.off_nmt = take(4);
     L.off_logits = take(4 * T * p.N);
     L.off_zh = take((int64_t)p.esize * T * p.ld_zh);
@@ -334,8 +334,7 @@ Workspace carve_ws(void *base, const Layout &L)
     w.chunk_base = reinterpret_cast<int *>(b + L.off_cb);
     w.counts = reinterpret_cast<int *>(b + L.off_counts);
     w.offsets = reinterpret_cast<int *>(b + L.off_offsets);
-    w.tile_expert = reinterpret_cast<int *>(b + L.off_te);
-    w.tile_row0 = reinterpret_cast<int *>(b + L.off_tr);
+    w.tile_info = reinterpret_cast<int4 *>(b + L.off_ti);
     w.n_mtiles = reinterpret_cast<int *>(b + L.off_nmt);
     w.logits = reinterpret_cast<float *>(b + L.off_logits);
     w.zh = b + L.off_zh;
@@ -832,14 +831,14 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     if (T <= kTinyTokens) {
         tm.begin(ST_FINALIZE);
         dispatch_tiny_kernel<<<dim3(1), dim3(1024), 0, s>>>(w.idx, T, K, N, gbm, slack, w.counts, w.offsets,
-                                                            w.tile_expert, w.tile_row0, w.n_mtiles, w.pos, w.perm);
+                                                            w.tile_info, w.n_mtiles, w.pos, w.perm);
         hip_check(hipGetLastError());
         tm.end(ST_FINALIZE);
     } else if (nchunks <= 64) {
         tm.begin(ST_FINALIZE);
         dispatch_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(
             w.chunk_counts, nchunks, w.idx, w.rank, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm, slack, w.chunk_base,
-            w.counts, w.offsets, w.tile_expert, w.tile_row0, w.n_mtiles, w.pos, w.perm);
+            w.counts, w.offsets, w.tile_info, w.n_mtiles, w.pos, w.perm);
         hip_check(hipGetLastError());
         tm.end(ST_FINALIZE);
     } else {
@@ -853,7 +852,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
         const int64_t blocks = std::min<int64_t>((P + 1023) / 1024, 256);
         finalize_kernel<<<dim3((unsigned)blocks), dim3(1024), 0, s>>>(
             w.idx, w.rank, w.chunk_base, w.counts, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm, slack,
-            w.offsets, w.tile_expert, w.tile_row0, w.n_mtiles, w.pos, w.perm);
+            w.offsets, w.tile_info, w.n_mtiles, w.pos, w.perm);
         hip_check(hipGetLastError());
         tm.end(ST_FINALIZE);
     }
@@ -874,8 +873,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
     g1.relu2_from = p.glu ? kNoColumn : 0;
     g1.glu_from = p.glu ? 0 : kNoColumn;
     g1.gather = w.perm;
-    g1.tile_expert = w.tile_expert;
-    g1.tile_row0 = w.tile_row0;
+    g1.tile_info = w.tile_info;
     g1.n_mtiles = w.n_mtiles;
     g1.offsets = w.offsets;
     g1.scaleB = h->s1;
@@ -899,8 +897,7 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
         mp.l = (int)p.l;
         mp.m = (int)p.m;
         mp.nb1 = (int)p.nb1;
-        mp.tile_expert = w.tile_expert;
-        mp.tile_row0 = w.tile_row0;
+        mp.tile_info = w.tile_info;
         mp.n_mtiles = w.n_mtiles;
         mp.offsets = w.offsets;
         tm.begin(ST_MLP);
@@ -1402,8 +1399,7 @@ void backward_impl(latentmoe_handle *h, const void *x, const void *dy, int T, hi
     gb.ld_pre = p.nb1;
     gb.N = (int)p.m;
     gb.K = (int)p.l;
-    gb.tile_expert = h->wk.tile_expert;
-    gb.tile_row0 = h->wk.tile_row0;
+    gb.tile_info = h->wk.tile_info;
     gb.n_mtiles = h->wk.n_mtiles;
     gb.offsets = h->wk.offsets;
     if (p.glu)
