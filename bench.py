@@ -137,7 +137,8 @@ STAGE_OF_TAG = {0: "gemm_x_router_down_shared1", 1: "grouped_gemm1_relu2", 2: "g
                 4: "backward_dgrad", 5: "backward_wgrad", 6: "backward_wgrad_experts", 7: "backward_x_recompute",
                 8: "backward_gemm1_recompute"}
 # kernel template -> position of the stage tag among its integer arguments
-TAG_POS = {"gemm_kernel": 7, "skinny_gemm_kernel": 3, "fewrow_split_kernel": 3}
+# (-1: the last one)
+TAG_POS = {"gemm_kernel": 7, "skinny_gemm_kernel": -1, "fewrow_split_kernel": -1}
 FIXED_STAGE = {"expert_mlp_kernel": "expert_mlp", "router_select_kernel": "router_select",
                "dispatch_tiny_kernel": "dispatch_finalize", "dispatch_small_kernel": "dispatch_finalize",
                "finalize_kernel": "dispatch_finalize", "chunk_scan_kernel": "dispatch_scan",
@@ -154,13 +155,15 @@ def stage_of_kernel(name: str) -> str:
             return st
     for k, pos in TAG_POS.items():
         if re.search(r"(^|[^a-z_])" + k, name):
-            if "<" in name:  # demangled: integer arguments after the element type
-                args = name[name.index("<") + 1:name.rindex(">")].split(",")[1:]
-                vals = [a.strip() for a in args]
-                ints = [int(v == "true") if v in ("true", "false") else int(v) for v in vals]
+            if "<" in name:  # demangled: the integer (and bool) arguments in order
+                vals = [a.strip() for a in name[name.index("<") + 1:name.rindex(">")].split(",")]
+                ints = [int(v == "true") if v in ("true", "false") else int(v) for v in vals
+                        if v in ("true", "false") or v.lstrip("-").isdigit()]
             else:            # mangled: Li<n>E / Lb<n>E in order
                 ints = [int(v) for v in re.findall(r"L[ib](\d+)E", name)]
-            return STAGE_OF_TAG.get(ints[pos], f"{k}[{ints[pos]}]") if len(ints) > pos else k
+            if not ints or len(ints) <= pos:
+                return k
+            return STAGE_OF_TAG.get(ints[pos], f"{k}[{ints[pos]}]")
     if "elementwise" in name or "vectorized" in name:
         return "copy calibration (torch add)"
     return name.split("(")[0][:60]
