@@ -207,9 +207,9 @@ def summarize_pmc(d):
     """Per stage: the average per dispatch of every counter collected, and
     derived figures where their inputs are there: MFMA busy share of the
     shader cycles (SQ_VALU_MFMA_BUSY_CYCLES over 4 SIMDs x 256 CUs of
-    GRBM_GUI_ACTIVE / 8 XCDs), the vector L1's pending-miss stall share
-    (TCP_PENDING_STALL_CYCLES over TCP_TOTAL_CACHE_ACCESSES' busy cycles is not
-    defined: reported raw), the L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))
+    GRBM_GUI_ACTIVE / 8 XCDs), the share of cycles the vector L1s wait on
+    pending misses (TCP_PENDING_STALL_CYCLES summed over the 256 L1s, over 256
+    x GRBM_GUI_ACTIVE / 8), the L2 hit rate (TCC_HIT / (TCC_HIT + TCC_MISS))
     and the effective shader clock (GRBM_GUI_ACTIVE / 8 per kernel time)."""
     per, dur = _counters(d)
     lines = []
@@ -224,6 +224,8 @@ def summarize_pmc(d):
             der.append(f"shader_clock_GHz={c['GRBM_GUI_ACTIVE'] / 8 / (avg_us * 1e3):.3f}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in c and "GRBM_GUI_ACTIVE" in c:
             der.append(f"mfma_busy={c['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * 256 * c['GRBM_GUI_ACTIVE'] / 8):.3f}")
+        if "TCP_PENDING_STALL_CYCLES_sum" in c and "GRBM_GUI_ACTIVE" in c:
+            der.append(f"l1_pending_stall={c['TCP_PENDING_STALL_CYCLES_sum'] / (256 * c['GRBM_GUI_ACTIVE'] / 8):.3f}")
         hit, miss = c.get("TCC_HIT_sum", c.get("TCC_HIT")), c.get("TCC_MISS_sum", c.get("TCC_MISS"))
         if hit is not None and miss is not None and hit + miss > 0:
             der.append(f"l2_hit_rate={hit / (hit + miss):.3f}")
