@@ -94,7 +94,10 @@ __device__ __forceinline__ void select_token_vals(const float (&val)[NPL], int N
         const int e = lane + 64 * j;
         key[j] = (e < N) ? ordered_key(val[j]) : 0u;
     }
-    // 1. the K'-th largest key: largest th with #{key >= th} >= K'
+    // 1. the K'-th largest key: largest th with #{key >= th} >= K'.  Once a
+    // candidate has exactly K' keys at or above it, those keys are the
+    // selection (every key equal to th is among them, so step 1's tie rule
+    // takes all of them) and the lower bits need not be resolved.
     unsigned th = 0u;
     for (int b = 31; b >= 0; --b) {
         const unsigned cand = th | (1u << b);
@@ -102,8 +105,11 @@ __device__ __forceinline__ void select_token_vals(const float (&val)[NPL], int N
 #pragma unroll
         for (int j = 0; j < NPL; ++j)
             cnt += wave_count(key[j] >= cand);
-        if (cnt >= K)
+        if (cnt >= K) {
             th = cand;
+            if (cnt == K)
+                break;
+        }
     }
     int need = K;
 #pragma unroll
