@@ -84,10 +84,13 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int *__restrict__
 // row on, 0), so that a kernel finds its tile with one load.  Tiles are BM rows from each expert's first row,
 // except that the last one may hold up to BM + slack rows: max(1, ceil((c -
 // slack) / BM)) tiles for an expert with c > 0 rows (slack 0: ceil(c / BM)).
-// 1024 threads, N' <= 1024; every thread calls it.  s_off is complete on return.
+// 1024 threads, N' <= 1024; every thread calls it.  s_off is complete on return;
+// s_toff, if given (lead only), receives each expert's first tile, complete
+// after the next barrier.
 __device__ __forceinline__ void block_offsets(int c, bool lead, int N, int BM, int slack, int *__restrict__ offsets,
                                               int4 *__restrict__ tile_info,
-                                              int *__restrict__ n_mtiles, int *s_off, int *s_wsum)
+                                              int *__restrict__ n_mtiles, int *s_off, int *s_wsum,
+                                              int *s_toff = nullptr)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int incl = wave_incl_scan(c, lane);
@@ -116,6 +119,8 @@ __device__ __forceinline__ void block_offsets(int c, bool lead, int N, int BM, i
         for (int w = 0; w < wave; ++w)
             tbefore += s_wsum[w];
         const int texcl = tbefore + tincl - nt;
+        if (s_toff)
+            s_toff[tid] = texcl;
         for (int j = 0; j < nt; ++j)
             tile_info[texcl + j] = make_int4(tid, excl + j * BM, c - j * BM, 0);
         if (tid == 1023)
@@ -212,15 +217,21 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restr
 
 // Batches of at most 64 tokens (kTinyTokens), one workgroup of 1024 threads,
 // N' <= 1024, T K' <= 4096: every pair's expert is loaded up front, the token
-// masks are ORed together in LDS, and the rest reads LDS only.
+// masks are ORed together in LDS, and the rest reads LDS only.  With 32-row
+// tiles (BM = 32, so no slack) and a row table it also writes the token of
+// each dispatch row at [tile][row in tile] (rows past an expert's last row
+// stay unwritten), so that a grouped GEMM workgroup loads its A rows together
+// with its tile record instead of through perm after it.
 __global__ __launch_bounds__(1024) void dispatch_tiny_kernel(const int *__restrict__ idx, int T, int K, int N, int BM,
                                                             int slack, int *__restrict__ counts,
                                                             int *__restrict__ offsets, int4 *__restrict__ tile_info,
                                                             int *__restrict__ n_mtiles,
-                                                            int *__restrict__ pos, int *__restrict__ perm)
+                                                            int *__restrict__ pos, int *__restrict__ perm,
+                                                            int *__restrict__ tile_rows)
 {
     __shared__ unsigned long long s_mask[1024];
     __shared__ int s_off[1024];
+    __shared__ int s_toff[1024];
     __shared__ int s_wsum[16];
     const int tid = threadIdx.x, P = T * K;
     int e_q[4];
@@ -239,16 +250,22 @@ __global__ __launch_bounds__(1024) void dispatch_tiny_kernel(const int *__restri
     const int c = tid < N ? __popcll(s_mask[tid]) : 0;
     if (tid < N)
         counts[tid] = c;
-    block_offsets(c, true, N, BM, slack, offsets, tile_info, n_mtiles, s_off, s_wsum);
+    const bool rows = BM == 32 && slack == 0 && tile_rows;
+    block_offsets(c, true, N, BM, slack, offsets, tile_info, n_mtiles, s_off, s_wsum, rows ? s_toff : nullptr);
+    if (rows)
+        __syncthreads();  // s_toff
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int e = e_q[j];
         if (e < 0)
             continue;
         const int q = tid + 1024 * j, t = q / K;
-        const int p = s_off[e] + __popcll(s_mask[e] & ((1ull << t) - 1ull));
+        const int r = __popcll(s_mask[e] & ((1ull << t) - 1ull));  // row within the expert
+        const int p = s_off[e] + r;
         pos[q] = p;
         perm[p] = t;
+        if (rows)
+            tile_rows[(s_toff[e] + (r >> 5)) * 32 + (r & 31)] = t;
     }
 }
 

@@ -76,6 +76,8 @@ struct GemmParams {
     // grouped mode
     const int *gather;       // dispatch row -> A row, or nullptr (A rows = dispatch rows)
     const int4 *tile_info;   // [tiles] expert, first dispatch row, rows of the expert from it on, 0
+    const int *tile_rows;    // 32-row tiles, nullable: [tiles][32] A row (after the gather) of each tile
+                             // row; undefined past the expert's rows
     const int *n_mtiles;     // device scalar: number of valid M tiles
     const int *offsets;      // [N'+1] first dispatch row of each expert
     const float *scaleB;     // grouped, E4M3 B: [N'][N] scale of each expert's output column
@@ -685,6 +687,20 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     __shared__ uint4 sA0[BMA * 8], sA1[BMA * 8], sA2[NS > 2 ? BMA * 8 : 1], sA3[NS > 3 ? BMA * 8 : 1];
     __shared__ uint4 sB0[BN * CHB], sB1[BN * CHB], sB2[NS > 2 ? BN * CHB : 1], sB3[NS > 3 ? BN * CHB : 1];
 
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // decode-sized tile tables with a row table: this thread's A rows load
+    // together with the tile record (both are indexed by the grid position),
+    // instead of after it through the gather
+    int pre_row[NIA];
+    if constexpr (GROUPED && BM == 32) {
+        if (p.tile_rows) {
+            const int tm = blockIdx.x / ((p.N + BN - 1) / BN);
+#pragma unroll
+            for (int i = 0; i < NIA; ++i)
+                pre_row[i] = p.tile_rows[tm * 32 + (((i * NW + wave) * 64 + lane) >> 3)];
+        }
+    }
     TileInfo ti;
     if (!locate_tile<BM, BN, GROUPED, XR>(p, ti))
         return;
@@ -692,8 +708,6 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     const int64_t row_base = ti.row_base;
     const int n0 = ti.n0;
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave - (wave / WN) * WN;
 
     // Buffer descriptors and this thread's source offsets (fixed for the K loop).
@@ -709,7 +723,9 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         a_off[i] = kOOB;
         if (r < rows_valid) {
             int64_t arow = row_base + r;
-            if (GROUPED && p.gather)
+            if (GROUPED && BM == 32 && p.tile_rows)
+                arow = pre_row[i];
+            else if (GROUPED && p.gather)
                 arow = p.gather[arow];
             a_off[i] = (unsigned)(arow * p.lda * (int64_t)sizeof(E)) + c * 16;
         }

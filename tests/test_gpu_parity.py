@@ -56,6 +56,18 @@ def test_zipf_bias_ragged_tokens():
     _full_check(make_workload(get_config("zipf_skew"), T=231))
 
 
+@pytest.mark.parametrize("T", [64, 40])
+def test_zipf_decode_multi_tile_experts(T):
+    """Decode batches whose biased router gives several experts up to T rows:
+    two 32-row tiles per such expert (the second ragged at T = 40 and for the
+    experts with 63 rows), through the per-tile A-row table of the first
+    grouped GEMM."""
+    wl = make_workload(get_config("zipf_skew"), T=T)
+    counts = np.bincount(G.oracle_routing(wl).idx.ravel(), minlength=wl.shape.n_experts)
+    assert counts.max() > 32
+    _full_check(wl)
+
+
 @pytest.mark.parametrize("name,n_sample", [("readme_acc", None), ("decode_eff", None),
                                            ("wide_prefill", 1024), ("zipf_skew", 1024)])
 def test_full_size(name, n_sample):
