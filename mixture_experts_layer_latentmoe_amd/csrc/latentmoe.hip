@@ -608,7 +608,12 @@ void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_
 // kGroupBMBig); otherwise 128x256 tiles (8 waves, three LDS stages, one
 // workgroup per CU) when N is a multiple of 256, else 128x128 (two
 // workgroups per CU); when experts average few rows (decode), 32x128 tiles
-// with four LDS stages so that more weight bytes are in flight.
+// with four LDS stages so that more weight bytes are in flight, and for
+// grouped GEMM 2 (N = l columns) 32x64 tiles of two waves, also four stages:
+// 48 KiB of LDS, three workgroups per CU, twice the tiles on 1.5x the slots,
+// so a shorter ragged last round (measured at decode_eff: 56.5-57.1 us
+// against 57.9-58.8 us with 32x128; grouped GEMM 1 is slower with them,
+// 53.2-53.9 -> 55.6-55.9 us).
 // fp8: the weights (B) are E4M3 bytes with column scales in gp.scaleB; for few
 // rows, 32x64 tiles of two waves and two stages (small LDS footprint, many
 // workgroups per CU) stream the half-size weights fastest.
@@ -635,7 +640,9 @@ void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hi
     }
     if ((bm != kGroupBMSmall && bm != kGroupBM) || slack != 0)  // a tile table these kernels cannot walk
         throw HipError{hipErrorInvalidValue};
-    if (bm == kGroupBMSmall)
+    if (bm == kGroupBMSmall && TAG == kTagG2)
+        launch_grouped<E, kGroupBMSmall, 64, 1, 2, 4, TAG, false, ACT>(gp, max_mtiles, s);
+    else if (bm == kGroupBMSmall)
         launch_grouped<E, kGroupBMSmall, 128, 1, 4, 4, TAG, false, ACT>(gp, max_mtiles, s);
     else if (sizeof(E) == 2 && gp.N % 256 == 0)
         launch_grouped<E, kGroupBM, 256, 2, 4, 3, TAG, false, ACT>(gp, max_mtiles, s);
