@@ -138,13 +138,18 @@ STAGE_OF_TAG = {0: "gemm_x_router_down_shared1", 1: "grouped_gemm1_relu2", 2: "g
                 8: "backward_gemm1_recompute"}
 # kernel template -> position of the stage tag among its integer arguments
 # (-1: the last one)
-TAG_POS = {"gemm_kernel": 7, "skinny_gemm_kernel": -1, "fewrow_split_kernel": -1}
+TAG_POS = {"gemm_kernel": 7, "skinny_gemm_kernel": -1, "fewrow_split_kernel": -1, "gemm_tn_kernel": 0}
 FIXED_STAGE = {"expert_mlp_kernel": "expert_mlp", "router_select_kernel": "router_select",
                "dispatch_tiny_kernel": "dispatch_finalize", "dispatch_small_kernel": "dispatch_finalize",
                "finalize_kernel": "dispatch_finalize", "chunk_scan_kernel": "dispatch_scan",
                "combine_kernel": "combine", "splitk_reduce_kernel": "splitk_reduce",
                "transpose_kernel": "repack_transpose (create only)",
-               "fragmajor_kernel": "repack_fragmajor (create only)"}
+               "fragmajor_kernel": "repack_fragmajor (create only)",
+               # the backward's element-wise and re-layout kernels
+               "xpass_act_kernel": "backward_x_recompute_act", "gather_sum8_kernel": "backward_gather_sum",
+               "shared_act_grad_kernel": "backward_shared_act_grad",
+               "gate_combine_grad_kernel": "backward_gate_combine_grad", "retile_kernel": "backward_retile",
+               "split_cols_kernel": "backward_split_cols", "gather_rows_kernel": "backward_gather_rows"}
 
 
 def stage_of_kernel(name: str) -> str:
@@ -165,7 +170,7 @@ def stage_of_kernel(name: str) -> str:
                 return k
             return STAGE_OF_TAG.get(ints[pos], f"{k}[{ints[pos]}]")
     if "elementwise" in name or "vectorized" in name:
-        return "copy calibration (torch add)"
+        return "torch elementwise (the copy calibration in traffic runs)"
     return name.split("(")[0][:60]
 
 
@@ -240,7 +245,7 @@ def summarize_traffic(d_fetch, d_write):
     (a torch add of 64 Mi fp32: 256 MiB read and 256 MiB written)."""
     f, _ = _counters(d_fetch)
     w, _ = _counters(d_write)
-    cal = "copy calibration (torch add)"
+    cal = "torch elementwise (the copy calibration in traffic runs)"
     fk = f[cal]["FETCH_SIZE"]
     wk = w[cal]["WRITE_SIZE"]
     f_cal, w_cal = sum(fk.values()) / len(fk), sum(wk.values()) / len(wk)

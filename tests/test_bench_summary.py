@@ -28,6 +28,10 @@ def test_stage_of_kernel_mangled_and_demangled():
         "_ZN4lmoe17expert_mlp_kernelILi128ELi512ELi128ELi32ELi4ELi4ELi2ELi2ELi4ELb0ELi8EEEvNS_9MlpParamsE":
             "expert_mlp",
         "_ZN4lmoe14combine_kernelIDF16bEEvPKT_PKiPKfiiiPS1_l": "combine",
+        "_ZN4lmoe14gemm_tn_kernelILi6EEEvNS_10GemmParamsE.kd": "backward_wgrad_experts",
+        "void lmoe::gemm_tn_kernel<5>(lmoe::GemmParams)": "backward_wgrad",
+        "_ZN4lmoe13retile_kernelIDF16bLi64EEEvPKT_iiPS1_.kd": "backward_retile",
+        "_ZN12_GLOBAL__N_118gather_rows_kernelIDF16bEEvPKT_lPKiliPS1_": "backward_gather_rows",
     }
     for name, stage in cases.items():
         assert bench.stage_of_kernel(name) == stage, name
