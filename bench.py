@@ -272,13 +272,18 @@ def cpu_baseline(wl, target_s=12.0):
     from oracle import oracle
     T = wl.shape.T
     rng = np.random.default_rng(123)
-    n = min(T, 8)
-    toks = np.sort(rng.choice(T, size=n, replace=False))
-    t0 = time.perf_counter()
-    oracle.forward(wl, tokens=toks, want=("y",))
-    dt = time.perf_counter() - t0
-    per_tok = dt / n
-    n2 = int(min(T, max(n, target_s / max(per_tok, 1e-9))))
+    # two pilots that keep every thread busy (a few tokens per thread): a call
+    # costs a fixed part (the weights' conversion) plus a part per token
+    n = min(T, max(8, 4 * oracle.max_threads()))
+    times = []
+    for k in (n, 2 * n):
+        toks = np.sort(rng.choice(T, size=min(T, k), replace=False))
+        t0 = time.perf_counter()
+        oracle.forward(wl, tokens=toks, want=("y",))
+        times.append(time.perf_counter() - t0)
+    per_tok = max((times[1] - times[0]) / n, times[1] / (2 * n) / 4, 1e-9)
+    fixed = max(times[0] - per_tok * n, 0.0)
+    n2 = int(min(T, max(n, (target_s - fixed) / per_tok)))
     toks = np.sort(rng.choice(T, size=n2, replace=False))
     t0 = time.perf_counter()
     oracle.forward(wl, tokens=toks, want=("y",))
