@@ -392,7 +392,11 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
     constexpr int ES = (int)sizeof(E);
     constexpr int CPR = WTN * ES / 16;  // 16-byte chunks per staged row
     constexpr int RPI = 64 / CPR;       // staged rows per store instruction
-    static_assert(CPR >= 1 && CPR <= 64 && (CPR & (CPR - 1)) == 0, "staged row");
+    // chunk c of staged row r sits at c ^ (r % CPR), or, for a CPR that is not
+    // a power of two (160-column wave tiles), at (c + r) % CPR
+    constexpr bool P2 = (CPR & (CPR - 1)) == 0;
+    static_assert(CPR >= 1 && CPR <= 64, "staged row");
+    auto spos = [](int r, int c) { return P2 ? (c ^ (r & (CPR - 1))) : (c + r) % CPR; };
     const int lr = lane & 31, lc = lane >> 5;
     const int cbase = n0 + wn * WTN - p.c_split;  // first C column of this wave
     const int rows_here = rows_valid - wm * WTM;
@@ -423,15 +427,19 @@ __device__ __forceinline__ void store_tile_staged(const GemmParams &p, const f32
                         v[r] = t * t;
                     }
                 const int byte = cc * ES, ch = byte / 16;
-                store4(reinterpret_cast<E *>(sb + (lr * CPR + (ch ^ (lr & (CPR - 1)))) * 16 + byte % 16), v[0], v[1],
-                       v[2], v[3]);
+                store4(reinterpret_cast<E *>(sb + (lr * CPR + spos(lr, ch)) * 16 + byte % 16), v[0], v[1], v[2],
+                       v[3]);
             }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int r0 = 0; r0 < 32; r0 += RPI) {
             const int rl = r0 + lane / CPR;
-            const uint4 v = stg[rl * CPR + (cw ^ (rl & (CPR - 1)))];
+            // P2: the 64 lanes cover RPI whole rows and 32 % RPI == 0; otherwise
+            // the lanes past RPI rows, and rows past 32, have nothing to store
+            if (!P2 && (lane >= RPI * CPR || rl >= 32))
+                continue;
+            const uint4 v = stg[rl * CPR + spos(rl, cw)];
             if (col_ok && i * 32 + rl < rows_here)
                 store16_stream(C, ((row_base + wm * WTM + i * 32 + rl) * p.ldc + cbase + cw * (16 / ES)) * ES, v);
         }
@@ -877,9 +885,13 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         wait_vm_lgkm0<0>();
         __builtin_amdgcn_s_barrier();
         uint4 *stg = (IN_A ? (wave < PER_ARR ? sA0 : sA1) : (wave < PER_ARR ? sB0 : sB1)) + (wave % PER_ARR) * WAVE_U;
-        if (n0 >= p.glu_from)
-            store_tile_staged_glu<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg, cs);
-        else
+        constexpr int CPR = WAVE_U / 32;  // 16-byte chunks per staged row
+        if (n0 >= p.glu_from) {
+            if constexpr ((CPR & (CPR - 1)) == 0)
+                store_tile_staged_glu<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg, cs);
+            else  // the gated staging needs power-of-two rows
+                store_tile_direct<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, cs);
+        } else
             store_tile_staged<E, TM, TN, WTM, WTN>(p, acc, c_row_base, rows_valid, n0, wm, wn, lane, stg, cs);
         if constexpr (XM > 0) {
             // the extra rows: XR x 32 outputs per wave, straight from the registers

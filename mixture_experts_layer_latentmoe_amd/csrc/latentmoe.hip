@@ -605,7 +605,10 @@ void launch_splitk(GemmParams gp, float *partial, int64_t cap_floats, hipStream_
 
 // Grouped GEMMs: the forward of a bf16 layer with bf16 expert banks takes
 // 256x256 tiles (8 waves, two LDS stages) on a 256-row tile table (bm =
-// kGroupBMBig); otherwise 128x256 tiles (8 waves, three LDS stages, one
+// kGroupBMBig) -- 256x320 for grouped GEMM 2 when N = l is a multiple of 320
+// but not of 256 and the table has no extra rows (l = 640: two tiles per row
+// block instead of three with the third half empty; measured at zipf_skew
+// 252-256 -> 234-236 us); otherwise 128x256 tiles (8 waves, three LDS stages, one
 // workgroup per CU) when N is a multiple of 256, else 128x128 (two
 // workgroups per CU); when experts average few rows (decode), 32x128 tiles
 // with four LDS stages so that more weight bytes are in flight, and for
@@ -622,7 +625,9 @@ void grouped_gemm(const GemmParams &gp, int64_t max_mtiles, int bm, bool fp8, hi
 {
     if constexpr (sizeof(E) == 2 && ACT == ACT_NONE) {
         if (bm == kGroupBMBig && !fp8) {
-            if (slack == kGroupSlack)
+            if (TAG == kTagG2 && slack == 0 && gp.N % 320 == 0 && gp.N % 256 != 0)
+                launch_grouped<E, kGroupBMBig, 320, 4, 2, 2, TAG, false>(gp, max_mtiles, s);
+            else if (slack == kGroupSlack)
                 launch_grouped<E, kGroupBMBig, 256, 4, 2, 2, TAG, false, ACT_NONE, kGroupSlack>(gp, max_mtiles, s);
             else if (slack == 0)
                 launch_grouped<E, kGroupBMBig, 256, 4, 2, 2, TAG, false>(gp, max_mtiles, s);

@@ -138,6 +138,29 @@ def test_expert_rows_at_tile_boundaries(T):
     G.check_stages(out, wl, ref, toks, np.ones(T, dtype=bool))
 
 
+@pytest.mark.parametrize("zero_router,T", [(True, 1300), (False, 2048)])
+def test_grouped_gemm2_320_column_tiles(zero_router, T):
+    """l = 640 with more than 320 rows per expert on average: the 256-row tile
+    table without extra rows, where grouped GEMM 2 (N = l) takes 256x320
+    tiles, two per row block instead of three 256-column ones.  A zero
+    router gives experts 0..3 exactly 1300 rows (5 full tiles and one of 20
+    rows); a random one about 512 rows each.  Every token, stage by stage."""
+    sh = shape(T=T, d=1280, l=640, m=192, n_experts=16, top_k=4, n_shared=1, m_shared=128, dtype="bf16")
+    arr = random_arrays(sh, np.random.default_rng(T))
+    if zero_router:
+        arr["w_router"] = np.zeros_like(arr["w_router"])
+    wl = workload_from_arrays(sh, arr)
+    if not zero_router:
+        out = _full_check(wl)
+        assert out["counts"].min() > 320
+        return
+    out = G.run_gpu(wl)
+    assert np.array_equal(out["counts"], np.array([T] * 4 + [0] * 12, dtype=out["counts"].dtype))
+    toks = np.arange(T)
+    ref = oracle.forward(wl, tokens=toks, want=("logits", "idx", "gate", "z", "h", "o", "u", "hs", "y"))
+    G.check_stages(out, wl, ref, toks, np.ones(T, dtype=bool))
+
+
 def test_expert_rows_straddle_tile_height():
     """2048 tokens over 16 experts with K' = 2: about 256 rows per expert,
     some just under and some just over one 256-row tile."""
