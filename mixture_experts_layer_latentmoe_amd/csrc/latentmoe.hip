@@ -567,9 +567,20 @@ void dense_gemm(const GemmParams &gp, float *partial, int64_t cap_floats, int *c
         return;
     }
     const int64_t wide = ((gp.M + 127) / 128) * ((gp.N + 255) / 256);
-    if (big >= 192)
+    if (big >= 192) {
+        // one 256x256 or 256x320 workgroup per CU: 256x320 when its rounds of
+        // 256 tiles times its width come out smaller (zipf_skew's x-pass and
+        // up-projection: 3 rounds of 256 columns -> 2 of 320)
+        const int64_t ntm = (gp.M + 255) / 256;
+        const int64_t r256 = (ntm * ((gp.N + 255) / 256) + 255) / 256, r320 = (ntm * ((gp.N + 319) / 320) + 255) / 256;
+        if constexpr (sizeof(E) == 2) {
+            if (r320 * 320 < r256 * 256) {
+                launch_dense<E, 256, 320, 4, 2, 2, TAG>(gp, s);
+                return;
+            }
+        }
         launch_dense<E, 256, 256, 4, 2, 2, TAG>(gp, s);
-    else if (sizeof(E) == 2 && wide >= 256)
+    } else if (sizeof(E) == 2 && wide >= 256)
         launch_dense<E, 128, 256, 2, 4, 3, TAG>(gp, s);
     else if (mid >= 256 || gp.M > kSplitKMaxRows)
         launch_dense<E, 128, 128, 2, 2, 2, TAG>(gp, s);
