@@ -125,6 +125,7 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned o
 }
 
 constexpr unsigned kOOB = 0x80000000u;  // offset that is always out of range
+constexpr int kLoadNonTemporal = 2;     // cache policy of a buffer load: nt (streamed)
 
 // 16-byte store of a staged epilogue, marked non-temporal (streamed through
 // L2 without displacing the operands other tiles still read).
@@ -627,7 +628,7 @@ __device__ __forceinline__ void store_tile_staged_glu(const GemmParams &p, const
 // (i * NW + w) * 64 .. +63.  With issue false every load is out of range and
 // reads nothing: the instructions still go out, so that the number of loads
 // in flight after a tile does not depend on the data.
-template <int NIA, int NIB, int NW>
+template <int NIA, int NIB, int NW, int BPOL = 0>
 __device__ __forceinline__ void tile_dma(uint4 *na, uint4 *nb, bool issue, unsigned kt, __amdgpu_buffer_rsrc_t ra,
                                          __amdgpu_buffer_rsrc_t rb, const unsigned (&a_off)[NIA],
                                          const unsigned (&b_off)[NIB], unsigned bks, int wave)
@@ -639,14 +640,15 @@ __device__ __forceinline__ void tile_dma(uint4 *na, uint4 *nb, bool issue, unsig
 #pragma unroll
     for (int i = 0; i < NIB; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LMOE_LDS(nb + (i * NW + wave) * 64), 16,
-                                                 issue ? b_off[i] + kt * bks : kOOB, 0, 0, 0);
+                                                 issue ? b_off[i] + kt * bks : kOOB, 0, 0, BPOL);
 }
 
 // One k-step: the refill of stages na, nb with tile kt, then (if live) the
 // tile held in sa, sb into the accumulators.  The four stages are different
 // LDS arrays; the restrict qualifiers tell the compiler so, which keeps it
 // from making the reads of sa, sb wait for the DMA into na, nb.
-template <typename E, int TM, int TN, int WTM, int WTN, bool BQ8, int NIA, int NIB, int NW, int XM = 0, int BM = 0>
+template <typename E, int TM, int TN, int WTM, int WTN, bool BQ8, int NIA, int NIB, int NW, int XM = 0, int BM = 0,
+          int BPOL = 0>
 __device__ __forceinline__ void dma_mma(uint4 *__restrict__ na, uint4 *__restrict__ nb, const uint4 *__restrict__ sa,
                                         const uint4 *__restrict__ sb, bool issue, unsigned kt,
                                         __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
@@ -654,7 +656,7 @@ __device__ __forceinline__ void dma_mma(uint4 *__restrict__ na, uint4 *__restric
                                         int wave, bool live, f32x16 (&acc)[TM][TN], int wm, int wn, int lane,
                                         f32x16 (*accx)[XM > 0 ? XM : 1][1] = nullptr, bool xlive = false)
 {
-    tile_dma<NIA, NIB, NW>(na, nb, issue, kt, ra, rb, a_off, b_off, bks, wave);
+    tile_dma<NIA, NIB, NW, BPOL>(na, nb, issue, kt, ra, rb, a_off, b_off, bks, wave);
     if (live)
         tile_mma<E, TM, TN, WTM, WTN, BQ8, XM, BM>(acc, sa, sb, wm, wn, lane, accx, xlive);
 }
@@ -690,6 +692,14 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
     static_assert(XR == 0 || (GROUPED && !BQ8 && ACT == ACT_NONE && XR % 32 == 0 && WM * 32 == WTN),
                   "extra rows: grouped bf16 tiles, one 32-column block per wave row");
     static_assert(NS >= 2 && NS <= 4, "stages");
+    // Expert weights that one M-tile uses alone -- decode's 32-row tiles, and
+    // 256-row tables with extra rows, whose experts average at most 320 rows --
+    // load non-temporally, so that streaming them does not evict the gathered
+    // A rows the expert's N-tiles share in L2.  Measured: decode_eff grouped
+    // GEMMs 53.9 / 56.0 -> 48.9 / 50.5 us, wide_prefill 354 / 358 -> 342 / 355
+    // us; with zipf_skew's 512 rows per expert (weights shared by the
+    // expert's M-tiles) they lost 3-4 %, so those tables keep the default.
+    constexpr int BPOL = (GROUPED && (BM == 32 || XR > 0)) ? kLoadNonTemporal : 0;
     static_assert(!BQ8 || (GROUPED && sizeof(E) == 2), "E4M3 B operands: grouped bf16 GEMMs");
 
     __shared__ uint4 sA0[BMA * 8], sA1[BMA * 8], sA2[NS > 2 ? BMA * 8 : 1], sA3[NS > 3 ? BMA * 8 : 1];
@@ -777,11 +787,11 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         nkl = p.k_offsets[expert + 1] / BK - kt0;
     }
     const int64_t c_row_base = row_base + ti.c_row0;  // first output row of the tile
-    tile_dma<NIA, NIB, NW>(sA0, sB0, nkl > 0, kt0, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
+    tile_dma<NIA, NIB, NW, BPOL>(sA0, sB0, nkl > 0, kt0, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
     if constexpr (NS > 2)
-        tile_dma<NIA, NIB, NW>(sA1, sB1, nkl > 1, kt0 + 1, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
+        tile_dma<NIA, NIB, NW, BPOL>(sA1, sB1, nkl > 1, kt0 + 1, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
     if constexpr (NS > 3)
-        tile_dma<NIA, NIB, NW>(sA2, sB2, nkl > 2, kt0 + 2, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
+        tile_dma<NIA, NIB, NW, BPOL>(sA2, sB2, nkl > 2, kt0 + 2, ra_rsrc, rb_rsrc, a_off, b_off, bks, wave);
 
 // One k-tile step j: wait until tile j is in LDS for every wave (the NS - 2
 // tiles issued after it, real or out of range, may stay in flight) and every
@@ -792,7 +802,7 @@ __global__ __launch_bounds__(64 * WM * WN, MINB) void gemm_kernel(const GemmPara
         wait_vm_lgkm0<(NS - 2) * NI>();                                                                       \
         __builtin_amdgcn_s_barrier();                                                                         \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
-        dma_mma<E, TM, TN, WTM, WTN, BQ8, NIA, NIB, NW, XM, BM>(                                              \
+        dma_mma<E, TM, TN, WTM, WTN, BQ8, NIA, NIB, NW, XM, BM, BPOL>(                                        \
             NA, NB, SA, SB, j + NS - 1 < nkl, (unsigned)(kt0 + j + NS - 1), ra_rsrc, rb_rsrc, a_off, b_off, bks,  \
             wave, wave_live, acc, wm, wn, lane, XM > 0 ? &accx : nullptr, rows_valid > BM);                  \
         __builtin_amdgcn_sched_barrier(0);                                                                    \
