@@ -9,7 +9,9 @@ up-projection) over one batch of seeded synthetic tokens already resident in
 HBM.  Prints one JSON line: whole-job tokens/s of the headline workload
 (wide_prefill, the largest of the named single-GPU workloads), the roofline
 position of its dominant kernel (timed with HIP events on the forward's
-stream during the timed steps), the fp64 CPU oracle timed on a bounded token
+stream over a second run of the K timed steps: the throughput steps record no
+events, which cost the stream about 3 us each), the fp64 CPU oracle timed on a
+bounded token
 sample, and the same measurements for the other named workloads under
 "workloads".
 
@@ -380,8 +382,8 @@ def measure(name, args, log):
             layers[i % R].forward(x, y)
         stage_out = {k: stage_entry(k, ms / n * 1e3, n) for k, (ms, n) in profile_end().items() if n}
         dom = max((k for k in stage_out if "frac" in stage_out[k]), key=lambda k: stage_out[k]["avg_us"])
-        # the timed region records events around the dominant stage only
-        profile_begin(args.steps, 1 << names[dom])
+    # the throughput: K forwards with no events in between (an event record
+    # costs the stream about 3 us, 5 % of a decode step)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -392,6 +394,15 @@ def measure(name, args, log):
     ms_per_step = dt / args.steps * 1e3
     roof = None
     if timing:
+        # the dominant kernel: the same K forwards again, with HIP events on
+        # the forward's stream around that stage only
+        profile_begin(args.steps, 1 << names[dom])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for i in range(args.steps):
+            layers[i % R].forward(x, y)
+        torch.cuda.synchronize()
+        log(f"{sh.name}: timed {args.steps} steps with events around {dom} in {time.perf_counter() - t1:.3f} s")
         tot = profile_end()[dom]
         e = stage_entry(dom, tot[0] / tot[1] * 1e3, tot[1])
         flop, nbytes, staged = work[dom]
@@ -537,7 +548,9 @@ def main():
         **({"graph": head["graph"]} if "graph" in head else {}),
         "workloads": others,
         "stages_note": "per-stage HIP-event times from an untimed pass of min(steps, 10) forwards; "
-                       "roofline.avg_us is the dominant kernel timed over the timed region; algorithmic "
+                       "value and ms_per_step from the K timed forwards, which record no events; "
+                       "roofline.avg_us is the dominant kernel timed with HIP events on the forward's "
+                       "stream over a second timed region of the same K forwards; algorithmic "
                        "bytes = weights touched + the kernel's own inputs and outputs, staged_bytes = H "
                        "between the expert GEMMs and the fp32 router scores",
     }
