@@ -142,7 +142,7 @@ STAGE_OF_TAG = {0: "gemm_x_router_down_shared1", 1: "grouped_gemm1_relu2", 2: "g
 # (-1: the last one)
 TAG_POS = {"gemm_kernel": 7, "skinny_gemm_kernel": -1, "fewrow_split_kernel": -1, "gemm_tn_kernel": 0}
 FIXED_STAGE = {"expert_mlp_kernel": "expert_mlp", "router_select_kernel": "router_select",
-               "dispatch_tiny_kernel": "dispatch_finalize", "dispatch_small_kernel": "dispatch_finalize",
+               "route_tiny_kernel": "router_select", "dispatch_small_kernel": "dispatch_finalize",
                "finalize_kernel": "dispatch_finalize", "chunk_scan_kernel": "dispatch_scan",
                "combine_kernel": "combine", "splitk_reduce_kernel": "splitk_reduce",
                "transpose_kernel": "repack_transpose (create only)",

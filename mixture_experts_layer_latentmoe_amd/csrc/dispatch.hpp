@@ -23,11 +23,7 @@
 //                      and the tile table of the grouped GEMMs
 //   dispatch_small_kernel  both in one workgroup when a batch has at most 64
 //                      chunks
-//   dispatch_tiny_kernel   batches of at most 64 tokens, straight from idx:
-//                      per expert the 64-bit mask of the tokens that chose
-//                      it (LDS atomic ORs, whose order does not matter);
-//                      counts[e] = popc(mask[e]) and
-//                      pos[t, k] = offsets[e] + popc(mask[e] & (2^t - 1))
+//   (batches of at most 64 tokens: route_tiny.hpp, straight from idx)
 // All integer, no ordering atomics: the same idx always gives the same bits.
 #pragma once
 
@@ -84,13 +80,10 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const int *__restrict__
 // row on, 0), so that a kernel finds its tile with one load.  Tiles are BM rows from each expert's first row,
 // except that the last one may hold up to BM + slack rows: max(1, ceil((c -
 // slack) / BM)) tiles for an expert with c > 0 rows (slack 0: ceil(c / BM)).
-// 1024 threads, N' <= 1024; every thread calls it.  s_off is complete on return;
-// s_toff, if given (lead only), receives each expert's first tile, complete
-// after the next barrier.
+// 1024 threads, N' <= 1024; every thread calls it.  s_off is complete on return.
 __device__ __forceinline__ void block_offsets(int c, bool lead, int N, int BM, int slack, int *__restrict__ offsets,
                                               int4 *__restrict__ tile_info,
-                                              int *__restrict__ n_mtiles, int *s_off, int *s_wsum,
-                                              int *s_toff = nullptr)
+                                              int *__restrict__ n_mtiles, int *s_off, int *s_wsum)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int incl = wave_incl_scan(c, lane);
@@ -119,8 +112,6 @@ __device__ __forceinline__ void block_offsets(int c, bool lead, int N, int BM, i
         for (int w = 0; w < wave; ++w)
             tbefore += s_wsum[w];
         const int texcl = tbefore + tincl - nt;
-        if (s_toff)
-            s_toff[tid] = texcl;
         for (int j = 0; j < nt; ++j)
             tile_info[texcl + j] = make_int4(tid, excl + j * BM, c - j * BM, 0);
         if (tid == 1023)
@@ -213,60 +204,6 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(const int *__restr
     }
     finalize_block(c, true, tid, 1024, idx, rank, chunk_base, T, K, N, chunk_tokens, ld_chunks, BM, slack, offsets,
                    tile_info, n_mtiles, pos, perm, s_off, s_wsum);
-}
-
-// Batches of at most 64 tokens (kTinyTokens), one workgroup of 1024 threads,
-// N' <= 1024, T K' <= 4096: every pair's expert is loaded up front, the token
-// masks are ORed together in LDS, and the rest reads LDS only.  With 32-row
-// tiles (BM = 32, so no slack) and a row table it also writes the token of
-// each dispatch row at [tile][row in tile] (rows past an expert's last row
-// stay unwritten), so that a grouped GEMM workgroup loads its A rows together
-// with its tile record instead of through perm after it.
-__global__ __launch_bounds__(1024) void dispatch_tiny_kernel(const int *__restrict__ idx, int T, int K, int N, int BM,
-                                                            int slack, int *__restrict__ counts,
-                                                            int *__restrict__ offsets, int4 *__restrict__ tile_info,
-                                                            int *__restrict__ n_mtiles,
-                                                            int *__restrict__ pos, int *__restrict__ perm,
-                                                            int *__restrict__ tile_rows)
-{
-    __shared__ unsigned long long s_mask[1024];
-    __shared__ int s_off[1024];
-    __shared__ int s_toff[1024];
-    __shared__ int s_wsum[16];
-    const int tid = threadIdx.x, P = T * K;
-    int e_q[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int q = tid + 1024 * j;
-        e_q[j] = q < P ? idx[q] : -1;
-    }
-    s_mask[tid] = 0ull;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        if (e_q[j] >= 0)
-            atomicOr(&s_mask[e_q[j]], 1ull << ((tid + 1024 * j) / K));
-    __syncthreads();
-    const int c = tid < N ? __popcll(s_mask[tid]) : 0;
-    if (tid < N)
-        counts[tid] = c;
-    const bool rows = BM == 32 && slack == 0 && tile_rows;
-    block_offsets(c, true, N, BM, slack, offsets, tile_info, n_mtiles, s_off, s_wsum, rows ? s_toff : nullptr);
-    if (rows)
-        __syncthreads();  // s_toff
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int e = e_q[j];
-        if (e < 0)
-            continue;
-        const int q = tid + 1024 * j, t = q / K;
-        const int r = __popcll(s_mask[e] & ((1ull << t) - 1ull));  // row within the expert
-        const int p = s_off[e] + r;
-        pos[q] = p;
-        perm[p] = t;
-        if (rows)
-            tile_rows[(s_toff[e] + (r >> 5)) * 32 + (r & 31)] = t;
-    }
 }
 
 }  // namespace lmoe

@@ -51,6 +51,7 @@
 #include "gemm.hpp"
 #include "gemm_tn.hpp"
 #include "repack.hpp"
+#include "route_tiny.hpp"
 #include "router.hpp"
 #include "skinny.hpp"
 #include "backward.hpp"
@@ -146,6 +147,7 @@ constexpr int kGroupSlack = 64;  // extra rows the 256-row tiles take (the kerne
 constexpr int kNoColumn = 1 << 30;  // relu2_from / glu_from: no such columns
 constexpr int kSplitKMaxRows = 256, kSplitKMax = 16;
 constexpr int kSplitCounters = 4096;  // column groups of 32 of the widest few-row split GEMM
+constexpr int kRouteCounter = kSplitCounters - 1;  // route_tiny_kernel's arrival counter
 
 int64_t max_mtiles_for(int64_t P, int64_t N, int bm) { return (P + bm - 1) / bm + std::min<int64_t>(N, P); }
 
@@ -735,6 +737,47 @@ void launch_select_tok(const Plan &p, const Workspace &w, int T, hipStream_t s)
         launch_select_n<NPL, kRouterTokens, true>(p, w, T, s);
 }
 
+// Decode batches: selection and dispatch order in one launch (route_tiny.hpp).
+template <int NPL>
+void launch_route_tiny_n(const TinyRouteParams &rp, hipStream_t s)
+{
+    const int blocks = (rp.T + kTinySelectWaves - 1) / kTinySelectWaves;
+    route_tiny_kernel<NPL><<<dim3(blocks), dim3(kRouteTinyThreads), route_tiny_smem_bytes(rp.K), s>>>(rp);
+    hip_check(hipGetLastError());
+}
+
+void launch_route_tiny(const Plan &p, const Workspace &w, int T, int bm, int slack, bool row_table, hipStream_t s)
+{
+    TinyRouteParams rp{};
+    rp.scores = w.logits;
+    rp.T = T;
+    rp.N = (int)p.N;
+    rp.K = (int)p.K;
+    rp.idx = w.idx;
+    rp.gate = w.gate;
+    rp.counter = w.counters + kRouteCounter;
+    rp.BM = bm;
+    rp.slack = slack;
+    rp.counts = w.counts;
+    rp.offsets = w.offsets;
+    rp.tile_info = w.tile_info;
+    rp.n_mtiles = w.n_mtiles;
+    rp.pos = w.pos;
+    rp.perm = w.perm;
+    rp.tile_rows = row_table ? w.tile_rows : nullptr;
+    const int64_t npl = (p.N + 63) / 64;
+    if (npl <= 1)
+        launch_route_tiny_n<1>(rp, s);
+    else if (npl <= 2)
+        launch_route_tiny_n<2>(rp, s);
+    else if (npl <= 4)
+        launch_route_tiny_n<4>(rp, s);
+    else if (npl <= 8)
+        launch_route_tiny_n<8>(rp, s);
+    else
+        launch_route_tiny_n<16>(rp, s);
+}
+
 void launch_select(const Plan &p, const Workspace &w, int T, hipStream_t s)
 {
     const int64_t npl = (p.N + 63) / 64;
@@ -850,31 +893,33 @@ void forward_impl(latentmoe_handle *h, const Workspace &w, const void *x, void *
         copy2d(dbg->h_shared, es * (p.ld_zh - p.l), static_cast<char *>(w.zh) + es * p.l, es * p.ld_zh,
                es * (p.ld_zh - p.l), T, s);
 
-    // 1: top-K', gates, chunk ranks
-    tm.begin(ST_SELECT);
-    launch_select(p, w, T, s);
-    tm.end(ST_SELECT);
-    // 2-4: dispatch order (small batches: one workgroup, one launch)
     // per-tile A-row table for 32-row tiles of decode batches: the first
     // grouped GEMM's workgroups load their A rows together with the tile record
     // (measured: bf16 experts -2.9 us in that GEMM, +0.6 us in the dispatch;
     // E4M3 experts gain nothing there, so they go through perm)
     const bool row_table = T <= kTinyTokens && gbm == kGroupBMSmall && !p.fp8;
     if (T <= kTinyTokens) {
-        tm.begin(ST_FINALIZE);
-        dispatch_tiny_kernel<<<dim3(1), dim3(1024), 0, s>>>(w.idx, T, K, N, gbm, slack, w.counts, w.offsets,
-                                                            w.tile_info, w.n_mtiles, w.pos, w.perm,
-                                                            row_table ? w.tile_rows : nullptr);
-        hip_check(hipGetLastError());
-        tm.end(ST_FINALIZE);
-    } else if (nchunks <= 64) {
+        // 1-4 for decode batches in one launch: selection, and in its last
+        // workgroup the dispatch order (measured at decode_eff: -2 us)
+        tm.begin(ST_SELECT);
+        launch_route_tiny(p, w, T, gbm, slack, row_table, s);
+        tm.end(ST_SELECT);
+    } else {
+        // 1: top-K', gates, chunk ranks
+        tm.begin(ST_SELECT);
+        launch_select(p, w, T, s);
+        tm.end(ST_SELECT);
+    }
+    // 2-4: dispatch order of larger batches (up to 64 chunks: one workgroup,
+    // one launch)
+    if (T > kTinyTokens && nchunks <= 64) {
         tm.begin(ST_FINALIZE);
         dispatch_small_kernel<<<dim3(1), dim3(1024), 0, s>>>(
             w.chunk_counts, nchunks, w.idx, w.rank, T, K, N, kRouterTokens, (int)w.ld_chunks, gbm, slack, w.chunk_base,
             w.counts, w.offsets, w.tile_info, w.n_mtiles, w.pos, w.perm);
         hip_check(hipGetLastError());
         tm.end(ST_FINALIZE);
-    } else {
+    } else if (T > kTinyTokens) {
         tm.begin(ST_SCAN);
         chunk_scan_kernel<<<dim3((unsigned)((N + 3) / 4)), dim3(256), 0, s>>>(w.chunk_counts, nchunks,
                                                                               (int)w.ld_chunks, N, w.chunk_base,

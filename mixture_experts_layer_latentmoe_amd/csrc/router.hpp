@@ -14,7 +14,7 @@
 // CU busy at a few thousand tokens.  Batches of at most kTinyTokens tokens
 // take workgroups of 4 tokens (one wave per SIMD: the selection is a chain of
 // dependent wave operations, and four waves sharing a SIMD take four times as
-// long) and skip step 4 (dispatch_tiny_kernel orders them by token masks):
+// long) and skip step 4 (route_tiny.hpp orders them by token masks):
 //   1. scores become order-preserving 32-bit keys (-0.0 folded into +0.0, so
 //      signed zeros tie); a 32-round radix search, counting with wave ballots,
 //      finds the K'-th largest key; every key above it is selected, and of the

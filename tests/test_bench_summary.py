@@ -21,8 +21,9 @@ def test_stage_of_kernel_mangled_and_demangled():
         "void lmoe::gemm_kernel<__hip_bfloat16, 128, 128, 2, 2, 2, true, 1, 2, false, 0, 0>(lmoe::GemmParams)":
             "grouped_gemm2",
         "void lmoe::fewrow_split_kernel<__hip_bfloat16, 2, 1, 8, 3>(lmoe::GemmParams)": "gemm_up_shared2",
-        "lmoe::dispatch_tiny_kernel(int const*, int, int, int, int, int, int*, int*, HIP_vector_type<int, 4u>*, int*, "
-        "int*, int*)": "dispatch_finalize",
+        "_ZN4lmoe17route_tiny_kernelILi4EEEvNS_15TinyRouteParamsE.kd": "router_select",
+        "void lmoe::dispatch_small_kernel(int const*, int, int const*, int const*, int, int, int, int, int, int, int, "
+        "int*, int*, int*, HIP_vector_type<int, 4u>*, int*, int*, int*)": "dispatch_finalize",
         "void lmoe::router_select_kernel<4, 4, false>(float const*, int, int, int, int*, float*, int*, int*, int)":
             "router_select",
         "_ZN4lmoe17expert_mlp_kernelILi128ELi512ELi128ELi32ELi4ELi4ELi2ELi2ELi4ELb0ELi8EEEvNS_9MlpParamsE":
