@@ -295,6 +295,66 @@ __device__ __forceinline__ void tile_mma(f32x16 (&acc)[TM][TN], const uint4 *a, 
     }
 }
 
+// The same product (bf16 operands in LDS, no extra rows) with the fragment
+// reads software-pipelined: the fragments of k-step s + 1 go into a second
+// register set, one LDS read between consecutive MFMAs of k-step s, so a
+// k-step's LDS latency hides behind the previous one's multiplies instead of
+// stalling the matrix pipe (left to itself, the compiler reads each k-step's
+// fragments just before its first MFMA and waits for them there).  Each
+// k-step is its own scheduling region; the group barriers fix the
+// interleave inside it.  Same MFMAs in the same order: the sums are
+// bit-identical.  Measured at wide_prefill: x-pass 346 -> 333-337 us,
+// up-projection 291-293 -> 281-283 us; zipf_skew grouped GEMM 1 226-228 ->
+// 218-222 us.
+// (the accumulators and two fragment sets fit beside the addresses, and a
+// k-step has at least as many MFMAs as fragment reads to interleave)
+template <int TM, int TN>
+constexpr bool kPipeFits = TM * TN * 16 + 8 * (TM + TN) <= 176 && TM * TN >= TM + TN;
+
+template <typename E, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void tile_mma_pipe(f32x16 (&acc)[TM][TN], const uint4 *a, const uint4 *b, int wm, int wn,
+                                              int lane)
+{
+    uint4 af[2][TM], bfr[2][TN];
+    auto load = [&](int s, uint4(&fa)[TM], uint4(&fb)[TN]) {
+        const int c = s * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * WTM + i * 32 + (lane & 31);
+            fa[i] = a[r * 8 + (c ^ ((r >> 1) & 7))];
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int r = wn * WTN + j * 32 + (lane & 31);
+            fb[j] = b[r * 8 + (c ^ ((r >> 1) & 7))];
+        }
+    };
+    load(0, af[0], bfr[0]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int cur = s & 1;
+        if (s < 3)
+            load(s + 1, af[cur ^ 1], bfr[cur ^ 1]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = Mfma32<E>::run(bfr[cur][j], af[cur][i], acc[i][j]);
+        if (s < 3) {
+#pragma unroll
+            for (int q = 0; q < TM + TN; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN - (TM + TN), 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Epilogue of four consecutive output columns col .. col + 3 of one row.
 // Columns below c_split go to C32 in fp32 (+ bias32), the rest to C, with
 // relu^2 from relu2_from on.  c_split is a multiple of 4, so a group never
@@ -657,8 +717,12 @@ __device__ __forceinline__ void dma_mma(uint4 *__restrict__ na, uint4 *__restric
                                         f32x16 (*accx)[XM > 0 ? XM : 1][1] = nullptr, bool xlive = false)
 {
     tile_dma<NIA, NIB, NW, BPOL>(na, nb, issue, kt, ra, rb, a_off, b_off, bks, wave);
-    if (live)
-        tile_mma<E, TM, TN, WTM, WTN, BQ8, XM, BM>(acc, sa, sb, wm, wn, lane, accx, xlive);
+    if (live) {
+        if constexpr (!BQ8 && XM == 0 && sizeof(E) == 2 && kPipeFits<TM, TN>)
+            tile_mma_pipe<E, TM, TN, WTM, WTN>(acc, sa, sb, wm, wn, lane);
+        else
+            tile_mma<E, TM, TN, WTM, WTN, BQ8, XM, BM>(acc, sa, sb, wm, wn, lane, accx, xlive);
+    }
 }
 
 // NT = 64 * WM * WN threads; NS LDS stages (2 or 3), one barrier per k-tile;
