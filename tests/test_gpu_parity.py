@@ -77,6 +77,14 @@ def test_full_size(name, n_sample):
     _full_check(make_workload(get_config(name)), n_sample=n_sample)
 
 
+def test_large_ragged_token_count():
+    """4059 tokens at the README widths: the x-pass on 256x256 tiles and the
+    up-projection on 128x256 tiles (both with the software-pipelined fragment
+    reads) end in a ragged row tile (219 and 91 rows); output and every
+    intermediate on 1024 seeded tokens including the first and the last."""
+    _full_check(make_workload(get_config("readme_acc"), T=4059), n_sample=1024)
+
+
 def test_single_token():
     _full_check(make_workload(get_config("readme_acc"), T=1))
 
