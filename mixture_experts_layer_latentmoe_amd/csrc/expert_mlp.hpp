@@ -101,28 +101,62 @@ __device__ __forceinline__ void mlp_store_h(f32x16 (&acc)[TM][TN], uint4 *hbuf, 
     }
 }
 
-// Phase 1 multiply of one step: one 64-wide k-tile of Z (a) and W1 (b), both
-// in the current slot.  The operands are restrict-qualified: the compiler
-// then tells these LDS reads apart from the DMA into the next slot that is
-// still in flight, and does not wait for it (same rule as gemm.hpp's dma_mma).
-template <int TM, int TN, int WTM, int WTN>
-__device__ __forceinline__ void mlp_mma1(f32x16 (&acc)[TM][TN], const uint4 *__restrict__ a,
-                                         const uint4 *__restrict__ b, int wm, int wn, int lane)
+// A lane's LDS byte offsets of its MFMA fragments, computed once per kernel.
+// Every fragment read of both phases is (row of the lane) x 128 (64 for the
+// W2 slices) + (its swizzled 16-byte chunk) + a compile-time part: the row
+// swizzle of a wave's rows depends only on lane % 32 (wave tiles start at
+// multiples of 16 rows), and a k16-step's chunk pair 2 m + lane / 32 takes
+// four values, m = 0..3.  With these offsets the compile-time part (fragment
+// row block, H buffer k-tile) folds into the reads' immediate offsets: the
+// loop holds 44 address registers instead of the 72 the compiler kept when
+// it formed each step's addresses itself (256 VGPRs, one fragment register
+// pair in rotation); 245 VGPRs now, the same reads and MFMAs, bit-identical
+// sums.  Measured at readme_acc: 421-424 -> 407-417 us.
+struct MlpOffs {
+    unsigned p1a[4], p1b[4];  // phase 1: Z rows, W1 columns; k16-step m
+    unsigned p2a[4];          // phase 2: H rows; chunk pair m
+    unsigned p2b[2];          // phase 2: W2 slice rows; k16-step s of the slice
+};
+
+template <int WTM1, int WTN1, int WTM2, int WTN2, int CH2>
+__device__ __forceinline__ MlpOffs mlp_offsets(int lane, int wm1, int wn1, int wm2, int wn2)
 {
+    static_assert(WTM1 % 16 == 0 && WTN1 % 16 == 0 && WTM2 % 16 == 0 && WTN2 % 16 == 0 && CH2 == 4,
+                  "row swizzles of a wave's rows depend on the lane only");
+    const int L = lane & 31, h = lane >> 5, sw = (L >> 1) & 7, swb = (L >> 2) & 3;
+    MlpOffs o;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const unsigned x = (unsigned)(((2 * m + h) ^ sw) * 16);
+        o.p1a[m] = (unsigned)(wm1 * WTM1 + L) * 128u + x;
+        o.p1b[m] = (unsigned)(wn1 * WTN1 + L) * 128u + x;
+        o.p2a[m] = (unsigned)(wm2 * WTM2 + L) * 128u + x;
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+        o.p2b[q] = (unsigned)(wn2 * WTN2 + L) * 64u + (unsigned)(((2 * q + h) ^ swb) * 16);
+    return o;
+}
+
+// Phase 1 multiply of one step: one 64-wide k-tile of Z (a) and W1 (b), both
+// in the current slot, fragments at the lane's precomputed offsets.  The
+// operands are restrict-qualified: the compiler then tells these LDS reads
+// apart from the DMA into the next slot that is still in flight, and does not
+// wait for it (same rule as gemm.hpp's dma_mma).
+template <int TM, int TN>
+__device__ __forceinline__ void mlp_mma1_off(f32x16 (&acc)[TM][TN], const uint4 *__restrict__ a,
+                                             const uint4 *__restrict__ b, const MlpOffs &o)
+{
+    const char *ac = reinterpret_cast<const char *>(a), *bc = reinterpret_cast<const char *>(b);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const int c = s * 2 + (lane >> 5);
         uint4 af[TM], bfr[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = wm * WTM + i * 32 + (lane & 31);
-            af[i] = a[r * 8 + (c ^ ((r >> 1) & 7))];
-        }
+        for (int i = 0; i < TM; ++i)
+            af[i] = *reinterpret_cast<const uint4 *>(ac + o.p1a[s] + i * 32 * 128);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int r = wn * WTN + j * 32 + (lane & 31);
-            bfr[j] = b[r * 8 + (c ^ ((r >> 1) & 7))];
-        }
+        for (int j = 0; j < TN; ++j)
+            bfr[j] = *reinterpret_cast<const uint4 *>(bc + o.p1b[s] + j * 32 * 128);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -131,27 +165,23 @@ __device__ __forceinline__ void mlp_mma1(f32x16 (&acc)[TM][TN], const uint4 *__r
     }
 }
 
-// Phase 2 multiply of one step: k-values k0 .. k0 + 8 CH2 - 1 of the chunk,
+// Phase 2 multiply of one step: k-values K0 .. K0 + 8 CH2 - 1 of the chunk,
 // A fragments from the H buffer, B fragments (W2 slice) from the slot.
-template <int BM, int TM, int TN, int WTM, int WTN, int CH2>
-__device__ __forceinline__ void mlp_mma2(f32x16 (&acc)[TM][TN], const uint4 *hbuf, const uint4 *__restrict__ b, int k0,
-                                         int wm, int wn, int lane)
+template <int BM, int TM, int TN, int CH2, int K0>
+__device__ __forceinline__ void mlp_mma2_off(f32x16 (&acc)[TM][TN], const uint4 *hbuf, const uint4 *__restrict__ b,
+                                             const MlpOffs &o)
 {
+    const char *hc = reinterpret_cast<const char *>(hbuf), *bc = reinterpret_cast<const char *>(b);
 #pragma unroll
     for (int s = 0; s < CH2 / 2; ++s) {
-        const int kk = k0 + 16 * s;
-        const int kt = kk >> 6, ca = ((kk & 63) >> 3) + (lane >> 5), cb = 2 * s + (lane >> 5);
+        const int kk = K0 + 16 * s, kt = kk >> 6, m = (kk & 63) >> 4;
         uint4 af[TM], bfr[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = wm * WTM + i * 32 + (lane & 31);
-            af[i] = hbuf[(kt * BM + r) * 8 + (ca ^ ((r >> 1) & 7))];
-        }
+        for (int i = 0; i < TM; ++i)
+            af[i] = *reinterpret_cast<const uint4 *>(hc + o.p2a[m] + (kt * BM + i * 32) * 128);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int r = wn * WTN + j * 32 + (lane & 31);
-            bfr[j] = b[r * CH2 + (cb ^ swz2<CH2>(r))];
-        }
+        for (int j = 0; j < TN; ++j)
+            bfr[j] = *reinterpret_cast<const uint4 *>(bc + o.p2b[s] + j * 32 * 64);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -252,7 +282,7 @@ struct MlpChunk {
                                                __amdgpu_buffer_rsrc_t rw2, const unsigned (&a_off)[SH::NIA1],
                                                unsigned b1_off, unsigned b2_off, int wave, int lane,
                                                f32x16 (&accH)[SH::TM1][SH::TN1], f32x16 (&accY)[SH::TM2][SH::TN2],
-                                               int wm1, int wn1, int wm2, int wn2, bool live2)
+                                               int wm1, int wn1, int wm2, int wn2, bool live2, const MlpOffs &of)
     {
         constexpr int AHEAD = POS + NS - 1;
         constexpr int NXT = AHEAD < SH::SPC ? AHEAD : AHEAD - SH::SPC;
@@ -277,18 +307,17 @@ struct MlpChunk {
             }
             // no skip for padding rows here: with one, the compiler also waited
             // for the DMA in flight before this step's LDS reads
-            mlp_mma1<SH::TM1, SH::TN1, SH::WTM1, SH::WTN1>(accH, cur, cur + BM * 8, wm1, wn1, lane);
+            mlp_mma1_off<SH::TM1, SH::TN1>(accH, cur, cur + BM * 8, of);
             if constexpr (POS == SH::S1 - 1)
                 mlp_store_h<BM, SH::TM1, SH::TN1, SH::WTM1, SH::WTN1, GLU>(accH, hbuf, wm1, wn1, lane, true);
         } else {
             if (live2)
-                mlp_mma2<BM, SH::TM2, SH::TN2, SH::WTM2, SH::WTN2, SH::CH2>(accY, hbuf, cur, (POS - SH::S1) * KS2,
-                                                                           wm2, wn2, lane);
+                mlp_mma2_off<BM, SH::TM2, SH::TN2, SH::CH2, (POS - SH::S1) * KS2>(accY, hbuf, cur, of);
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (POS + 1 < SH::SPC)
             run<POS + 1>(s0, s1, s2, s3, hbuf, c, more, nb1, rz, rw1, rw2, a_off, b1_off, b2_off, wave, lane, accH,
-                         accY, wm1, wn1, wm2, wn2, live2);
+                         accY, wm1, wn1, wm2, wn2, live2, of);
     }
 };
 
@@ -350,6 +379,7 @@ __global__ __launch_bounds__(512, 1) void expert_mlp_kernel(const MlpParams p)
     // waves whose rows are all padding skip their phase-2 multiplies
     const bool live2 = wm2 * SH::WTM2 < rows_valid;
     const int nchunks = p.m / MC;
+    const MlpOffs of = mlp_offsets<SH::WTM1, SH::WTN1, SH::WTM2, SH::WTN2, SH::CH2>(lane, wm1, wn1, wm2, wn2);
     mlp_dma<SH, BM, LW, MC, KS2, 0>(slot0, 0, true, p.nb1, rz, rw1, rw2, a_off, b1_off, b2_off, wave);
     mlp_dma<SH, BM, LW, MC, KS2, 1>(slot1, 0, true, p.nb1, rz, rw1, rw2, a_off, b1_off, b2_off, wave);
     if constexpr (NS > 3)
@@ -357,7 +387,7 @@ __global__ __launch_bounds__(512, 1) void expert_mlp_kernel(const MlpParams p)
     for (int c = 0; c < nchunks; ++c)
         MlpChunk<SH, BM, LW, MC, KS2, NS, GLU>::template run<0>(slot0, slot1, slot2, slot3, hbuf, c, c + 1 < nchunks,
                                                                 p.nb1, rz, rw1, rw2, a_off, b1_off, b2_off, wave,
-                                                                lane, accH, accY, wm1, wn1, wm2, wn2, live2);
+                                                                lane, accH, accY, wm1, wn1, wm2, wn2, live2, of);
 
     // Y [rows, l] through LDS: every wave is done with the ring (no load in flight)
     wait_vm_lgkm0<0>();
