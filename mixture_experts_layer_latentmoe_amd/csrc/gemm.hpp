@@ -15,7 +15,9 @@
 // LDS stage, no staging registers): a row outside the valid range gets an
 // offset beyond the buffer's size, and the hardware returns zeros for it, so
 // the main loop has no branches.  With NS stages, k-tiles j + 1 .. j + NS - 1
-// are in flight while k-tile j is multiplied; one barrier per k-tile.
+// are in flight while k-tile j is multiplied; one barrier per k-tile.  Inside
+// a k-tile, where registers allow, the MFMA fragments of the next 16-wide
+// k-step are read from LDS while the current one multiplies (tile_mma_pipe).
 //
 // Dense mode: rows = M; tiles walk grouped-by-M order inside each XCD.
 // Grouped mode (routed experts): the dispatch rows of expert e are the
