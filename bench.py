@@ -523,8 +523,9 @@ def main():
                     help="also time the layer's backward pass (its forward recompute included) over the same "
                          "steps and report it under \"backward\"")
     ap.add_argument("--graph", action="store_true",
-                    help="also replay the forward from captured HIP graphs (one per weight copy) over the same "
-                         "steps and report it under \"graph\"; the headline value stays the eager forward")
+                    help="also replay the forward from captured HIP graphs (one per weight copy, and one "
+                         "holding the forwards of a whole weight-copy rotation) over the same steps and report "
+                         "them under \"graph\"; the headline value stays the eager forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain elementwise copy of 256 MiB (3 launches) so that profiler "
                          "byte counters can be scaled by a kernel of known traffic")
